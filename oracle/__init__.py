@@ -1,0 +1,25 @@
+"""Plain fp64 CPU oracle for block-sparse attention with NABLA / sliding-tile masks.
+
+TEST INFRASTRUCTURE ONLY. The product path (the HIP library and its Python
+binding) never imports, calls or links anything here; only the tests, the smoke
+check and the benchmark's CPU-baseline leg do. Nothing here is blocked, fused or
+reordered beyond the definitions it cites, so each step can be checked against the
+pages by eye:
+
+  nabla.py      adaptive block mask: block pooling, reduced map, row softmax,
+                descending sort, exclusive cumulative mass, threshold at 1 - thr
+  sta.py        static sliding-tile block mask (tile window, clipped at borders)
+  attention.py  softmax attention restricted to the kept N x N blocks
+  csr.py        union of masks and the per-query-block kv index lists
+
+Pins: every function is checked by `tests/test_oracle_*.py` against closed forms,
+brute force, textbook identities or library routines (see those files).
+"""
+from .nabla import block_pool, reduced_map, row_softmax, cdf_select, nabla_mask, nabla_masks
+from .sta import sta_block_mask, sta_token_mask
+from .attention import block_sparse_attention
+from .csr import mask_or, mask_to_csr
+
+__all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask",
+           "nabla_masks", "sta_block_mask", "sta_token_mask", "block_sparse_attention",
+           "mask_or", "mask_to_csr"]
