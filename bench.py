@@ -1,0 +1,208 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input resident in HBM:
+sliding-tile mask (if the workload has one) -> NABLA mask (pool + select, OR'd with
+the sliding-tile mask) -> kv lists (CSR) -> block-sparse attention forward.
+
+Prints ONE JSON line. `value` is the effective attention throughput of the whole step:
+kept-tile FLOPs (4 * 64 * 64 * D per kept 64x64 tile) / step time. The roofline object
+is for the dominant kernel (the attention kernel), timed with HIP events on the stream
+it runs on; `cpu_baseline` times the fp64 oracle on a bounded sample of the same work.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--dense] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
+FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (published)
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E (published)
+
+
+def _flops_per_tile(D):
+    return 4.0 * 64 * 64 * D
+
+
+def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
+    import torch
+    import block_sparse_attention_mask_amd as bsa
+    from synth import make_inputs, quantize_fp8_blocks
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(cfg, seed=0, device=dev)
+    qa, ka, qs, ks = q, k, None, None
+    if fp8:
+        qa, qs = quantize_fp8_blocks(q)
+        ka, ks = quantize_fp8_blocks(k)
+    nb, S = cfg.nb, cfg.S
+    use_nabla = (thr is not None) and not dense
+    plane = torch.empty(nb, nb, dtype=torch.uint8, device=dev)
+    mask = torch.empty(cfg.B, cfg.H, nb, nb, dtype=torch.uint8, device=dev)
+    ones = torch.ones(nb, nb, dtype=torch.uint8, device=dev)
+    rows = cfg.B * cfg.H * nb
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(rows * nb, dtype=torch.int32, device=dev)
+    out = torch.empty_like(v)
+    import ctypes
+    shp = bsa.Shape(cfg.B, cfg.H, S, cfg.S_valid, cfg.D, 64)
+    lib = bsa.load()
+    csr_ws = torch.empty(max(256, lib.csr_workspace_size(cfg.B, cfg.H, nb)), dtype=torch.uint8, device=dev)
+    attn_ws = torch.empty(max(256, lib.attn_csr_workspace_size(ctypes.byref(shp), bsa._dtype_code(qa))),
+                          dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if cfg.sta is not None and not dense:
+            bsa.sta_build_mask(S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                               order_tile=cfg.order_tile, device=dev, out=plane)
+        m = mask
+        if use_nabla:
+            bsa.nabla_build_mask(q, k, thr, or_mask=plane if cfg.sta is not None else None, out=mask)
+        elif dense:
+            m = ones
+        else:
+            m = plane
+        if ev is not None:
+            ev[1].record()
+        rp, ci = bsa.mask_to_csr(m, B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
+        if ev is not None:
+            ev[2].record()
+        bsa.block_sparse_attn_fwd_csr(qa, ka, v, rp, ci, s_valid=cfg.S_valid, q_scale=qs, k_scale=ks, out=out,
+                                      ws=attn_ws)
+        if ev is not None:
+            ev[3].record()
+        return m, rp
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_all0.record()
+    for s in range(steps):
+        m, rp = step(evs[s])
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = t_all0.elapsed_time(t_all1)
+    mask_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    csr_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    kept = int(rp[-1].item())
+    return dict(ms_per_step=ms_total / steps, wall_s=wall, mask_ms=mask_ms, csr_ms=csr_ms, attn_ms=attn_ms,
+                kept_tiles=kept, kept_fraction=kept / (cfg.B * cfg.H * nb * nb), mask=m.cpu() if use_nabla else None,
+                q=q, k=k, v=v)
+
+
+def run_cpu_baseline(cfg, thr, budget_s=15.0):
+    """The fp64 oracle (as it stands) on a bounded sample: whole heads, mask + attention."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    from synth import make_inputs, get_config
+    c1 = get_config(cfg.cid, heads=min(cfg.H, 16))
+    q, k, v = make_inputs(c1, seed=0, device="cpu")
+    plane = None
+    if cfg.sta is not None:
+        plane = oracle.sta_block_mask(cfg.grid, cfg.order, cfg.order_tile, cfg.sta.tile, cfg.sta.window, 64, cfg.S)
+    flops, heads, blocks_done = 0.0, 0, 0
+    t0 = time.perf_counter()
+    for h in range(c1.H):
+        qh, kh, vh = (x[0, h].double().numpy() for x in (q, k, v))
+        if thr is not None:
+            keep, _, _ = oracle.nabla_mask(qh, kh, 64, thr)
+            if plane is not None:
+                keep = keep | plane
+        else:
+            keep = plane
+        # attention on as many query blocks as the budget allows (whole head when possible)
+        for i0 in range(0, cfg.nb, 32):
+            blocks = list(range(i0, min(cfg.nb, i0 + 32)))
+            oracle.block_sparse_attention(qh, kh, vh, keep, 64, cfg.S_valid, q_blocks=blocks)
+            flops += keep[blocks].sum() * _flops_per_tile(cfg.D)
+            blocks_done += len(blocks)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{cfg.name}: NABLA/STA mask of {heads} head(s) + attention of {blocks_done} query blocks "
+                      f"in fp64 numpy ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2, the 2B-DiT shape)")
+    ap.add_argument("--thr", type=float, default=None, help="NABLA threshold (default: the config's first)")
+    ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
+    ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path shards by "
+              f"(batch, head) with no communication, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    from synth import get_config
+    cfg = get_config(args.config)
+    thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
+    r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8)
+    fpt = _flops_per_tile(cfg.D)
+    kept_flops = r["kept_tiles"] * fpt
+    attn_tflops = kept_flops / (r["attn_ms"] * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS
+    if args.fp8:
+        peak = 4.0 / (2.0 / FP8_PEAK_TFLOPS + 2.0 / BF16_PEAK_TFLOPS)   # fp8 QK^T + bf16 PV
+    qk_bytes = 2 * cfg.B * cfg.H * cfg.S * cfg.D * (4 if cfg.dtype == "f32" else 2)
+    mask_bytes = qk_bytes + cfg.B * cfg.H * cfg.nb * cfg.nb
+    line = {
+        "metric": "sparse attn effective TFLOP/s (kept tiles) + % bf16 MFMA peak; mask build GB/s",
+        "value": round(kept_flops / (r["ms_per_step"] * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16" if args.fp8 else cfg.dtype,
+        "data": "synthetic (seeded Q/K/V with smooth positional term)",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S, "S_valid": cfg.S_valid, "D": cfg.D,
+                   "grid": list(cfg.grid), "token_order": cfg.order, "thr": thr,
+                   "sta": None if cfg.sta is None else {"tile": list(cfg.sta.tile), "window": list(cfg.sta.window)},
+                   "dense": args.dense, "fp8_qk": args.fp8},
+        "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
+        "attn_tflops": round(attn_tflops, 2), "attn_frac_bf16_peak": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+        "mask_build_gbps": round(mask_bytes / (r["mask_ms"] * 1e-3) / 1e9, 1) if thr is not None else None,
+        "mask_build_frac_hbm": round(mask_bytes / (r["mask_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        if thr is not None else None,
+        "kept_fraction": round(r["kept_fraction"], 5), "kept_tiles": r["kept_tiles"],
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel", "per_launch_flops": kept_flops},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(cfg, None if args.dense else thr)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+"""Python binding of libbsa: block-sparse attention with NABLA / sliding-tile masks on MI355X.
+
+Argument marshalling only. Every step runs in the HIP kernels of libbsa.so; torch is
+used for device memory (outputs, workspaces) and for the current HIP stream. If the
+library is not built, every call raises.
+
+    mask = nabla_build_mask(q, k, thr=0.2)                   # [B,H,nb,nb] uint8
+    sta  = sta_build_mask(S, S_valid, grid, tile, window)    # [nb,nb] uint8
+    out  = block_sparse_attn_fwd(q, k, v, mask)              # [B,H,S,D]
+"""
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsa.so")
+
+BSA_F32, BSA_BF16, BSA_FP8_E4M3FN = 0, 1, 2
+_STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPACE", 4: "BSA_EHIP"}
+
+# every function the C header declares, in declaration order
+EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "sta_workspace_size", "sta_build_mask", "mask_or",
+           "csr_workspace_size", "bsa_mask_to_csr", "attn_workspace_size", "block_sparse_attn_fwd",
+           "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "bsa_last_error", "bsa_abi_version"]
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int), ("sb", ctypes.c_int64),
+                ("sh", ctypes.c_int64), ("ss", ctypes.c_int64)]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("S", ctypes.c_int), ("S_valid", ctypes.c_int),
+                ("D", ctypes.c_int), ("N", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libbsa.so and declare its signatures; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libbsa.so not found at {p}; build it with "
+                           "`python -m block_sparse_attention_mask_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32, dbl, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+    PT, PS = ctypes.POINTER(Tensor), ctypes.POINTER(Shape)
+    i3 = ctypes.POINTER(ctypes.c_int)
+    sig = {
+        "nabla_workspace_size": (sz, [PS]),
+        "nabla_build_mask": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, sz, vp]),
+        "sta_workspace_size": (sz, [PS]),
+        "sta_build_mask": (i32, [PS, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
+        "mask_or": (i32, [vp, vp, i64, vp, i64, vp]),
+        "csr_workspace_size": (sz, [i32, i32, i32]),
+        "bsa_mask_to_csr": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, sz, vp]),
+        "attn_workspace_size": (sz, [PS, i32]),
+        "block_sparse_attn_fwd": (i32, [PT, PT, PT, PS, vp, i64, i64, vp, vp, dbl, PT, vp, vp, sz, vp]),
+        "attn_csr_workspace_size": (sz, [PS, i32]),
+        "block_sparse_attn_fwd_csr": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
+        "bsa_last_error": (ctypes.c_char_p, []),
+        "bsa_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise BsaError(status, _lib.bsa_last_error().decode())
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return BSA_F32
+    if t.dtype == torch.bfloat16:
+        return BSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return BSA_FP8_E4M3FN
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _tensor(t: torch.Tensor) -> Tensor:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, H, S, D] tensor with contiguous D")
+    return Tensor(t.data_ptr(), _dtype_code(t), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _shape(t: torch.Tensor, s_valid: Optional[int]) -> Shape:
+    B, H, S, D = t.shape
+    return Shape(B, H, S, S if s_valid is None else int(s_valid), D, 64)
+
+
+def _ws(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+def _mask_strides(mask: torch.Tensor):
+    """(ptr, sb, sh) of a [B,H,nb,nb] or [nb,nb] uint8 mask (bytes; 0 = broadcast)."""
+    if mask.dtype not in (torch.uint8, torch.bool):
+        raise TypeError("mask must be uint8 or bool")
+    if mask.dim() == 2:
+        mask = mask[None, None]
+    if mask.stride(3) != 1 or mask.stride(2) != mask.shape[3]:
+        raise ValueError("mask rows must be contiguous")
+    sb = mask.stride(0) if mask.shape[0] > 1 else 0
+    sh = mask.stride(1) if mask.shape[1] > 1 else 0
+    return mask.data_ptr(), sb, sh, mask
+
+
+def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Optional[float] = None,
+                     or_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """NABLA adaptive block mask of q, k [B,H,S,D] (bf16 or f32) -> uint8 [B,H,S/64,S/64]."""
+    lib = load()
+    B, H, S, D = q.shape
+    nb = S // 64
+    shp = _shape(q, None)
+    if out is None:
+        out = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device)
+    ws = _ws(lib.nabla_workspace_size(ctypes.byref(shp)), q.device)
+    om, osb, osh = None, 0, 0
+    if or_mask is not None:
+        om, osb, osh, _keep = _mask_strides(or_mask)
+    tq, tk = _tensor(q), _tensor(k)
+    _check(lib.nabla_build_mask(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
+                                float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(), ws.data_ptr(),
+                                ws.numel(), _stream(q.device)))
+    return out
+
+
+def sta_build_mask(S: int, S_valid: int, grid: Sequence[int], tile: Sequence[int], window: Sequence[int],
+                   order: str = "row", order_tile: Optional[Sequence[int]] = None, device="cuda",
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sliding-tile block mask -> uint8 [S/64, S/64] (shared by all heads)."""
+    lib = load()
+    nb = S // 64
+    shp = Shape(1, 1, S, S_valid, 64, 64)
+    dev = torch.device(device)
+    if out is None:
+        out = torch.empty(nb, nb, dtype=torch.uint8, device=dev)
+    ws = _ws(lib.sta_workspace_size(ctypes.byref(shp)), dev)
+    arr = ctypes.c_int * 3
+    ot = arr(*order_tile) if order_tile is not None else None
+    _check(lib.sta_build_mask(ctypes.byref(shp), arr(*grid), arr(*tile), arr(*window),
+                              0 if order == "row" else 1, ot, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream(dev)))
+    return out
+
+
+def mask_or(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """a | b elementwise; b may be one [nb, nb] plane broadcast over a [B,H,nb,nb] mask."""
+    lib = load()
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("mask_or needs contiguous masks")
+    if out is None:
+        out = torch.empty_like(a, dtype=torch.uint8)
+    _check(lib.mask_or(out.data_ptr(), a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), _stream(a.device)))
+    return out
+
+
+def mask_to_csr(mask: torch.Tensor, B: Optional[int] = None, H: Optional[int] = None,
+                row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None):
+    """Per-query-block kv lists of a [B,H,nb,nb] mask (or one [nb,nb] plane broadcast
+    over B, H) -> (row_ptr int32 [B*H*nb+1], col_idx int32 [B*H*nb*nb])."""
+    lib = load()
+    ptr, sb, sh, m = _mask_strides(mask)
+    B = B or m.shape[0]
+    H = H or m.shape[1]
+    nb = m.shape[-1]
+    rows = B * H * nb
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=m.device)
+    if col_idx is None:
+        col_idx = torch.empty(rows * nb, dtype=torch.int32, device=m.device)
+    if ws is None:
+        ws = _ws(lib.csr_workspace_size(B, H, nb), m.device)
+    _check(lib.bsa_mask_to_csr(ptr, sb, sh, B, H, nb, row_ptr.data_ptr(), col_idx.data_ptr(), ws.data_ptr(),
+                               ws.numel(), _stream(m.device)))
+    return row_ptr, col_idx
+
+
+class AttnPlan:
+    """Reusable output and workspace buffers for repeated block_sparse_attn_fwd calls."""
+
+    def __init__(self, q: torch.Tensor, v: torch.Tensor, s_valid: Optional[int] = None, lse: bool = False):
+        lib = load()
+        self.shape = _shape(q, s_valid)
+        self.qk_code = _dtype_code(q)
+        self.ws = _ws(lib.attn_workspace_size(ctypes.byref(self.shape), self.qk_code), q.device)
+        odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+        self.out = torch.empty(q.shape, dtype=odt, device=q.device)
+        self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse else None
+
+
+def block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor,
+                          scale: Optional[float] = None, s_valid: Optional[int] = None,
+                          q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                          return_lse: bool = False, plan: Optional[AttnPlan] = None):
+    """Attention over the kept 64x64 tiles of `mask` ([B,H,nb,nb] or one [nb,nb] plane).
+
+    q, k: bf16, f32, or fp8 e4m3 codes (uint8 / float8_e4m3fn, then q_scale, k_scale
+    are float32 [B,H,nb]); v bf16 (f32 for f32 q, k). Returns O (and lse if asked).
+    """
+    lib = load()
+    if plan is None:
+        plan = AttnPlan(q, v, s_valid, lse=return_lse)
+    ptr, sb, sh, _m = _mask_strides(mask)
+    tq, tk, tv, to = _tensor(q), _tensor(k), _tensor(v), _tensor(plan.out)
+    qs = q_scale.data_ptr() if q_scale is not None else None
+    ks = k_scale.data_ptr() if k_scale is not None else None
+    lse_ptr = plan.lse.data_ptr() if (return_lse and plan.lse is not None) else None
+    _check(lib.block_sparse_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(plan.shape),
+                                     ptr, sb, sh, qs, ks, float(scale) if scale else 0.0, ctypes.byref(to), lse_ptr,
+                                     plan.ws.data_ptr(), plan.ws.numel(), _stream(q.device)))
+    if return_lse:
+        return plan.out, plan.lse
+    return plan.out
+
+
+def block_sparse_attn_fwd_csr(q, k, v, row_ptr, col_idx, scale=None, s_valid=None, q_scale=None, k_scale=None,
+                              return_lse=False, out=None, lse=None, ws=None):
+    """Attention over prebuilt kv lists (see mask_to_csr)."""
+    lib = load()
+    shp = _shape(q, s_valid)
+    code = _dtype_code(q)
+    if ws is None:
+        ws = _ws(lib.attn_csr_workspace_size(ctypes.byref(shp), code), q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if q.dtype == torch.float32 else torch.bfloat16,
+                          device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    tq, tk, tv, to = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    _check(lib.block_sparse_attn_fwd_csr(
+        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(shp), row_ptr.data_ptr(),
+        col_idx.data_ptr(), q_scale.data_ptr() if q_scale is not None else None,
+        k_scale.data_ptr() if k_scale is not None else None, float(scale) if scale else 0.0, ctypes.byref(to),
+        lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,307 @@
+// C-ABI entry points of libbsa (see include/bsa.h for the contract of each call).
+// Host-side only: argument validation, workspace carving and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/bsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+bsa_status fail(bsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSA_OK;
+  return fail(BSA_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t dtype_size(bsa_dtype t) { return t == BSA_F32 ? 4 : (t == BSA_BF16 ? 2 : 1); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+bsa_status check_shape(const bsa_shape* s, bool need_valid_d = true) {
+  if (!s) return fail(BSA_EINVAL, "shape is NULL");
+  if (s->N != 64) return fail(BSA_EUNSUPPORTED, "block size N=%d (only 64 is supported)", s->N);
+  if (s->B < 1 || s->H < 1) return fail(BSA_EINVAL, "B=%d, H=%d must be >= 1", s->B, s->H);
+  if ((int64_t)s->B * s->H > 65535) return fail(BSA_EUNSUPPORTED, "B*H=%lld exceeds 65535", (long long)s->B * s->H);
+  if (s->S < 64 || s->S % 64) return fail(BSA_EINVAL, "S=%d must be a positive multiple of 64", s->S);
+  if (s->S_valid < 1 || s->S_valid > s->S) return fail(BSA_EINVAL, "S_valid=%d must be in [1, S=%d]", s->S_valid, s->S);
+  if (need_valid_d && s->D != 64 && s->D != 128) return fail(BSA_EUNSUPPORTED, "head dim D=%d (64 or 128 supported)", s->D);
+  return BSA_OK;
+}
+
+bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* s) {
+  if (!t) return fail(BSA_EINVAL, "%s is NULL", name);
+  if (!t->ptr) return fail(BSA_EINVAL, "%s->ptr is NULL", name);
+  if (t->dtype != BSA_F32 && t->dtype != BSA_BF16 && t->dtype != BSA_FP8_E4M3FN)
+    return fail(BSA_EINVAL, "%s has an unknown dtype %d", name, (int)t->dtype);
+  if (!aligned16(t->ptr)) return fail(BSA_EINVAL, "%s->ptr is not 16-byte aligned", name);
+  const int64_t es = (int64_t)dtype_size(t->dtype);
+  if (t->sb < 0 || t->sh < 0 || t->ss < s->D)
+    return fail(BSA_EINVAL, "%s strides (sb=%lld, sh=%lld, ss=%lld) invalid for D=%d", name, (long long)t->sb,
+                (long long)t->sh, (long long)t->ss, s->D);
+  if ((t->ss * es) % 16 || (t->sh * es) % 16 || (t->sb * es) % 16)
+    return fail(BSA_EINVAL, "%s strides must be multiples of 16 bytes", name);
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_last_error(void) { return g_err.c_str(); }
+int bsa_abi_version(void) { return 1; }
+
+// ---------------------------------------------------------------------------
+size_t nabla_workspace_size(const bsa_shape* s) {
+  if (!s || s->S <= 0 || s->D <= 0) return 0;
+  const size_t nb = (size_t)s->S / 64, bh = (size_t)s->B * s->H;
+  return 2 * align256(bh * nb * (size_t)s->D * sizeof(double));
+}
+
+bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                            double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh, uint8_t* mask_out,
+                            void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  if ((st = check_tensor("q", q, shape)) != BSA_OK) return st;
+  if ((st = check_tensor("k", k, shape)) != BSA_OK) return st;
+  if (q->dtype != k->dtype || (q->dtype != BSA_BF16 && q->dtype != BSA_F32))
+    return fail(BSA_EUNSUPPORTED, "nabla_build_mask needs q and k both bf16 or both f32");
+  if (!(thr >= 0.0 && thr < 1.0)) return fail(BSA_EINVAL, "thr=%g must satisfy 0 <= thr < 1", thr);
+  if (!std::isfinite(scale)) return fail(BSA_EINVAL, "scale is not finite");
+  const int nb = shape->S / 64;
+  if (nb > 2048) return fail(BSA_EUNSUPPORTED, "nb=%d exceeds 2048 blocks per sequence", nb);
+  if (!mask_out) return fail(BSA_EINVAL, "mask_out is NULL");
+  if (or_mask && (or_sb < 0 || or_sh < 0)) return fail(BSA_EINVAL, "or_mask strides must be >= 0");
+  const size_t need = nabla_workspace_size(shape);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)shape->D);
+
+  const size_t bh = (size_t)shape->B * shape->H;
+  double* qbar = (double*)ws;
+  double* kbarT = (double*)((char*)ws + align256(bh * nb * (size_t)shape->D * sizeof(double)));
+  const int64_t qs[3] = {q->sb, q->sh, q->ss}, ks[3] = {k->sb, k->sh, k->ss};
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = bsa::launch_pool(q->dtype == BSA_F32, shape->D, q->ptr, qs, k->ptr, ks, shape->B, shape->H, nb,
+                                  qbar, kbarT, hs);
+  if (e != hipSuccess) return hip_status(e, "pool launch");
+  const uint64_t T_fixed = (uint64_t)std::ldexp(1.0 - thr, 60);
+  e = bsa::launch_select(qbar, kbarT, shape->B, shape->H, nb, shape->D, scale, T_fixed, or_mask, or_sb, or_sh,
+                         mask_out, hs);
+  return hip_status(e, "select launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t sta_workspace_size(const bsa_shape* s) {
+  if (!s || s->S <= 0) return 0;
+  return align256((size_t)(s->S / 64) * (bsa::STA_MAX_TILES + 1) * sizeof(int32_t));
+}
+
+bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
+                          int token_order, const int order_tile_thw[3], uint8_t* mask_out, void* ws, size_t ws_bytes,
+                          bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape, false)) != BSA_OK) return st;
+  if (!grid_thw || !tile_thw || !win_thw) return fail(BSA_EINVAL, "grid/tile/window arrays must not be NULL");
+  if (token_order != 0 && token_order != 1) return fail(BSA_EINVAL, "token_order=%d (0 row-major, 1 tile-major)", token_order);
+  if (token_order == 1 && !order_tile_thw) return fail(BSA_EINVAL, "order_tile_thw is NULL for tile-major order");
+  for (int x = 0; x < 3; ++x) {
+    if (grid_thw[x] < 1 || tile_thw[x] < 1 || win_thw[x] < 1)
+      return fail(BSA_EINVAL, "grid, tile and window sizes must be >= 1");
+    if (win_thw[x] % 2 == 0) return fail(BSA_EINVAL, "window sizes must be odd (centred window), got %d", win_thw[x]);
+    if ((grid_thw[x] + tile_thw[x] - 1) / tile_thw[x] > 1023)
+      return fail(BSA_EUNSUPPORTED, "more than 1023 tiles along one axis");
+    if (token_order == 1 && order_tile_thw[x] < 1) return fail(BSA_EINVAL, "order tile sizes must be >= 1");
+  }
+  const int64_t cells = (int64_t)grid_thw[0] * grid_thw[1] * grid_thw[2];
+  if (cells != shape->S_valid)
+    return fail(BSA_EINVAL, "T*H*W=%lld must equal S_valid=%d", (long long)cells, shape->S_valid);
+  if (!mask_out) return fail(BSA_EINVAL, "mask_out is NULL");
+  const size_t need = sta_workspace_size(shape);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  bsa::StaGeom g;
+  g.T = grid_thw[0]; g.H = grid_thw[1]; g.W = grid_thw[2];
+  g.tt = tile_thw[0]; g.th = tile_thw[1]; g.tw = tile_thw[2];
+  g.rt = win_thw[0] / 2; g.rh = win_thw[1] / 2; g.rw = win_thw[2] / 2;
+  g.order = token_order;
+  g.ot = token_order ? order_tile_thw[0] : 1;
+  g.oh = token_order ? order_tile_thw[1] : 1;
+  g.ow = token_order ? order_tile_thw[2] : 1;
+  g.S_valid = shape->S_valid;
+  g.nb = shape->S / 64;
+  return hip_status(bsa::launch_sta(g, (int32_t*)ws, mask_out, (hipStream_t)stream), "sta launch");
+}
+
+// ---------------------------------------------------------------------------
+bsa_status mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, int64_t b_n, bsa_stream_t stream) {
+  g_err.clear();
+  if (!dst || !a || !b) return fail(BSA_EINVAL, "mask_or: NULL pointer");
+  if (n < 0 || b_n < 1 || n % b_n) return fail(BSA_EINVAL, "mask_or: b_n=%lld must divide n=%lld", (long long)b_n, (long long)n);
+  if (n == 0) return BSA_OK;
+  return hip_status(bsa::launch_mask_or(dst, a, n, b, b_n, (hipStream_t)stream), "mask_or launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t csr_workspace_size(int B, int H, int nb) {
+  if (B < 1 || H < 1 || nb < 1) return 0;
+  return align256((size_t)B * H * nb * sizeof(int32_t));
+}
+
+static bsa_status check_mask_args(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H, int nb) {
+  if (!mask) return fail(BSA_EINVAL, "mask is NULL");
+  if (sb < 0 || sh < 0) return fail(BSA_EINVAL, "mask strides must be >= 0");
+  if (B < 1 || H < 1 || nb < 1) return fail(BSA_EINVAL, "B, H, nb must be >= 1");
+  if ((int64_t)B * H * nb >= (1ll << 31) / 2) return fail(BSA_EUNSUPPORTED, "too many rows");
+  if ((int64_t)B * H * nb * nb >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "B*H*nb*nb must be < 2^31");
+  return BSA_OK;
+}
+
+bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H, int nb,
+                           int32_t* row_ptr, int32_t* col_idx, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_mask_args(mask, mask_sb, mask_sh, B, H, nb)) != BSA_OK) return st;
+  if (!row_ptr || !col_idx) return fail(BSA_EINVAL, "row_ptr / col_idx is NULL");
+  const size_t need = csr_workspace_size(B, H, nb);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  return hip_status(bsa::launch_csr(mask, mask_sb, mask_sh, B, H, nb, row_ptr, col_idx, (int32_t*)ws,
+                                    (hipStream_t)stream), "csr launch");
+}
+
+// ---------------------------------------------------------------------------
+static size_t split_bytes(const bsa_shape* s) {
+  return align256((size_t)s->B * s->H * s->S * s->D * 2);
+}
+
+size_t attn_csr_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
+  if (!s || s->S <= 0 || s->D <= 0) return 0;
+  return qk_dtype == BSA_F32 ? 6 * split_bytes(s) : 0;   // hi/lo bf16 copies of f32 q, k, v
+}
+
+size_t attn_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
+  if (!s || s->S <= 0 || s->D <= 0) return 0;
+  const size_t rows = (size_t)s->B * s->H * (s->S / 64), nb = s->S / 64;
+  return align256((rows + 1) * 4) + align256(rows * nb * 4) + csr_workspace_size(s->B, s->H, (int)nb) +
+         attn_csr_workspace_size(s, qk_dtype);
+}
+
+static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const bsa_shape* shape,
+                              const int32_t* row_ptr, const int32_t* col_idx, const float* q_scale,
+                              const float* k_scale, double scale, const bsa_tensor* o, float* lse, void* split_ws,
+                              hipStream_t hs) {
+  bsa::AttnArgs a = {};
+  bsa::AttnMode mode;
+  if (q->dtype == BSA_BF16) mode = bsa::ATTN_BF16;
+  else if (q->dtype == BSA_F32) mode = bsa::ATTN_SPLIT_F32;
+  else mode = bsa::ATTN_FP8;
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)shape->D);
+  a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
+  a.k = k->ptr; a.k_sb = k->sb; a.k_sh = k->sh; a.k_ss = k->ss;
+  a.v = v->ptr; a.v_sb = v->sb; a.v_sh = v->sh; a.v_ss = v->ss;
+  a.o = (void*)o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.lse = lse;
+  a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.q_scale = q_scale; a.k_scale = k_scale;
+  a.B = shape->B; a.H = shape->H; a.nb = shape->S / 64; a.S = shape->S; a.S_valid = shape->S_valid; a.D = shape->D;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  if (mode == bsa::ATTN_SPLIT_F32) {
+    const size_t sb = split_bytes(shape);
+    uint16_t* p[6];
+    for (int x = 0; x < 6; ++x) p[x] = (uint16_t*)((char*)split_ws + x * sb);
+    const bsa_tensor* src[3] = {q, k, v};
+    for (int x = 0; x < 3; ++x) {
+      hipError_t e = bsa::launch_split_f32((const float*)src[x]->ptr, src[x]->sb, src[x]->sh, src[x]->ss, shape->B,
+                                           shape->H, shape->S, shape->D, p[2 * x], p[2 * x + 1], hs);
+      if (e != hipSuccess) return hip_status(e, "split launch");
+    }
+    a.q = p[0]; a.q_lo = p[1]; a.k = p[2]; a.k_lo = p[3]; a.v = p[4]; a.v_lo = p[5];
+  }
+  return hip_status(bsa::launch_attn(a, mode, hs), "attention launch");
+}
+
+static bsa_status check_attn(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const bsa_shape* shape,
+                             const float* q_scale, const float* k_scale, const bsa_tensor* o) {
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  if ((st = check_tensor("q", q, shape)) != BSA_OK) return st;
+  if ((st = check_tensor("k", k, shape)) != BSA_OK) return st;
+  if ((st = check_tensor("v", v, shape)) != BSA_OK) return st;
+  if ((st = check_tensor("o", o, shape)) != BSA_OK) return st;
+  if (q->dtype != k->dtype) return fail(BSA_EINVAL, "q and k must have the same dtype");
+  if (q->dtype == BSA_F32) {
+    if (v->dtype != BSA_F32 || o->dtype != BSA_F32) return fail(BSA_EINVAL, "f32 q/k need f32 v and f32 o");
+  } else {
+    if (v->dtype != BSA_BF16 || o->dtype != BSA_BF16)
+      return fail(BSA_EINVAL, "bf16/fp8 q/k need bf16 v and bf16 o");
+  }
+  if (q->dtype == BSA_FP8_E4M3FN) {
+    if (!q_scale || !k_scale) return fail(BSA_EINVAL, "fp8 q/k need q_scale and k_scale");
+  }
+  if ((int64_t)shape->B * shape->H * (shape->S / 64) >= (1ll << 30)) return fail(BSA_EUNSUPPORTED, "too many rows");
+  return BSA_OK;
+}
+
+bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                 const bsa_shape* shape, const uint8_t* mask, int64_t mask_sb, int64_t mask_sh,
+                                 const float* q_scale, const float* k_scale, double scale, const bsa_tensor* o,
+                                 float* lse, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_attn(q, k, v, shape, q_scale, k_scale, o)) != BSA_OK) return st;
+  if (!std::isfinite(scale)) return fail(BSA_EINVAL, "scale is not finite");
+  const int nb = shape->S / 64;
+  if ((st = check_mask_args(mask, mask_sb, mask_sh, shape->B, shape->H, nb)) != BSA_OK) return st;
+  const size_t need = attn_workspace_size(shape, q->dtype);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+  const size_t rows = (size_t)shape->B * shape->H * nb;
+  char* w = (char*)ws;
+  int32_t* row_ptr = (int32_t*)w;
+  w += align256((rows + 1) * 4);
+  int32_t* col_idx = (int32_t*)w;
+  w += align256(rows * nb * 4);
+  int32_t* counts = (int32_t*)w;
+  w += csr_workspace_size(shape->B, shape->H, nb);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = bsa::launch_csr(mask, mask_sb, mask_sh, shape->B, shape->H, nb, row_ptr, col_idx, counts, hs);
+  if (e != hipSuccess) return hip_status(e, "csr launch");
+  return attn_common(q, k, v, shape, row_ptr, col_idx, q_scale, k_scale, scale, o, lse, w, hs);
+}
+
+bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                     const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                                     const float* q_scale, const float* k_scale, double scale, const bsa_tensor* o,
+                                     float* lse, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_attn(q, k, v, shape, q_scale, k_scale, o)) != BSA_OK) return st;
+  if (!std::isfinite(scale)) return fail(BSA_EINVAL, "scale is not finite");
+  if (!row_ptr || !col_idx) return fail(BSA_EINVAL, "row_ptr / col_idx is NULL");
+  if (q->dtype == BSA_F32) {
+    const size_t need = attn_csr_workspace_size(shape, q->dtype);
+    if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  }
+  return attn_common(q, k, v, shape, row_ptr, col_idx, q_scale, k_scale, scale, o, lse, ws, (hipStream_t)stream);
+}
+
+}  // extern "C"

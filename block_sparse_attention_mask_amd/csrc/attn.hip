@@ -1,0 +1,378 @@
+// Block-sparse attention forward on gfx950 (bf16 MFMA; fp32 inputs via a hi/lo bf16
+// split; fp8 e4m3 Q/K with per-block scales).
+//
+// Method: FlashAttention (Daily Papers listing): exact attention computed tile by tile
+// with an online softmax (running maximum and normaliser), extended to block-sparse
+// attention by visiting only listed key blocks; FlashAttention-2: parallelise over
+// query blocks, keep the work of one query block inside one wave so that no
+// cross-wave communication is needed; NABLA (Pith review, "What carries the
+// argument"): the binary block mask tells the operator which N x N blocks to compute.
+//
+// Work decomposition: one wave (one workgroup) per query block of 64 tokens; the wave
+// walks that block's kv list. Per kv block:
+//   * the 64 x D K and V tiles are copied global -> LDS with direct-to-LDS 16-byte
+//     loads, each 1 KB instruction fully coalesced; 16-byte chunks are XOR-swizzled
+//     inside a row so that the MFMA operand reads below are bank-conflict free;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K rows are the A operand read with
+//     ds_read_b128, Q^T the B operand kept in registers for the whole block); in
+//     this transposed form each lane owns the scores of ONE query (its column), so
+//     the row max and the row sum need only a swap with the lane 32 apart;
+//   * online softmax in fp32 with exp2 and the scale folded into one multiply;
+//   * O^T += V^T P^T: P^T is the B operand straight from the S^T accumulators
+//     (converted to bf16, no data movement), V^T the A operand read from the
+//     row-major V tile with ds_read_b64_tr_b16 (transposing LDS read of gfx950).
+#include "common.h"
+#include "launch.h"
+
+namespace bsa {
+
+// ---- LDS tile geometry ------------------------------------------------------
+// A tile row holds RB = D * elem bytes = NCH 16-byte chunks. 256 bytes of LDS span
+// all 64 banks, i.e. 16 chunks; rows shorter than that share a bank line.
+template <int RB>
+struct TileGeom {
+  static constexpr int NCH = RB / 16;           // chunks per row
+  static constexpr int RPL = 16 / NCH;          // rows per 256-byte bank line
+  // K-style swizzle: 16 consecutive rows at the same chunk hit 16 distinct chunk slots
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPL) % NCH; }
+  // V-style swizzle: 4 consecutive rows x 4 consecutive chunks hit 16 distinct slots
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) % (NCH / 4)); }
+};
+
+// Copy a 64-row tile (row stride ss elements of esize bytes) global -> LDS, swizzled.
+template <int RB, bool VSWZ>
+__device__ __forceinline__ void load_tile_lds(const char* __restrict__ gsrc, int64_t row_bytes_stride,
+                                              char BSA_LDS* lds, int lane) {
+  using G = TileGeom<RB>;
+  constexpr int RPI = 1024 / RB;                // rows per 1 KB instruction
+  constexpr int NI = 64 / RPI;
+#pragma unroll
+  for (int t = 0; t < NI; ++t) {
+    const int r = t * RPI + lane / G::NCH;
+    const int pos = lane % G::NCH;
+    const int c = pos ^ (VSWZ ? G::swz_v(r) : G::swz_k(r));
+    const char* src = gsrc + (int64_t)r * row_bytes_stride + c * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src, (void BSA_LDS*)(lds + t * 1024), 16, 0, 0);
+  }
+}
+
+// byte offset of (row r, byte column cb) in a K-swizzled / V-swizzled tile
+template <int RB>
+__device__ __forceinline__ int koff(int r, int cb) {
+  using G = TileGeom<RB>;
+  return r * RB + (((cb >> 4) ^ G::swz_k(r)) << 4) + (cb & 15);
+}
+template <int RB>
+__device__ __forceinline__ int voff(int r, int cb) {
+  using G = TileGeom<RB>;
+  return r * RB + (((cb >> 4) ^ G::swz_v(r)) << 4) + (cb & 15);
+}
+
+__device__ __forceinline__ float partner(float x) {
+  // value of x in lane (l ^ 32)
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return lane_id() < 32 ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
+}
+
+// Eight consecutive accumulator values -> one bf16x8 MFMA operand (round to nearest even).
+// The operand is assembled from packed 32-bit words and cast as a whole vector: building
+// a bf16 vector element by element is mis-compiled by the current toolchain.
+__device__ __forceinline__ bf16x8_t pack_bf16x8(const f32x16_t& s, int base) {
+  i32x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = (int)((unsigned)f32_to_bf16_bits(s[base + 2 * e]) |
+                 ((unsigned)f32_to_bf16_bits(s[base + 2 * e + 1]) << 16));
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8_t join_bf16x8(s16x4_t a, s16x4_t b) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
+template <int MODE, int D>
+__global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int QK_ES = MODE == ATTN_FP8 ? 1 : 2;   // bytes per Q/K element
+  constexpr int RBK = D * QK_ES;                    // K tile row bytes
+  constexpr int RBV = D * 2;                        // V tile row bytes (bf16)
+  constexpr int KT_BYTES = 64 * RBK, VT_BYTES = 64 * RBV;
+  constexpr int NSPLIT = MODE == ATTN_SPLIT_F32 ? 2 : 1;
+  constexpr int DT = D / 32;                        // 32-wide d tiles of the output
+  constexpr int KS = MODE == ATTN_FP8 ? D / 64 : D / 16;   // k-steps of S = K Q^T
+
+  __shared__ __attribute__((aligned(1024))) char smem[NSPLIT * (KT_BYTES + VT_BYTES)];
+  char BSA_LDS* lds = (char BSA_LDS*)smem;
+  char BSA_LDS* kt_lds[NSPLIT];
+  char BSA_LDS* vt_lds[NSPLIT];
+#pragma unroll
+  for (int x = 0; x < NSPLIT; ++x) {
+    kt_lds[x] = lds + x * KT_BYTES;
+    vt_lds[x] = lds + NSPLIT * KT_BYTES + x * VT_BYTES;
+  }
+
+  const int l = threadIdx.x;
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int row = bh * a.nb + i;
+  const int start = a.row_ptr[row], end = a.row_ptr[row + 1];
+  const int l32 = l & 31, hi = l >> 5;
+
+  // element strides -> byte strides (split copies are contiguous [B,H,S,D] bf16)
+  const int64_t qes = MODE == ATTN_SPLIT_F32 ? 2 : QK_ES;
+  const char* qbase[NSPLIT];
+  const char* kbase[NSPLIT];
+  const char* vbase[NSPLIT];
+  int64_t q_rs, k_rs, v_rs;
+  if constexpr (MODE == ATTN_SPLIT_F32) {
+    const int64_t plane = (int64_t)a.S * D * 2;
+    const int64_t off = (int64_t)bh * plane;
+    qbase[0] = (const char*)a.q + off; qbase[1] = (const char*)a.q_lo + off;
+    kbase[0] = (const char*)a.k + off; kbase[1] = (const char*)a.k_lo + off;
+    vbase[0] = (const char*)a.v + off; vbase[1] = (const char*)a.v_lo + off;
+    q_rs = k_rs = v_rs = D * 2;
+  } else {
+    qbase[0] = (const char*)a.q + (b * a.q_sb + h * a.q_sh) * qes;
+    kbase[0] = (const char*)a.k + (b * a.k_sb + h * a.k_sh) * qes;
+    vbase[0] = (const char*)a.v + (b * a.v_sb + h * a.v_sh) * 2;
+    q_rs = a.q_ss * qes; k_rs = a.k_ss * qes; v_rs = a.v_ss * 2;
+  }
+
+  // ---- Q^T as the B operand: lane holds query qt*32 + l32
+  bf16x8_t qop[NSPLIT][2][MODE == ATTN_FP8 ? 1 : KS];
+  i32x8_t qop8[2][MODE == ATTN_FP8 ? KS : 1];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int64_t qrow = (int64_t)i * 64 + qt * 32 + l32;
+    if constexpr (MODE == ATTN_FP8) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const char* p = qbase[0] + qrow * q_rs + 64 * s + 32 * hi;
+        i32x4_t x0 = *(const i32x4_t*)p, x1 = *(const i32x4_t*)(p + 16);
+        qop8[qt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < NSPLIT; ++x)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          qop[x][qt][s] = *(const bf16x8_t*)(qbase[x] + qrow * q_rs + (16 * s + 8 * hi) * 2);
+    }
+  }
+
+  f32x16_t oacc[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[dt][qt][v] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  const float qsc = MODE == ATTN_FP8 ? a.q_scale[row] : 1.f;
+
+  for (int it = start; it < end; ++it) {
+    const int j = a.col_idx[it];
+    const int kv0 = j * 64;
+    if (kv0 >= a.S_valid) continue;           // block made only of padding
+    __syncthreads();                          // previous tile fully consumed
+#pragma unroll
+    for (int x = 0; x < NSPLIT; ++x) {
+      load_tile_lds<RBK, false>(kbase[x] + (int64_t)kv0 * k_rs, k_rs, kt_lds[x], l);
+      load_tile_lds<RBV, true>(vbase[x] + (int64_t)kv0 * v_rs, v_rs, vt_lds[x], l);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- S^T = K Q^T  (sacc[kt][qt]: kv = kt*32 + 8(v/4) + 4 hi + v%4, q = qt*32 + l32)
+    f32x16_t sacc[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[kt][qt][v] = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int r = kt * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (MODE == ATTN_FP8) {
+          const int cb = 64 * s + 32 * hi;
+          i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb));
+          i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb + 16));
+          i32x8_t ka = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            sacc[kt][qt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop8[qt][s], sacc[kt][qt], 0, 0,
+                                                                           0, 127, 0, 127);
+        } else {
+          const int cb = (16 * s + 8 * hi) * 2;
+          bf16x8_t ka = *(const bf16x8_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb));
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
+          if constexpr (MODE == ATTN_SPLIT_F32) {
+            bf16x8_t kl = *(const bf16x8_t BSA_LDS*)(kt_lds[1] + koff<RBK>(r, cb));
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+              sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[1][qt][s], sacc[kt][qt], 0, 0, 0);
+              sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- mask padded keys of the last block
+    if (kv0 + 64 > a.S_valid) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kv = kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (kv0 + kv >= a.S_valid) {
+            sacc[kt][0][v] = -INFINITY;
+            sacc[kt][1][v] = -INFINITY;
+          }
+        }
+    }
+
+    // ---- online softmax (log2 domain)
+    const float c = MODE == ATTN_FP8 ? a.scale_log2 * qsc * a.k_scale[bh * a.nb + j] : a.scale_log2;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][qt][v]);
+      mx = fmaxf(mx, partner(mx));
+      const float mnew = fmaxf(m_run[qt], mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
+      m_run[qt] = mnew;
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][v], c, -mnew));
+          sacc[kt][qt][v] = p;
+          ls += p;
+        }
+      l_run[qt] = l_run[qt] * alpha + ls;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][qt][v] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T
+    bf16x8_t pop[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) pop[qt][sp] = pack_bf16x8(sacc[sp >> 1][qt], 8 * (sp & 1));
+    const int g16 = l & 15, mbase = 16 * ((l >> 4) & 1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;   // byte column of this lane's 4 elements
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) {
+        const int K0 = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi;
+        const int ra = K0 + (g16 >> 2), rb = ra + 8;
+#pragma unroll
+        for (int x = 0; x < NSPLIT; ++x) {
+          s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra, cb)));
+          s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(rb, cb)));
+          const bf16x8_t va = join_bf16x8(v0, v1);
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qt][sp], oacc[dt][qt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, written row-major; padded rows and empty rows are 0
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = l_run[qt] + partner(l_run[qt]);
+    const int q = i * 64 + qt * 32 + l32;
+    const bool live = q < a.S_valid && lt > 0.f;
+    const float inv = live ? 1.f / lt : 0.f;
+    if (a.lse && hi == 0)
+      a.lse[(int64_t)bh * a.S + q] = live ? (m_run[qt] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hi;
+        if constexpr (MODE == ATTN_SPLIT_F32) {
+          float* o = (float*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d;
+          *(f32x4_t*)o = f32x4_t{oacc[dt][qt][4 * g] * inv, oacc[dt][qt][4 * g + 1] * inv,
+                                 oacc[dt][qt][4 * g + 2] * inv, oacc[dt][qt][4 * g + 3] * inv};
+        } else {
+          u16* o = (u16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d;
+          uint2 w;
+          w.x = f32_to_bf16_bits(oacc[dt][qt][4 * g] * inv) | ((unsigned)f32_to_bf16_bits(oacc[dt][qt][4 * g + 1] * inv) << 16);
+          w.y = f32_to_bf16_bits(oacc[dt][qt][4 * g + 2] * inv) | ((unsigned)f32_to_bf16_bits(oacc[dt][qt][4 * g + 3] * inv) << 16);
+          *(uint2*)o = w;
+        }
+      }
+  }
+}
+
+// f32 -> (hi, lo) bf16 split, written contiguous [B,H,S,D]
+__global__ __launch_bounds__(256) void split_f32_kernel(const float* __restrict__ x, int64_t sb, int64_t sh,
+                                                        int64_t ss, int H, int S, int D, u16* __restrict__ hi,
+                                                        u16* __restrict__ lo, int64_t total) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const int d = (int)(e % D);
+    const int64_t s = (e / D) % S;
+    const int64_t bh = e / ((int64_t)D * S);
+    const float v = x[(bh / H) * sb + (bh % H) * sh + s * ss + d];
+    const u16 hb = f32_to_bf16_bits(v);
+    hi[e] = hb;
+    lo[e] = f32_to_bf16_bits(v - bf16_bits_to_f32(hb));
+  }
+}
+
+hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, int B, int H, int S, int D,
+                            uint16_t* hi, uint16_t* lo, hipStream_t st) {
+  const int64_t total = (int64_t)B * H * S * D;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(split_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, sb, sh, ss, H, S, D, hi, lo,
+                     total);
+  return hipGetLastError();
+}
+
+template <int MODE, int D>
+static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
+  dim3 grid(a.nb, a.B * a.H);
+  hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs& a, AttnMode mode, hipStream_t st) {
+  if (a.D == 64) {
+    switch (mode) {
+      case ATTN_BF16: return launch_attn_t<ATTN_BF16, 64>(a, st);
+      case ATTN_SPLIT_F32: return launch_attn_t<ATTN_SPLIT_F32, 64>(a, st);
+      case ATTN_FP8: return launch_attn_t<ATTN_FP8, 64>(a, st);
+    }
+  } else {
+    switch (mode) {
+      case ATTN_BF16: return launch_attn_t<ATTN_BF16, 128>(a, st);
+      case ATTN_SPLIT_F32: return launch_attn_t<ATTN_SPLIT_F32, 128>(a, st);
+      case ATTN_FP8: return launch_attn_t<ATTN_FP8, 128>(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bsa

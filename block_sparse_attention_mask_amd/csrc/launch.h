@@ -1,0 +1,55 @@
+// Host-side launchers of the library's kernels (internal interface between the
+// C-ABI layer and the .hip translation units). All arguments are validated by the
+// caller; every launcher returns the HIP launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// nabla.hip
+hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* q_strides, const void* k,
+                       const int64_t* k_strides, int B, int H, int nb, double* qbar, double* kbarT,
+                       hipStream_t st);
+hipError_t launch_select(const double* qbar, const double* kbarT, int B, int H, int nb, int D, double scale,
+                         uint64_t T_fixed, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                         uint8_t* mask_out, hipStream_t st);
+
+// sta.hip
+struct StaGeom {
+  int T, H, W;           // latent grid
+  int tt, th, tw;        // window tile
+  int rt, rh, rw;        // window half-widths (window / 2)
+  int order;             // 0 row-major, 1 tile-major
+  int ot, oh, ow;        // tile of the tile-major order
+  int S_valid, nb;
+};
+constexpr int STA_MAX_TILES = 64;   // distinct window tiles touched by one 64-token block
+hipError_t launch_sta(const StaGeom& g, int32_t* tiles_ws, uint8_t* mask_out, hipStream_t st);
+
+// mask_ops.hip
+hipError_t launch_mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, int64_t b_n,
+                          hipStream_t st);
+hipError_t launch_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H, int nb,
+                      int32_t* row_ptr, int32_t* col_idx, int32_t* counts_ws, hipStream_t st);
+
+// attn.hip
+struct AttnArgs {
+  const void* q; int64_t q_sb, q_sh, q_ss;
+  const void* k; int64_t k_sb, k_sh, k_ss;
+  const void* v; int64_t v_sb, v_sh, v_ss;
+  // split copies (f32 inputs: hi parts in q/k/v above, lo parts here; contiguous)
+  const void* q_lo; const void* k_lo; const void* v_lo;
+  void* o; int64_t o_sb, o_sh, o_ss;
+  float* lse;
+  const int32_t* row_ptr; const int32_t* col_idx;
+  const float* q_scale; const float* k_scale;
+  int B, H, nb, S, S_valid, D;
+  float scale_log2;      // softmax scale * log2(e)
+};
+enum AttnMode { ATTN_BF16 = 0, ATTN_SPLIT_F32 = 1, ATTN_FP8 = 2 };
+hipError_t launch_attn(const AttnArgs& a, AttnMode mode, hipStream_t st);
+hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, int B, int H, int S, int D,
+                            uint16_t* hi, uint16_t* lo, hipStream_t st);
+
+}  // namespace bsa

@@ -1,0 +1,98 @@
+// Static sliding-tile (STA-style) block mask.
+//
+// Method: blog review "Fast Video Generation with SLIDING TILE ATTENTION", section
+// "Observation & Proposed Method": tokens are grouped into 3D tiles and every query
+// of a tile attends to the keys of the tiles in a local 3D window around it; with
+// tiles equal to the attention block there are no partially used blocks. Here the
+// window is centred on the query tile, cut off at the grid border, and a 64-token
+// block pair is kept iff some token of one may see some token of the other.
+//
+// Two kernels: sta_tiles lists the distinct window tiles touched by each block;
+// sta_pairs tests every block pair with those lists.
+#include "common.h"
+#include "launch.h"
+
+namespace bsa {
+
+// (t, h, w) of sequence position p under the token order of g.
+__device__ __forceinline__ void token_coord(const StaGeom& g, int p, int& t, int& h, int& w) {
+  if (g.order == 0) {
+    w = p % g.W;
+    h = (p / g.W) % g.H;
+    t = p / (g.W * g.H);
+    return;
+  }
+  // tile-major: tiles visited row-major; border tiles are smaller
+  const int slab = g.ot * g.H * g.W;           // tokens in a full t-slab of tiles
+  const int a = p / slab;
+  int rem = p - a * slab;
+  const int st = min(g.ot, g.T - a * g.ot);    // t-extent of this slab
+  const int rowsz = st * g.oh * g.W;
+  const int b = rem / rowsz;
+  rem -= b * rowsz;
+  const int sh = min(g.oh, g.H - b * g.oh);
+  const int tilesz = st * sh * g.ow;
+  const int c = rem / tilesz;
+  rem -= c * tilesz;
+  const int sw = min(g.ow, g.W - c * g.ow);
+  t = a * g.ot + rem / (sh * sw);
+  h = b * g.oh + (rem / sw) % sh;
+  w = c * g.ow + rem % sw;
+}
+
+__device__ __forceinline__ int32_t pack_tile(int a, int b, int c) { return (a << 20) | (b << 10) | c; }
+
+// One thread per block: distinct window tiles of its real tokens.
+__global__ __launch_bounds__(64) void sta_tiles_kernel(StaGeom g, int32_t* __restrict__ tiles) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= g.nb) return;
+  int32_t* out = tiles + (int64_t)i * (STA_MAX_TILES + 1);
+  int n = 0;
+  const int p1 = min((i + 1) * BSA_N, g.S_valid);
+  for (int p = i * BSA_N; p < p1; ++p) {
+    int t, h, w;
+    token_coord(g, p, t, h, w);
+    const int32_t key = pack_tile(t / g.tt, h / g.th, w / g.tw);
+    bool seen = false;
+    for (int x = 0; x < n; ++x) seen |= out[1 + x] == key;
+    if (!seen) out[1 + n++] = key;
+  }
+  out[0] = n;
+}
+
+// One workgroup per query block i; threads sweep the key blocks j.
+__global__ __launch_bounds__(256) void sta_pairs_kernel(StaGeom g, const int32_t* __restrict__ tiles,
+                                                        uint8_t* __restrict__ mask) {
+  __shared__ int32_t ti[STA_MAX_TILES];
+  __shared__ int nti;
+  const int i = blockIdx.x;
+  const int32_t* src = tiles + (int64_t)i * (STA_MAX_TILES + 1);
+  if (threadIdx.x == 0) nti = src[0];
+  if (threadIdx.x < STA_MAX_TILES) ti[threadIdx.x] = src[1 + threadIdx.x];
+  __syncthreads();
+  const int n_i = nti;
+  for (int j = threadIdx.x; j < g.nb; j += 256) {
+    const int32_t* tj = tiles + (int64_t)j * (STA_MAX_TILES + 1);
+    const int n_j = tj[0];
+    bool keep = false;
+    for (int x = 0; x < n_i && !keep; ++x) {
+      const int a0 = ti[x] >> 20, a1 = (ti[x] >> 10) & 1023, a2 = ti[x] & 1023;
+      for (int y = 0; y < n_j; ++y) {
+        const int32_t c = tj[1 + y];
+        const int c0 = c >> 20, c1 = (c >> 10) & 1023, c2 = c & 1023;
+        if (abs(a0 - c0) <= g.rt && abs(a1 - c1) <= g.rh && abs(a2 - c2) <= g.rw) { keep = true; break; }
+      }
+    }
+    mask[(int64_t)i * g.nb + j] = keep ? 1 : 0;
+  }
+}
+
+hipError_t launch_sta(const StaGeom& g, int32_t* tiles_ws, uint8_t* mask_out, hipStream_t st) {
+  hipLaunchKernelGGL(sta_tiles_kernel, dim3((g.nb + 63) / 64), dim3(64), 0, st, g, tiles_ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sta_pairs_kernel, dim3(g.nb), dim3(256), 0, st, g, (const int32_t*)tiles_ws, mask_out);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,198 @@
+/*
+ * bsa.h - block-sparse attention with adaptive (NABLA) and sliding-tile (STA)
+ * block masks, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *   [NABLA]  Pith review of "NABLA: Neighborhood Adaptive Block-Level Attention"
+ *            (arXiv 2507.13546), sections "What carries the argument", "Core claim"
+ *            and the referee report (minor comment 2 on Algorithm 1);
+ *   [STA]    blog review "Fast Video Generation with SLIDING TILE ATTENTION",
+ *            section "Observation & Proposed Method", and the STA abstract in the
+ *            Daily Papers listing;
+ *   [FA]     FlashAttention / FlashAttention-2 / FlashAttention-3 abstracts in the
+ *            Daily Papers listing (exact tiled attention, block-sparse extension,
+ *            online softmax);
+ *   [CalibAtt] the CalibAtt page (per-block skip lists handed to the kernel).
+ *
+ * Conventions shared by every call
+ *   - Tensors Q, K, V, O are [B, H, S, D] with D contiguous; the strides sb, sh, ss
+ *     of bsa_tensor are in ELEMENTS. S is a multiple of the block size N = 64;
+ *     tokens at positions >= S_valid are padding.
+ *   - Block masks are uint8 (0 = skip, nonzero = keep) [B, H, nb, nb] with
+ *     nb = S / 64, rows contiguous (row stride nb bytes); the per-(b,h) plane
+ *     strides are given in BYTES (0 broadcasts one plane to every head).
+ *   - Every pointer is a device pointer unless stated otherwise. The caller owns
+ *     all memory; the library never allocates, frees or synchronises.
+ *   - Every call validates its arguments on the host first and returns a status
+ *     without launching anything if they are invalid (bsa_last_error() then holds
+ *     a message for the calling thread). Work is enqueued on `stream` and runs
+ *     asynchronously; device faults surface at the caller's next synchronisation.
+ *     On an error the contents of the outputs are undefined.
+ *   - Calls are stateless and may be issued from several threads at once.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* bsa_stream_t;   /* same type as hipStream_t; NULL = default stream */
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_EINVAL = 1,         /* invalid argument (shape, stride, alignment, value)      */
+  BSA_EUNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim not 64/128)    */
+  BSA_EWORKSPACE = 3,     /* workspace missing or smaller than the *_workspace_size  */
+  BSA_EHIP = 4            /* a HIP launch failed; the message names the HIP error    */
+} bsa_status;
+
+typedef enum {
+  BSA_F32 = 0,
+  BSA_BF16 = 1,
+  BSA_FP8_E4M3FN = 2      /* OCP fp8 e4m3 (max 448), one scale per 64-token block    */
+} bsa_dtype;
+
+/* A [B, H, S, D] tensor: element (b,h,s,d) lives at ptr + b*sb + h*sh + s*ss + d. */
+typedef struct {
+  const void* ptr;
+  bsa_dtype dtype;
+  int64_t sb, sh, ss;
+} bsa_tensor;
+
+/* B batch, H heads, S padded sequence (multiple of N), S_valid real tokens
+ * (1 <= S_valid <= S), D head dim, N block size (must be 64). */
+typedef struct {
+  int B, H, S, S_valid, D, N;
+} bsa_shape;
+
+/* ---------------------------------------------------------------------------
+ * Adaptive block mask [NABLA, "What carries the argument"; "Core claim"].
+ *
+ * For every (b, h): Qbar, Kbar = means of Q, K over each block of N tokens
+ * (padding rows included as zeros); L = scale * Qbar Kbar^T ((S/N) x (S/N));
+ * P = softmax of each row of L; in each row, visit the entries by descending P
+ * (ties: ascending key-block index) and keep an entry iff the mass of the entries
+ * visited before it is < 1 - thr, i.e. keep the smallest prefix whose cumulative
+ * mass reaches 1 - thr; write the result in the original column order
+ * (referee report, minor comment 2: sort and cumsum along the key-block axis,
+ * then reorder). The top entry of a row is always kept.
+ *
+ *   q, k       bf16 or f32 [B,H,S,D] (the same dtype), D in {64, 128}
+ *   thr        0 <= thr < 1
+ *   scale      softmax temperature of the reduced map; <= 0 selects 1/sqrt(D)
+ *   or_mask    optional (NULL = none) uint8 mask OR'd into the result, e.g. a
+ *              sliding-tile mask [NABLA: the adaptive mask may be OR'd with STA];
+ *              plane strides or_sb, or_sh in bytes (0, 0 = one shared plane)
+ *   mask_out   uint8 [B,H,nb,nb], contiguous; written with 0/1
+ *   ws         device workspace of at least nabla_workspace_size(shape) bytes,
+ *              256-byte aligned; its contents on entry do not matter
+ * The reduced map, softmax and cumulative mass are evaluated in fp64 (the
+ * cumulative mass in 2^-60 fixed point), so a block whose exclusive cumulative
+ * mass lies within ~1e-12 of 1 - thr may be decided differently from an
+ * exact-arithmetic evaluation; all others are decided exactly.
+ * ------------------------------------------------------------------------- */
+size_t nabla_workspace_size(const bsa_shape* shape);
+bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
+                            double thr, double scale,
+                            const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                            uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Static sliding-tile block mask [STA, "Observation & Proposed Method"].
+ *
+ * The T x H x W latent grid (T*H*W == shape->S_valid) is cut into tiles of
+ * tile_thw tokens (smaller tiles at the far borders if they do not divide).
+ * A query tile a sees key tile c iff |a - c| <= win_thw / 2 on every axis
+ * (odd window sizes, centred, cut off at the grid border, not shifted).
+ * Sequence position p holds grid cell token_order(p): order 0 = row-major (t,h,w);
+ * order 1 = tile-major with tiles of order_tile_thw tokens visited row-major and
+ * tokens row-major inside each tile. Block pair (i, j) is kept iff some real
+ * token of block i may see some real token of block j (whole blocks are computed).
+ *
+ *   grid_thw, tile_thw, win_thw, order_tile_thw   host arrays of 3 ints
+ *                  (order_tile_thw may be NULL for order 0)
+ *   mask_out       uint8 [nb, nb] (one plane shared by all heads), contiguous
+ *   ws             workspace of at least sta_workspace_size(shape) bytes
+ * ------------------------------------------------------------------------- */
+size_t sta_workspace_size(const bsa_shape* shape);
+bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const int tile_thw[3],
+                          const int win_thw[3], int token_order, const int order_tile_thw[3],
+                          uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Union of block masks [NABLA: adaptive mask OR sliding-tile mask].
+ *   dst[i] = (a[i] | b[i % b_n]) != 0 for 0 <= i < n; b_n divides n (b_n == n is a
+ *   plain elementwise OR; b_n == nb*nb broadcasts one plane over every head).
+ *   dst may alias a.
+ * ------------------------------------------------------------------------- */
+bsa_status mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, int64_t b_n,
+                   bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Mask compaction into per-query-block kv lists [CalibAtt skip lists].
+ *   mask       uint8 [B,H,nb,nb] with plane strides mask_sb, mask_sh (bytes)
+ *   row_ptr    int32 [B*H*nb + 1]; row r = (b*H + h)*nb + i
+ *   col_idx    int32 [B*H*nb*nb] capacity; row r's kept kv blocks, ascending, are
+ *              col_idx[row_ptr[r] .. row_ptr[r+1])
+ *   ws         at least csr_workspace_size(B, H, nb) bytes
+ * ------------------------------------------------------------------------- */
+size_t csr_workspace_size(int B, int H, int nb);
+bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H,
+                           int nb, int32_t* row_ptr, int32_t* col_idx, void* ws, size_t ws_bytes,
+                           bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention forward [FA: exact tiled attention with online softmax,
+ * extended to block-sparse attention; NABLA: the mask tells the operator which
+ * N x N blocks to compute].
+ *
+ * For query token p of head (b,h): key token q is allowed iff mask[p/64][q/64]
+ * is nonzero and q < S_valid;  O_p = sum_q softmax_q(scale * <Q_p, K_q>) V_q over
+ * allowed q. Only kept 64 x 64 tiles are computed. Query rows >= S_valid, and
+ * query rows with no allowed key, get O = 0 and lse = -inf.
+ *
+ *   q, k       bf16 [B,H,S,D]; or both f32; or both fp8 e4m3fn (then q_scale,
+ *              k_scale are float [B,H,nb] contiguous: the value of a code c in
+ *              block j is fp8(c) * scale[b,h,j]); D in {64, 128}
+ *   v          bf16 (f32 when q, k are f32) [B,H,S,D]
+ *   scale      softmax scale; <= 0 selects 1/sqrt(D)
+ *   o          output [B,H,S,D]: bf16, or f32 when q, k are f32; o->ptr is written
+ *   lse        optional (NULL = none) float [B,H,S] natural-log sum of exp
+ *   ws         at least attn_workspace_size(shape, q->dtype) bytes, 256-byte
+ *              aligned (holds the kv lists and, for f32 inputs, hi/lo bf16 copies)
+ * All of q, k, v, o must have 16-byte aligned rows (ss*elem_size % 16 == 0 and the
+ * base pointers 16-byte aligned).
+ * block_sparse_attn_fwd_csr takes kv lists already built by bsa_mask_to_csr (for
+ * masks reused across calls) and needs attn_csr_workspace_size(shape, q->dtype)
+ * bytes (zero for bf16 and fp8 inputs; ws may then be NULL).
+ * ------------------------------------------------------------------------- */
+size_t attn_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
+bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                 const bsa_shape* shape,
+                                 const uint8_t* mask, int64_t mask_sb, int64_t mask_sh,
+                                 const float* q_scale, const float* k_scale, double scale,
+                                 const bsa_tensor* o, float* lse,
+                                 void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+size_t attn_csr_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
+bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                     const bsa_shape* shape,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     const float* q_scale, const float* k_scale, double scale,
+                                     const bsa_tensor* o, float* lse,
+                                     void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* bsa_last_error(void);
+
+/* Version of this interface (incremented on incompatible changes). */
+int bsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

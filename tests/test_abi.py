@@ -1,0 +1,113 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments
+on the host before any launch (CPU only: no compute call reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_mask_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bsa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 13
+    assert sorted(names) == sorted(bsa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.bsa_abi_version() == 1
+
+
+def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
+    return bsa.Tensor(ptr, dtype, 0, 0, ss)
+
+
+def _nabla(lib, shape, thr=0.2, q=None, k=None, mask=4096, ws=8192, ws_bytes=1 << 40):
+    q = q or _t()
+    k = k or _t()
+    return lib.nabla_build_mask(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), thr, 0.0, None, 0, 0, mask,
+                                ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("shape,thr,msg", [
+    (bsa.Shape(1, 2, 256, 256, 128, 64), 1.0, "thr"),
+    (bsa.Shape(1, 2, 256, 256, 128, 64), -0.1, "thr"),
+    (bsa.Shape(1, 2, 250, 250, 128, 64), 0.2, "multiple of 64"),
+    (bsa.Shape(1, 2, 256, 300, 128, 64), 0.2, "S_valid"),
+    (bsa.Shape(0, 2, 256, 256, 128, 64), 0.2, "B="),
+    (bsa.Shape(1, 2, 256, 256, 96, 64), 0.2, "head dim"),
+    (bsa.Shape(1, 2, 256, 256, 128, 32), 0.2, "block size"),
+    (bsa.Shape(1, 1, 64 * 2049, 64 * 2049, 128, 64), 0.2, "2048"),
+])
+def test_nabla_rejects_bad_arguments(lib, shape, thr, msg):
+    st = _nabla(lib, shape, thr)
+    assert st in (1, 2)
+    assert msg in lib.bsa_last_error().decode()
+
+
+def test_nabla_rejects_misaligned_and_mixed(lib):
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    assert _nabla(lib, shape, q=_t(ptr=258)) == 1
+    assert _nabla(lib, shape, q=_t(ss=100)) == 1
+    assert _nabla(lib, shape, k=_t(dtype=bsa.BSA_F32)) == 2
+    assert _nabla(lib, shape, ws_bytes=16) == 3
+    assert "workspace" in lib.bsa_last_error().decode()
+    assert _nabla(lib, shape, mask=None) == 1
+
+
+def test_sta_rejects_bad_geometry(lib):
+    shape = bsa.Shape(1, 1, 256, 256, 64, 64)
+    a3 = ctypes.c_int * 3
+    st = lib.sta_build_mask(ctypes.byref(shape), a3(4, 8, 8), a3(4, 8, 8), a3(3, 2, 3), 0, None, 4096, 8192,
+                            1 << 20, None)
+    assert st == 1 and "odd" in lib.bsa_last_error().decode()
+    st = lib.sta_build_mask(ctypes.byref(shape), a3(4, 8, 9), a3(4, 8, 8), a3(3, 3, 3), 0, None, 4096, 8192,
+                            1 << 20, None)
+    assert st == 1 and "S_valid" in lib.bsa_last_error().decode()
+    st = lib.sta_build_mask(ctypes.byref(shape), a3(4, 8, 8), a3(4, 8, 8), a3(3, 3, 3), 1, None, 4096, 8192,
+                            1 << 20, None)
+    assert st == 1
+
+
+def test_mask_or_and_csr_reject(lib):
+    assert lib.mask_or(4096, 4096, 10, 8192, 3, None) == 1
+    assert lib.mask_or(None, 4096, 10, 8192, 10, None) == 1
+    assert lib.bsa_mask_to_csr(4096, -1, 0, 1, 1, 4, 8192, 8192, 8192, 1 << 20, None) == 1
+    assert lib.bsa_mask_to_csr(4096, 0, 0, 1, 1, 4, 8192, 8192, 8192, 0, None) == 3
+
+
+def test_attention_rejects(lib):
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    q, k, v, o = _t(), _t(), _t(), _t()
+    ws = lib.attn_workspace_size(ctypes.byref(shape), bsa.BSA_BF16)
+    assert ws > 0
+    args = lambda **kw: dict(dict(q=q, k=k, v=v, o=o, mask=4096, qs=None, ks=None, ws=4096, wsb=ws), **kw)
+
+    def call(a):
+        return lib.block_sparse_attn_fwd(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                                         ctypes.byref(shape), a["mask"], 0, 0, a["qs"], a["ks"], 0.0,
+                                         ctypes.byref(a["o"]), None, a["ws"], a["wsb"], None)
+    assert call(args(v=_t(dtype=bsa.BSA_F32))) == 1
+    assert call(args(q=_t(dtype=bsa.BSA_FP8_E4M3FN, ss=128), k=_t(dtype=bsa.BSA_FP8_E4M3FN))) == 1   # no scales
+    assert "scale" in lib.bsa_last_error().decode()
+    assert call(args(mask=None)) == 1
+    assert call(args(wsb=ws - 1)) == 3
+    assert call(args(ws=4097)) == 1
+    f32 = lib.attn_workspace_size(ctypes.byref(shape), bsa.BSA_F32)
+    assert f32 > ws            # f32 inputs need room for their bf16 hi/lo copies

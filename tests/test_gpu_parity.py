@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Masks are compared bit for bit, except blocks whose exclusive cumulative mass lies
+within 1e-6 of 1 - thr (counted and printed). Attention is compared with the oracle's
+mask, max |err| <= 2e-2 and mean |err| <= 2e-3, on every query block where the oracle
+is cheap and on seeded samples (always with the first, last, densest and sparsest rows)
+at the full workload sizes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import get_config, make_inputs, quantize_fp8_blocks
+from parity_util import (MAX_ERR, MEAN_ERR, attention_errors, compare_masks, f64, oracle_attention_blocks,
+                         oracle_masks, sample_blocks)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sta_plane(cfg):
+    if cfg.sta is None:
+        return None
+    return oracle.sta_block_mask(cfg.grid, cfg.order, cfg.order_tile, cfg.sta.tile, cfg.sta.window, 64, cfg.S)
+
+
+def _gpu_sta(bsa, cfg):
+    return bsa.sta_build_mask(cfg.S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                              order_tile=cfg.order_tile, device=DEV)
+
+
+# ----------------------------------------------------------------------------- masks
+@pytest.mark.parametrize("cid,heads", [(1, None), (2, None), (3, 40)])
+def test_nabla_mask_parity(gpu_lib, cid, heads):
+    cfg = get_config(cid, heads)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    for thr in cfg.thrs:
+        print(f"[mask] config {cid} thr {thr} shape {tuple(q.shape)}", flush=True)
+        m = gpu_lib.nabla_build_mask(q, k, thr)
+        torch.cuda.synchronize()
+        keep, E = oracle_masks(q, k, thr)
+        bad, near = compare_masks(m, keep, E, thr)
+        print(f"  mismatches {bad}, near-threshold entries {near}, kept {keep.mean():.4f}", flush=True)
+        assert bad == 0
+
+
+def test_nabla_mask_sweep_with_sta_or(gpu_lib):
+    cfg = get_config(5, heads=6)
+    q, k, v = make_inputs(cfg, seed=1, device=DEV)
+    plane = _sta_plane(cfg)
+    sta = _gpu_sta(gpu_lib, cfg)
+    for thr in cfg.thrs:
+        m = gpu_lib.nabla_build_mask(q, k, thr, or_mask=sta)
+        torch.cuda.synchronize()
+        keep, E = oracle_masks(q, k, thr, or_plane=plane)
+        bad, near = compare_masks(m, keep, E, thr)
+        print(f"[mask] config 5 thr {thr}: mismatches {bad}, near {near}, kept {keep.mean():.4f}", flush=True)
+        assert bad == 0
+
+
+def test_nabla_degenerate_rows(gpu_lib):
+    """All-equal rows (q = 0): every key block ties; ties go by ascending index."""
+    B, H, S, D = 1, 3, 64 * 37, 128
+    q = torch.zeros(B, H, S, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(B, H, S, D, device=DEV).to(torch.bfloat16)
+    for thr in (0.0, 0.3, 0.5, 0.99):
+        m = gpu_lib.nabla_build_mask(q, k, thr)
+        keep, E = oracle_masks(q, k, thr)
+        bad, near = compare_masks(m, keep, E, thr)
+        assert bad == 0, (thr, bad)
+
+
+def test_nabla_thr_edges_and_determinism(gpu_lib):
+    cfg = get_config(2, heads=4)
+    q, k, _ = make_inputs(cfg, seed=3, device=DEV)
+    for thr in (0.0, 0.999):
+        m = gpu_lib.nabla_build_mask(q, k, thr)
+        keep, E = oracle_masks(q, k, thr)
+        assert compare_masks(m, keep, E, thr)[0] == 0
+    a = gpu_lib.nabla_build_mask(q, k, 0.1).clone()
+    b = gpu_lib.nabla_build_mask(q, k, 0.1)
+    assert torch.equal(a, b)
+
+
+def test_nabla_f32_and_d64(gpu_lib):
+    cfg = get_config(1)
+    q, k, _ = make_inputs(cfg, seed=4, device=DEV)
+    # a longer f32 sequence with a ragged number of 16-row groups
+    q2 = torch.randn(2, 2, 64 * 21, 64, device=DEV)
+    k2 = torch.randn(2, 2, 64 * 21, 64, device=DEV)
+    for (qq, kk) in ((q, k), (q2, k2), (q2.to(torch.bfloat16), k2.to(torch.bfloat16))):
+        m = gpu_lib.nabla_build_mask(qq, kk, 0.2)
+        keep, E = oracle_masks(qq, kk, 0.2)
+        assert compare_masks(m, keep, E, 0.2)[0] == 0
+
+
+# ----------------------------------------------------------------------------- STA / OR / CSR
+@pytest.mark.parametrize("cid", [2, 4, 5])
+def test_sta_mask_parity(gpu_lib, cid):
+    cfg = get_config(cid)
+    g = _gpu_sta(gpu_lib, cfg).cpu().numpy().astype(bool)
+    assert np.array_equal(g, _sta_plane(cfg))
+
+
+@pytest.mark.parametrize("grid,order,otile,tile,window", [
+    ((3, 5, 7), "row", None, (2, 2, 3), (3, 3, 3)),
+    ((5, 6, 7), "tile", (2, 4, 4), (2, 4, 4), (1, 3, 5)),
+    ((4, 9, 10), "tile", (3, 4, 4), (2, 3, 5), (3, 1, 3)),
+])
+def test_sta_ragged_geometries(gpu_lib, grid, order, otile, tile, window):
+    Sv = int(np.prod(grid))
+    S = -(-Sv // 64) * 64
+    g = gpu_lib.sta_build_mask(S, Sv, grid, tile, window, order=order, order_tile=otile, device=DEV)
+    ref = oracle.sta_block_mask(grid, order, otile, tile, window, 64, S)
+    assert np.array_equal(g.cpu().numpy().astype(bool), ref)
+
+
+def test_mask_or_and_csr(gpu_lib):
+    rng = np.random.default_rng(0)
+    a = rng.random((2, 3, 37, 37)) < 0.2
+    bplane = rng.random((37, 37)) < 0.3
+    a[0, 1, 5] = False
+    ta = torch.from_numpy(a.astype(np.uint8)).to(DEV)
+    tb = torch.from_numpy(bplane.astype(np.uint8)).to(DEV)
+    u = gpu_lib.mask_or(ta, tb)
+    ref = oracle.mask_or(a, np.broadcast_to(bplane, a.shape))
+    assert np.array_equal(u.cpu().numpy().astype(bool), ref)
+    z = torch.zeros_like(ta)
+    z[0, 1] = 1
+    rp, ci = gpu_lib.mask_to_csr(ta)
+    rp_ref, ci_ref = oracle.mask_to_csr(a.reshape(-1, 37))
+    assert np.array_equal(rp.cpu().numpy(), rp_ref)
+    assert np.array_equal(ci.cpu().numpy()[:rp_ref[-1]], ci_ref)
+
+
+# ----------------------------------------------------------------------------- attention
+def _attn_check(gpu_lib, cfg, q, k, v, keep, blocks, **kw):
+    mask = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+    out = gpu_lib.block_sparse_attn_fwd(q, k, v, mask, s_valid=cfg.S_valid, **{x: y for x, y in kw.items()
+                                                                                if x in ("q_scale", "k_scale")})
+    torch.cuda.synchronize()
+    ref = oracle_attention_blocks(q, k, v, keep, blocks, cfg.S_valid, q_deq=kw.get("q_deq"), k_deq=kw.get("k_deq"))
+    mx, mean = attention_errors(out, ref)
+    print(f"[attn] {cfg.name}: {len(blocks)} query blocks, max err {mx:.3e}, mean err {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
+    return out
+
+
+def test_attention_config1_f32_full(gpu_lib):
+    cfg = get_config(1)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    keep, _ = oracle_masks(q, k, 0.2)
+    blocks = [(0, h, i) for h in range(cfg.H) for i in range(cfg.nb)]
+    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
+    # the same data in bf16 with head_dim 64
+    _attn_check(gpu_lib, cfg, q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), keep, blocks)
+
+
+def test_attention_config2_full(gpu_lib):
+    cfg = get_config(2)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    keep, _ = oracle_masks(q, k, 0.1, or_plane=_sta_plane(cfg))
+    blocks = [(0, h, i) for h in range(cfg.H) for i in range(cfg.nb)]
+    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
+
+
+def test_attention_config3_sampled(gpu_lib):
+    cfg = get_config(3)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    heads = [0, 17, 39]
+    qs, ks = q[:, heads], k[:, heads]
+    keep_s, _ = oracle_masks(qs, ks, 0.2)
+    keep = np.zeros((1, cfg.H, cfg.nb, cfg.nb), dtype=bool)
+    keep[:, :, np.arange(cfg.nb), np.arange(cfg.nb)] = True       # other heads: diagonal only
+    keep[:, heads] = keep_s
+    blocks = [(0, h, i) for (_, h, i) in sample_blocks(keep[:, heads], 10, seed=1)]
+    blocks = [(0, heads[h], i) for (_, h, i) in blocks]
+    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
+
+
+def test_attention_config4_sta_sampled(gpu_lib):
+    cfg = get_config(4, heads=6)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    plane = _sta_plane(cfg)
+    keep = np.broadcast_to(plane, (1, cfg.H, cfg.nb, cfg.nb)).copy()
+    blocks = sample_blocks(keep, 6, seed=2)
+    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
+
+
+def test_attention_config5_fp8_sampled(gpu_lib):
+    cfg = get_config(5, heads=3)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    keep, _ = oracle_masks(q, k, 0.2, or_plane=_sta_plane(cfg))
+    blocks = sample_blocks(keep, 8, seed=3)
+    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
+    q8, qs = quantize_fp8_blocks(q)
+    k8, ks = quantize_fp8_blocks(k)
+    deq = lambda c, s: (c.view(torch.float8_e4m3fn).to(torch.float64).reshape(*s.shape, 64, -1)
+                        * s.to(torch.float64)[..., None, None]).reshape(c.shape).cpu().numpy()
+    _attn_check(gpu_lib, cfg, q8, k8, v, keep, blocks, q_scale=qs, k_scale=ks, q_deq=deq(q8, qs),
+                k_deq=deq(k8, ks))
+
+
+def test_attention_edge_rows(gpu_lib):
+    """Empty kv lists give zeros; a fully masked padding tail; D=64 and D=128."""
+    for D in (64, 128):
+        B, H, S, Sv = 1, 2, 64 * 6, 64 * 5 + 7
+        q = torch.randn(B, H, S, D, device=DEV).to(torch.bfloat16)
+        k = torch.randn(B, H, S, D, device=DEV).to(torch.bfloat16)
+        v = torch.randn(B, H, S, D, device=DEV).to(torch.bfloat16)
+        keep = np.random.default_rng(D).random((B, H, 6, 6)) < 0.5
+        keep[0, 0, 2] = False              # a row with no kept block
+        keep[0, 1, 3] = False
+        keep[0, 1, 3, 5] = True            # only the partly padded last block
+        mask = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+        out, lse = gpu_lib.block_sparse_attn_fwd(q, k, v, mask, s_valid=Sv, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.all(out[0, 0, 128:192] == 0)
+        assert torch.all(out[:, :, Sv:] == 0)
+        assert torch.isinf(lse[0, 0, 128:192]).all()
+        for h in range(H):
+            O, L = oracle.block_sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), keep[0, h], 64, Sv)
+            assert np.abs(f64(out[0, h]) - O).max() <= MAX_ERR
+            fin = np.isfinite(L)
+            assert np.abs(f64(lse[0, h])[fin] - L[fin]).max() < 1e-3
+
+
+def test_attention_determinism_and_csr_entry(gpu_lib):
+    cfg = get_config(2, heads=4)
+    q, k, v = make_inputs(cfg, seed=5, device=DEV)
+    mask = gpu_lib.nabla_build_mask(q, k, 0.1)
+    a = gpu_lib.block_sparse_attn_fwd(q, k, v, mask).clone()
+    b = gpu_lib.block_sparse_attn_fwd(q, k, v, mask).clone()
+    assert torch.equal(a, b)
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    c = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci)
+    assert torch.equal(a, c)
+
+
+def test_full_mask_equals_dense(gpu_lib):
+    cfg = get_config(2, heads=2)
+    q, k, v = make_inputs(cfg, seed=6, device=DEV)
+    ones = torch.ones(cfg.nb, cfg.nb, dtype=torch.uint8, device=DEV)
+    out = gpu_lib.block_sparse_attn_fwd(q, k, v, ones)
+    torch.cuda.synchronize()
+    ref = torch.nn.functional.scaled_dot_product_attention(q.cpu().double(), k.cpu().double(), v.cpu().double())
+    err = (out.cpu().double() - ref).abs()
+    assert err.max().item() <= MAX_ERR and err.mean().item() <= MEAN_ERR
