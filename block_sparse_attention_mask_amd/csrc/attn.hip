@@ -21,6 +21,8 @@
 //   * O^T += V^T P^T: P^T is the B operand straight from the S^T accumulators
 //     (converted to bf16, no data movement), V^T the A operand read from the
 //     row-major V tile with ds_read_b64_tr_b16 (transposing LDS read of gfx950).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -39,20 +41,43 @@ struct TileGeom {
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) % (NCH / 4)); }
 };
 
-// Copy a 64-row tile (row stride ss elements of esize bytes) global -> LDS, swizzled.
+// One direct-to-LDS 16-byte load per lane: lane L's 16 bytes at gbase + voff land at
+// LDS address lds + 16 L. Issued from inline asm so that the compiler does not put a
+// blanket wait for every outstanding load in front of each LDS read; the kernel
+// waits for exactly the tiles it needs (wait_vm). The instruction has no register
+// result; its address operands are read at issue. M0 (the LDS base of the DMA) is
+// saved and restored around it.
+__device__ __forceinline__ void dma16(const char* gbase, unsigned voff, unsigned lds) {
+  unsigned sv;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(sv)
+      : "v"(voff), "s"(gbase), "s"(lds)
+      : "memory");
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Copy a 64-row tile (row stride rs bytes) global -> LDS in 1 KB instructions, each
+// fully coalesced; 16-byte chunk c of row r is stored at chunk slot c ^ swizzle(r).
 template <int RB, bool VSWZ>
-__device__ __forceinline__ void load_tile_lds(const char* __restrict__ gsrc, int64_t row_bytes_stride,
-                                              char BSA_LDS* lds, int lane) {
+__device__ __forceinline__ void load_tile_lds(const char* gtile, unsigned rs, unsigned lds, int lane) {
   using G = TileGeom<RB>;
   constexpr int RPI = 1024 / RB;                // rows per 1 KB instruction
   constexpr int NI = 64 / RPI;
 #pragma unroll
   for (int t = 0; t < NI; ++t) {
     const int r = t * RPI + lane / G::NCH;
-    const int pos = lane % G::NCH;
-    const int c = pos ^ (VSWZ ? G::swz_v(r) : G::swz_k(r));
-    const char* src = gsrc + (int64_t)r * row_bytes_stride + c * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (void BSA_LDS*)(lds + t * 1024), 16, 0, 0);
+    const int c = (lane % G::NCH) ^ (VSWZ ? G::swz_v(r) : G::swz_k(r));
+    dma16(gtile, (unsigned)r * rs + (unsigned)c * 16u, lds + t * 1024);
   }
 }
 
@@ -91,7 +116,23 @@ __device__ __forceinline__ bf16x8_t join_bf16x8(s16x4_t a, s16x4_t b) {
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// The running maximum is only moved when a tile's maximum exceeds it by more than
+// RESCALE_TAU (log2 units): the probabilities then stay below 2^TAU, far inside the
+// fp32 range, and the rescale of the output accumulators is skipped on most tiles.
+constexpr float RESCALE_TAU = 8.f;
+
 // MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
+//
+// Software pipeline (one wave): at the top of iteration j the K_j and V_j tiles are
+// read from LDS into registers; the DMA of K_{j+1}, V_{j+1} into the same LDS buffers
+// is issued right after, and the MFMA and softmax work of tile j runs while it flies.
 template <int MODE, int D>
 __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int QK_ES = MODE == ATTN_FP8 ? 1 : 2;   // bytes per Q/K element
@@ -101,6 +142,7 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NSPLIT = MODE == ATTN_SPLIT_F32 ? 2 : 1;
   constexpr int DT = D / 32;                        // 32-wide d tiles of the output
   constexpr int KS = MODE == ATTN_FP8 ? D / 64 : D / 16;   // k-steps of S = K Q^T
+  using KOp = typename std::conditional<MODE == ATTN_FP8, i32x8_t, bf16x8_t>::type;
 
   __shared__ __attribute__((aligned(1024))) char smem[NSPLIT * (KT_BYTES + VT_BYTES)];
   char BSA_LDS* lds = (char BSA_LDS*)smem;
@@ -140,25 +182,22 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- Q^T as the B operand: lane holds query qt*32 + l32
-  bf16x8_t qop[NSPLIT][2][MODE == ATTN_FP8 ? 1 : KS];
-  i32x8_t qop8[2][MODE == ATTN_FP8 ? KS : 1];
+  KOp qop[NSPLIT][2][KS];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int64_t qrow = (int64_t)i * 64 + qt * 32 + l32;
-    if constexpr (MODE == ATTN_FP8) {
+#pragma unroll
+    for (int x = 0; x < NSPLIT; ++x)
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const char* p = qbase[0] + qrow * q_rs + 64 * s + 32 * hi;
-        i32x4_t x0 = *(const i32x4_t*)p, x1 = *(const i32x4_t*)(p + 16);
-        qop8[qt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      }
-    } else {
-#pragma unroll
-      for (int x = 0; x < NSPLIT; ++x)
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
+        if constexpr (MODE == ATTN_FP8) {
+          const char* p = qbase[0] + qrow * q_rs + 64 * s + 32 * hi;
+          i32x4_t x0 = *(const i32x4_t*)p, x1 = *(const i32x4_t*)(p + 16);
+          qop[x][qt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        } else {
           qop[x][qt][s] = *(const bf16x8_t*)(qbase[x] + qrow * q_rs + (16 * s + 8 * hi) * 2);
-    }
+        }
+      }
   }
 
   f32x16_t oacc[DT][2];
@@ -170,23 +209,44 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
       for (int v = 0; v < 16; ++v) oacc[dt][qt][v] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
-
   const float qsc = MODE == ATTN_FP8 ? a.q_scale[row] : 1.f;
 
+  // lane-constant LDS offsets of the operand reads
+  const int g16 = l & 15, mbase = 16 * ((l >> 4) & 1);
+
+  // DMA instructions per K and per V tile group (all split parts)
+  constexpr int NK_DMA = NSPLIT * KT_BYTES / 1024, NV_DMA = NSPLIT * VT_BYTES / 1024;
+  unsigned kt_addr[NSPLIT], vt_addr[NSPLIT];
+#pragma unroll
+  for (int x = 0; x < NSPLIT; ++x) {
+    kt_addr[x] = (unsigned)(uintptr_t)kt_lds[x];
+    vt_addr[x] = (unsigned)(uintptr_t)vt_lds[x];
+  }
+  const unsigned k_rs32 = (unsigned)k_rs, v_rs32 = (unsigned)v_rs;
+
+  // prologue: K_0 then V_0 in flight
+  if (start < end) {
+    const int j0 = a.col_idx[start];
+#pragma unroll
+    for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBK, false>(kbase[x] + (int64_t)j0 * 64 * k_rs, k_rs32, kt_addr[x], l);
+#pragma unroll
+    for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBV, true>(vbase[x] + (int64_t)j0 * 64 * v_rs, v_rs32, vt_addr[x], l);
+  }
+
+  // Iteration j:  wait K_j | K_j -> registers | DMA K_{j+1} | S, softmax
+  //               wait V_j | PV reading V_j from LDS | DMA V_{j+1}
+  // so K_{j+1} streams in during softmax + PV and V_{j+1} during the next S.
   for (int it = start; it < end; ++it) {
     const int j = a.col_idx[it];
     const int kv0 = j * 64;
-    if (kv0 >= a.S_valid) continue;           // block made only of padding
-    __syncthreads();                          // previous tile fully consumed
-#pragma unroll
-    for (int x = 0; x < NSPLIT; ++x) {
-      load_tile_lds<RBK, false>(kbase[x] + (int64_t)kv0 * k_rs, k_rs, kt_lds[x], l);
-      load_tile_lds<RBV, true>(vbase[x] + (int64_t)kv0 * v_rs, v_rs, vt_lds[x], l);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    const bool has_next = it + 1 < end;
+    const int jn = has_next ? a.col_idx[it + 1] : 0;
+
+    wait_vm<NV_DMA>();                       // K_j landed (V_j may still be in flight)
+    const bool live_blk = kv0 < a.S_valid;   // a block made only of padding is skipped
 
     // ---- S^T = K Q^T  (sacc[kt][qt]: kv = kt*32 + 8(v/4) + 4 hi + v%4, q = qt*32 + l32)
+    // K operands are read from LDS right before their MFMAs.
     f32x16_t sacc[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -194,37 +254,45 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[kt][qt][v] = 0.f;
+    if (live_blk) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int r = kt * 32 + l32;
+      for (int kt = 0; kt < 2; ++kt) {
+        const int r = kt * 32 + l32;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if constexpr (MODE == ATTN_FP8) {
-          const int cb = 64 * s + 32 * hi;
-          i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb));
-          i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb + 16));
-          i32x8_t ka = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        for (int s = 0; s < KS; ++s) {
+          KOp k0, k1;
+          if constexpr (MODE == ATTN_FP8) {
+            const int cb = 64 * s + 32 * hi;
+            i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb));
+            i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb + 16));
+            k0 = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          } else {
+            k0 = *(const bf16x8_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+            if constexpr (MODE == ATTN_SPLIT_F32)
+              k1 = *(const bf16x8_t BSA_LDS*)(kt_lds[1] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+          }
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-            sacc[kt][qt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop8[qt][s], sacc[kt][qt], 0, 0,
-                                                                           0, 127, 0, 127);
-        } else {
-          const int cb = (16 * s + 8 * hi) * 2;
-          bf16x8_t ka = *(const bf16x8_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb));
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-            sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
-          if constexpr (MODE == ATTN_SPLIT_F32) {
-            bf16x8_t kl = *(const bf16x8_t BSA_LDS*)(kt_lds[1] + koff<RBK>(r, cb));
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-              sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[1][qt][s], sacc[kt][qt], 0, 0, 0);
-              sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
+          for (int qt = 0; qt < 2; ++qt) {
+            if constexpr (MODE == ATTN_FP8) {
+              sacc[kt][qt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0, qop[0][qt][s], sacc[kt][qt], 0, 0, 0,
+                                                                             127, 0, 127);
+            } else {
+              sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
+              if constexpr (MODE == ATTN_SPLIT_F32) {
+                sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[1][qt][s], sacc[kt][qt], 0, 0, 0);
+                sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
+              }
             }
           }
         }
       }
     }
+    wait_lgkm0();                            // K buffer free
+    if (has_next) {
+#pragma unroll
+      for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBK, false>(kbase[x] + (int64_t)jn * 64 * k_rs, k_rs32, kt_addr[x], l);
+    }
+    if (live_blk) {
 
     // ---- mask padded keys of the last block
     if (kv0 + 64 > a.S_valid) {
@@ -240,8 +308,9 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
         }
     }
 
-    // ---- online softmax (log2 domain)
+    // ---- online softmax (log2 domain, lazily rescaled)
     const float c = MODE == ATTN_FP8 ? a.scale_log2 * qsc * a.k_scale[bh * a.nb + j] : a.scale_log2;
+    bf16x8_t pop[2][4];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       float mx = -INFINITY;
@@ -249,50 +318,60 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][qt][v]);
-      mx = fmaxf(mx, partner(mx));
-      const float mnew = fmaxf(m_run[qt], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
-      m_run[qt] = mnew;
+      mx = fmaxf(mx, partner(mx)) * c;
+      if (__builtin_amdgcn_read_exec() && __ballot(mx > m_run[qt] + RESCALE_TAU)) {
+        const float mnew = fmaxf(m_run[qt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
+        m_run[qt] = mnew;
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[dt][qt][v] *= alpha;
+      }
+      const float mr = m_run[qt];
       float ls = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int sp = 0; sp < 4; ++sp) {
+        i32x4_t w;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][v], c, -mnew));
-          sacc[kt][qt][v] = p;
-          ls += p;
+        for (int e = 0; e < 4; ++e) {
+          const int v = 8 * (sp & 1) + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][qt][v], c, -mr));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][qt][v + 1], c, -mr));
+          ls += p0 + p1;
+          w[e] = (int)pk_bf16(p0, p1);
         }
-      l_run[qt] = l_run[qt] * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[dt][qt][v] *= alpha;
+        pop[qt][sp] = __builtin_bit_cast(bf16x8_t, w);
+      }
+      l_run[qt] += ls;
     }
 
-    // ---- O^T += V^T P^T
-    bf16x8_t pop[2][4];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int sp = 0; sp < 4; ++sp) pop[qt][sp] = pack_bf16x8(sacc[sp >> 1][qt], 8 * (sp & 1));
-    const int g16 = l & 15, mbase = 16 * ((l >> 4) & 1);
+    // ---- O^T += V^T P^T, V^T read from the row-major V tile with transposing reads
+    if (has_next) wait_vm<NK_DMA>(); else wait_vm<0>();   // V_j landed
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;   // byte column of this lane's 4 elements
+      const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
-        const int K0 = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi;
-        const int ra = K0 + (g16 >> 2), rb = ra + 8;
+        const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
 #pragma unroll
         for (int x = 0; x < NSPLIT; ++x) {
           s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra, cb)));
-          s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(rb, cb)));
+          s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra + 8, cb)));
           const bf16x8_t va = join_bf16x8(v0, v1);
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt)
             oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qt][sp], oacc[dt][qt], 0, 0, 0);
         }
       }
+    }
+    }  // live_blk
+    if (!live_blk) { if (has_next) wait_vm<NK_DMA>(); else wait_vm<0>(); }
+    wait_lgkm0();                            // V buffer free
+    if (has_next) {
+#pragma unroll
+      for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBV, true>(vbase[x] + (int64_t)jn * 64 * v_rs, v_rs32, vt_addr[x], l);
     }
   }
 
@@ -304,7 +383,7 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
     const bool live = q < a.S_valid && lt > 0.f;
     const float inv = live ? 1.f / lt : 0.f;
     if (a.lse && hi == 0)
-      a.lse[(int64_t)bh * a.S + q] = live ? (m_run[qt] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+      a.lse[(int64_t)bh * a.S + q] = live ? (m_run[qt] + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -317,8 +396,8 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
         } else {
           u16* o = (u16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d;
           uint2 w;
-          w.x = f32_to_bf16_bits(oacc[dt][qt][4 * g] * inv) | ((unsigned)f32_to_bf16_bits(oacc[dt][qt][4 * g + 1] * inv) << 16);
-          w.y = f32_to_bf16_bits(oacc[dt][qt][4 * g + 2] * inv) | ((unsigned)f32_to_bf16_bits(oacc[dt][qt][4 * g + 3] * inv) << 16);
+          w.x = pk_bf16(oacc[dt][qt][4 * g] * inv, oacc[dt][qt][4 * g + 1] * inv);
+          w.y = pk_bf16(oacc[dt][qt][4 * g + 2] * inv, oacc[dt][qt][4 * g + 3] * inv);
           *(uint2*)o = w;
         }
       }

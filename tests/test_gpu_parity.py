@@ -247,3 +247,21 @@ def test_full_mask_equals_dense(gpu_lib):
     ref = torch.nn.functional.scaled_dot_product_attention(q.cpu().double(), k.cpu().double(), v.cpu().double())
     err = (out.cpu().double() - ref).abs()
     assert err.max().item() <= MAX_ERR and err.mean().item() <= MEAN_ERR
+
+
+def test_attention_f32_d128(gpu_lib):
+    """f32 inputs with head_dim 128 (hi/lo bf16 split path) on a ragged sequence."""
+    B, H, S, Sv, D = 1, 2, 64 * 5, 64 * 4 + 9, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    q, k, v = (torch.randn(B, H, S, D, device=DEV, generator=g) for _ in range(3))
+    keep = np.random.default_rng(12).random((B, H, 5, 5)) < 0.6
+    keep[:, :, np.arange(5), np.arange(5)] = True
+    mask = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+    out = gpu_lib.block_sparse_attn_fwd(q, k, v, mask, s_valid=Sv)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    for h in range(H):
+        O, _ = oracle.block_sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), keep[0, h], 64, Sv)
+        err = np.abs(f64(out[0, h]) - O)
+        assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR
