@@ -81,6 +81,21 @@ __device__ __forceinline__ void load_tile_lds(const char* gtile, unsigned rs, un
   }
 }
 
+// Wave w of a two-wave workgroup issues instructions [w*NI/2, (w+1)*NI/2) of a tile copy.
+template <int RB, bool VSWZ>
+__device__ __forceinline__ void load_tile_half(const char* gtile, unsigned rs, unsigned lds, int lane, int w) {
+  using G = TileGeom<RB>;
+  constexpr int RPI = 1024 / RB;
+  constexpr int NH = 64 / RPI / 2;
+#pragma unroll
+  for (int u = 0; u < NH; ++u) {
+    const int t = w * NH + u;
+    const int r = t * RPI + lane / G::NCH;
+    const int c = (lane % G::NCH) ^ (VSWZ ? G::swz_v(r) : G::swz_k(r));
+    dma16(gtile, (unsigned)r * rs + (unsigned)c * 16u, lds + t * 1024);
+  }
+}
+
 // byte offset of (row r, byte column cb) in a K-swizzled / V-swizzled tile
 template <int RB>
 __device__ __forceinline__ int koff(int r, int cb) {
@@ -128,13 +143,25 @@ __device__ __forceinline__ unsigned pk_bf16(float a, float b) {
 // fp32 range, and the rescale of the output accumulators is skipped on most tiles.
 constexpr float RESCALE_TAU = 8.f;
 
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+
 // MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
 //
-// Software pipeline (one wave): at the top of iteration j the K_j and V_j tiles are
-// read from LDS into registers; the DMA of K_{j+1}, V_{j+1} into the same LDS buffers
-// is issued right after, and the MFMA and softmax work of tile j runs while it flies.
+// One workgroup of two waves per query block; wave w owns queries 32w..32w+31 of the
+// block. The K_j and V_j tiles live once in LDS and are read by both waves; each wave
+// issues half of every tile's DMA instructions.
+//
+// Pipeline per kv block j (B = workgroup barrier):
+//   wait own K_j half, B | S_j = K_j Q^T | B | DMA K_{j+1} | softmax_j
+//   wait own V_j half, B | O += V_j^T P_j^T | B | DMA V_{j+1}
+// so K_{j+1} streams in during softmax + PV and V_{j+1} during the next S; with two
+// workgroups per SIMD pair the MFMA work of one overlaps the softmax of the other.
 template <int MODE, int D>
-__global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ col_idx,
+                                                       const float* __restrict__ q_scale,
+                                                       const float* __restrict__ k_scale) {
   constexpr int QK_ES = MODE == ATTN_FP8 ? 1 : 2;   // bytes per Q/K element
   constexpr int RBK = D * QK_ES;                    // K tile row bytes
   constexpr int RBV = D * 2;                        // V tile row bytes (bf16)
@@ -143,49 +170,64 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
   constexpr int DT = D / 32;                        // 32-wide d tiles of the output
   constexpr int KS = MODE == ATTN_FP8 ? D / 64 : D / 16;   // k-steps of S = K Q^T
   using KOp = typename std::conditional<MODE == ATTN_FP8, i32x8_t, bf16x8_t>::type;
+  // DMA instructions per wave for one K / one V tile group (all split parts)
+  constexpr int NK_W = NSPLIT * KT_BYTES / 1024 / 2, NV_W = NSPLIT * VT_BYTES / 1024 / 2;
 
   __shared__ __attribute__((aligned(1024))) char smem[NSPLIT * (KT_BYTES + VT_BYTES)];
   char BSA_LDS* lds = (char BSA_LDS*)smem;
   char BSA_LDS* kt_lds[NSPLIT];
   char BSA_LDS* vt_lds[NSPLIT];
+  unsigned kt_addr[NSPLIT], vt_addr[NSPLIT];
 #pragma unroll
   for (int x = 0; x < NSPLIT; ++x) {
     kt_lds[x] = lds + x * KT_BYTES;
     vt_lds[x] = lds + NSPLIT * KT_BYTES + x * VT_BYTES;
+    kt_addr[x] = (unsigned)(uintptr_t)kt_lds[x];
+    vt_addr[x] = (unsigned)(uintptr_t)vt_lds[x];
   }
 
-  const int l = threadIdx.x;
+  const int l = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave: query half
   const int i = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
   const int row = bh * a.nb + i;
-  const int start = a.row_ptr[row], end = a.row_ptr[row + 1];
+  const int start = row_ptr[row], end = row_ptr[row + 1];
   const int l32 = l & 31, hi = l >> 5;
 
-  // element strides -> byte strides (split copies are contiguous [B,H,S,D] bf16)
-  const int64_t qes = MODE == ATTN_SPLIT_F32 ? 2 : QK_ES;
   const char* qbase[NSPLIT];
   const char* kbase[NSPLIT];
   const char* vbase[NSPLIT];
   int64_t q_rs, k_rs, v_rs;
   if constexpr (MODE == ATTN_SPLIT_F32) {
-    const int64_t plane = (int64_t)a.S * D * 2;
-    const int64_t off = (int64_t)bh * plane;
+    const int64_t off = (int64_t)bh * a.S * D * 2;
     qbase[0] = (const char*)a.q + off; qbase[1] = (const char*)a.q_lo + off;
     kbase[0] = (const char*)a.k + off; kbase[1] = (const char*)a.k_lo + off;
     vbase[0] = (const char*)a.v + off; vbase[1] = (const char*)a.v_lo + off;
     q_rs = k_rs = v_rs = D * 2;
   } else {
-    qbase[0] = (const char*)a.q + (b * a.q_sb + h * a.q_sh) * qes;
-    kbase[0] = (const char*)a.k + (b * a.k_sb + h * a.k_sh) * qes;
+    qbase[0] = (const char*)a.q + (b * a.q_sb + h * a.q_sh) * QK_ES;
+    kbase[0] = (const char*)a.k + (b * a.k_sb + h * a.k_sh) * QK_ES;
     vbase[0] = (const char*)a.v + (b * a.v_sb + h * a.v_sh) * 2;
-    q_rs = a.q_ss * qes; k_rs = a.k_ss * qes; v_rs = a.v_ss * 2;
+    q_rs = a.q_ss * QK_ES; k_rs = a.k_ss * QK_ES; v_rs = a.v_ss * 2;
   }
+  const unsigned k_rs32 = (unsigned)k_rs, v_rs32 = (unsigned)v_rs;
 
-  // ---- Q^T as the B operand: lane holds query qt*32 + l32
-  KOp qop[NSPLIT][2][KS];
+  // this wave's half of a tile's DMA instructions
+  auto dma_k = [&](int jt) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int64_t qrow = (int64_t)i * 64 + qt * 32 + l32;
+    for (int x = 0; x < NSPLIT; ++x)
+      load_tile_half<RBK, false>(kbase[x] + (int64_t)jt * 64 * k_rs, k_rs32, kt_addr[x], l, wv);
+  };
+  auto dma_v = [&](int jt) {
+#pragma unroll
+    for (int x = 0; x < NSPLIT; ++x)
+      load_tile_half<RBV, true>(vbase[x] + (int64_t)jt * 64 * v_rs, v_rs32, vt_addr[x], l, wv);
+  };
+
+  // ---- Q^T as the B operand: lane holds query 32 wv + l32 of the block
+  KOp qop[NSPLIT][KS];
+  {
+    const int64_t qrow = (int64_t)i * 64 + wv * 32 + l32;
 #pragma unroll
     for (int x = 0; x < NSPLIT; ++x)
 #pragma unroll
@@ -193,143 +235,122 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
         if constexpr (MODE == ATTN_FP8) {
           const char* p = qbase[0] + qrow * q_rs + 64 * s + 32 * hi;
           i32x4_t x0 = *(const i32x4_t*)p, x1 = *(const i32x4_t*)(p + 16);
-          qop[x][qt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          qop[x][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         } else {
-          qop[x][qt][s] = *(const bf16x8_t*)(qbase[x] + qrow * q_rs + (16 * s + 8 * hi) * 2);
+          qop[x][s] = *(const bf16x8_t*)(qbase[x] + qrow * q_rs + (16 * s + 8 * hi) * 2);
         }
       }
   }
+  const float qsc = MODE == ATTN_FP8 ? q_scale[row] : 1.f;
 
-  f32x16_t oacc[DT][2];
+  // The kv list is fetched 64 entries at a time into one register (lane e holds entry
+  // cbase + e) and read with readlane, so block indices are wave-uniform scalars; the
+  // fp8 key scales come along the same way. Each fetch is waited for right away.
+  int cbase = start;
+  int ccache = 0;
+  float kscache = 1.f;
+  auto fetch_chunk = [&](int base) {
+    const int e = min(base + l, end - 1);
+    ccache = col_idx[e];
+    if constexpr (MODE == ATTN_FP8) kscache = k_scale[bh * a.nb + ccache];
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+  if (start < end) fetch_chunk(cbase);
+  __builtin_amdgcn_s_waitcnt(0);            // Q and the first kv chunk are in registers
+
+  f32x16_t oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[dt][qt][v] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  const float qsc = MODE == ATTN_FP8 ? a.q_scale[row] : 1.f;
-
-  // lane-constant LDS offsets of the operand reads
+    for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
   const int g16 = l & 15, mbase = 16 * ((l >> 4) & 1);
 
-  // DMA instructions per K and per V tile group (all split parts)
-  constexpr int NK_DMA = NSPLIT * KT_BYTES / 1024, NV_DMA = NSPLIT * VT_BYTES / 1024;
-  unsigned kt_addr[NSPLIT], vt_addr[NSPLIT];
-#pragma unroll
-  for (int x = 0; x < NSPLIT; ++x) {
-    kt_addr[x] = (unsigned)(uintptr_t)kt_lds[x];
-    vt_addr[x] = (unsigned)(uintptr_t)vt_lds[x];
-  }
-  const unsigned k_rs32 = (unsigned)k_rs, v_rs32 = (unsigned)v_rs;
-
-  // prologue: K_0 then V_0 in flight
   if (start < end) {
-    const int j0 = a.col_idx[start];
-#pragma unroll
-    for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBK, false>(kbase[x] + (int64_t)j0 * 64 * k_rs, k_rs32, kt_addr[x], l);
-#pragma unroll
-    for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBV, true>(vbase[x] + (int64_t)j0 * 64 * v_rs, v_rs32, vt_addr[x], l);
+    const int j0 = __builtin_amdgcn_readlane(ccache, 0);
+    dma_k(j0);
+    dma_v(j0);
   }
 
-  // Iteration j:  wait K_j | K_j -> registers | DMA K_{j+1} | S, softmax
-  //               wait V_j | PV reading V_j from LDS | DMA V_{j+1}
-  // so K_{j+1} streams in during softmax + PV and V_{j+1} during the next S.
   for (int it = start; it < end; ++it) {
-    const int j = a.col_idx[it];
-    const int kv0 = j * 64;
+    const int j = __builtin_amdgcn_readlane(ccache, it - cbase);
+    const float ksc = MODE == ATTN_FP8 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kscache), it - cbase)) : 1.f;
     const bool has_next = it + 1 < end;
-    const int jn = has_next ? a.col_idx[it + 1] : 0;
-
-    wait_vm<NV_DMA>();                       // K_j landed (V_j may still be in flight)
+    if (has_next && it + 1 - cbase == 64) {
+      cbase += 64;
+      wait_all();                            // tiles of j in LDS before the chunk fetch waits anyway
+      fetch_chunk(cbase);
+    }
+    const int jn = has_next ? __builtin_amdgcn_readlane(ccache, it + 1 - cbase) : 0;
+    const int kv0 = j * 64;
     const bool live_blk = kv0 < a.S_valid;   // a block made only of padding is skipped
 
-    // ---- S^T = K Q^T  (sacc[kt][qt]: kv = kt*32 + 8(v/4) + 4 hi + v%4, q = qt*32 + l32)
-    // K operands are read from LDS right before their MFMAs.
-    f32x16_t sacc[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[kt][qt][v] = 0.f;
+    wait_vm<NV_W>();                         // own half of K_j landed (V_j may be in flight)
+    wg_barrier();                            // the other half too
+
+    // ---- S^T = K Q^T for this wave's 32 queries: sacc[kt], kv = kt*32 + 8(v/4) + 4 hi + v%4
+    const f32x16_t zero16 = {};
+    f32x16_t sacc[2];
     if (live_blk) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int r = kt * 32 + l32;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          KOp k0, k1;
           if constexpr (MODE == ATTN_FP8) {
             const int cb = 64 * s + 32 * hi;
             i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb));
             i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb + 16));
-            k0 = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            const i32x8_t k0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0, qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0,
+                                                                       127, 0, 127);
           } else {
-            k0 = *(const bf16x8_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
-            if constexpr (MODE == ATTN_SPLIT_F32)
-              k1 = *(const bf16x8_t BSA_LDS*)(kt_lds[1] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
-          }
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            if constexpr (MODE == ATTN_FP8) {
-              sacc[kt][qt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0, qop[0][qt][s], sacc[kt][qt], 0, 0, 0,
-                                                                             127, 0, 127);
-            } else {
-              sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
-              if constexpr (MODE == ATTN_SPLIT_F32) {
-                sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[1][qt][s], sacc[kt][qt], 0, 0, 0);
-                sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[0][qt][s], sacc[kt][qt], 0, 0, 0);
-              }
+            const bf16x8_t k0 = *(const bf16x8_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0);
+            if constexpr (MODE == ATTN_SPLIT_F32) {
+              const bf16x8_t k1 = *(const bf16x8_t BSA_LDS*)(kt_lds[1] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+              sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[1][s], sacc[kt], 0, 0, 0);
+              sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[0][s], sacc[kt], 0, 0, 0);
             }
           }
         }
       }
     }
-    wait_lgkm0();                            // K buffer free
-    if (has_next) {
-#pragma unroll
-      for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBK, false>(kbase[x] + (int64_t)jn * 64 * k_rs, k_rs32, kt_addr[x], l);
-    }
+    wait_lgkm0();
+    wg_barrier();                            // both waves are done with K_j
+    if (has_next) dma_k(jn);
+
+    bf16x8_t pop[4];
     if (live_blk) {
-
-    // ---- mask padded keys of the last block
-    if (kv0 + 64 > a.S_valid) {
+      // ---- mask padded keys of the last block
+      if (kv0 + 64 > a.S_valid) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kv = kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (kv0 + kv >= a.S_valid) {
-            sacc[kt][0][v] = -INFINITY;
-            sacc[kt][1][v] = -INFINITY;
+          for (int v = 0; v < 16; ++v) {
+            const int kv = kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+            if (kv0 + kv >= a.S_valid) sacc[kt][v] = -INFINITY;
           }
-        }
-    }
-
-    // ---- online softmax (log2 domain, lazily rescaled)
-    const float c = MODE == ATTN_FP8 ? a.scale_log2 * qsc * a.k_scale[bh * a.nb + j] : a.scale_log2;
-    bf16x8_t pop[2][4];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+      }
+      // ---- online softmax (log2 domain, lazily rescaled)
+      const float c = a.scale_log2 * qsc * ksc;
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][qt][v]);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
       mx = fmaxf(mx, partner(mx)) * c;
-      if (__builtin_amdgcn_read_exec() && __ballot(mx > m_run[qt] + RESCALE_TAU)) {
-        const float mnew = fmaxf(m_run[qt], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - mnew);
-        m_run[qt] = mnew;
-        l_run[qt] *= alpha;
+      if (__ballot(mx > m_run + RESCALE_TAU)) {
+        const float mnew = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+        m_run = mnew;
+        l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[dt][qt][v] *= alpha;
+          for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
       }
-      const float mr = m_run[qt];
+      const float mr = m_run;
       float ls = 0.f;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
@@ -337,71 +358,64 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 8 * (sp & 1) + 2 * e;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][qt][v], c, -mr));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][qt][v + 1], c, -mr));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][v], c, -mr));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][v + 1], c, -mr));
           ls += p0 + p1;
           w[e] = (int)pk_bf16(p0, p1);
         }
-        pop[qt][sp] = __builtin_bit_cast(bf16x8_t, w);
+        pop[sp] = __builtin_bit_cast(bf16x8_t, w);
       }
-      l_run[qt] += ls;
+      l_run += ls;
     }
 
-    // ---- O^T += V^T P^T, V^T read from the row-major V tile with transposing reads
-    if (has_next) wait_vm<NK_DMA>(); else wait_vm<0>();   // V_j landed
+    if (has_next) wait_vm<NK_W>(); else wait_vm<0>();   // own half of V_j landed
+    wg_barrier();
+    if (live_blk) {
+      // ---- O^T += V^T P^T, V^T read from the row-major V tile with transposing reads
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
+      for (int dt = 0; dt < DT; ++dt) {
+        const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
 #pragma unroll
-      for (int sp = 0; sp < 4; ++sp) {
-        const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
+        for (int sp = 0; sp < 4; ++sp) {
+          const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
 #pragma unroll
-        for (int x = 0; x < NSPLIT; ++x) {
-          s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra, cb)));
-          s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra + 8, cb)));
-          const bf16x8_t va = join_bf16x8(v0, v1);
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-            oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pop[qt][sp], oacc[dt][qt], 0, 0, 0);
+          for (int x = 0; x < NSPLIT; ++x) {
+            s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra, cb)));
+            s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra + 8, cb)));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(v0, v1), pop[sp], oacc[dt], 0, 0, 0);
+          }
         }
       }
     }
-    }  // live_blk
-    if (!live_blk) { if (has_next) wait_vm<NK_DMA>(); else wait_vm<0>(); }
-    wait_lgkm0();                            // V buffer free
-    if (has_next) {
-#pragma unroll
-      for (int x = 0; x < NSPLIT; ++x) load_tile_lds<RBV, true>(vbase[x] + (int64_t)jn * 64 * v_rs, v_rs32, vt_addr[x], l);
-    }
+    wait_lgkm0();
+    wg_barrier();                            // both waves are done with V_j
+    if (has_next) dma_v(jn);
   }
 
   // ---- epilogue: O = O^T / l, written row-major; padded rows and empty rows are 0
+  const float lt = l_run + partner(l_run);
+  const int q = i * 64 + wv * 32 + l32;
+  const bool live = q < a.S_valid && lt > 0.f;
+  const float inv = live ? 1.f / lt : 0.f;
+  if (a.lse && hi == 0)
+    a.lse[(int64_t)bh * a.S + q] = live ? (m_run + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float lt = l_run[qt] + partner(l_run[qt]);
-    const int q = i * 64 + qt * 32 + l32;
-    const bool live = q < a.S_valid && lt > 0.f;
-    const float inv = live ? 1.f / lt : 0.f;
-    if (a.lse && hi == 0)
-      a.lse[(int64_t)bh * a.S + q] = live ? (m_run[qt] + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hi;
-        if constexpr (MODE == ATTN_SPLIT_F32) {
-          float* o = (float*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d;
-          *(f32x4_t*)o = f32x4_t{oacc[dt][qt][4 * g] * inv, oacc[dt][qt][4 * g + 1] * inv,
-                                 oacc[dt][qt][4 * g + 2] * inv, oacc[dt][qt][4 * g + 3] * inv};
-        } else {
-          u16* o = (u16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d;
-          uint2 w;
-          w.x = pk_bf16(oacc[dt][qt][4 * g] * inv, oacc[dt][qt][4 * g + 1] * inv);
-          w.y = pk_bf16(oacc[dt][qt][4 * g + 2] * inv, oacc[dt][qt][4 * g + 3] * inv);
-          *(uint2*)o = w;
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * hi;
+      if constexpr (MODE == ATTN_SPLIT_F32) {
+        float* o = (float*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d;
+        *(f32x4_t*)o = f32x4_t{oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                               oacc[dt][4 * g + 3] * inv};
+      } else {
+        u16* o = (u16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d;
+        uint2 w;
+        w.x = pk_bf16(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
+        w.y = pk_bf16(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        *(uint2*)o = w;
       }
-  }
+    }
 }
 
 // f32 -> (hi, lo) bf16 split, written contiguous [B,H,S,D]
@@ -433,7 +447,8 @@ hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, 
 template <int MODE, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.nb, a.B * a.H);
-  hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(128), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
+                     a.k_scale);
   return hipGetLastError();
 }
 
