@@ -188,7 +188,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int l = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave: query half
-  const int i = blockIdx.x, bh = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin; remap so that XCD x runs the
+  // contiguous range [x*chunk, (x+1)*chunk) of (head, query block) rows: neighbouring
+  // query blocks share most kv tiles, and then share one L2.
+  const int total = a.B * a.H * a.nb;
+  const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
+  const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
+  if (lin >= total) return;
+  const int i = lin % a.nb, bh = lin / a.nb;
   const int b = bh / a.H, h = bh % a.H;
   const int row = bh * a.nb + i;
   const int start = row_ptr[row], end = row_ptr[row + 1];
@@ -446,7 +453,8 @@ hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, 
 
 template <int MODE, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.nb, a.B * a.H);
+  const int total = a.B * a.H * a.nb;
+  dim3 grid(((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
   hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(128), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
                      a.k_scale);
   return hipGetLastError();

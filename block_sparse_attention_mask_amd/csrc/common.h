@@ -5,6 +5,7 @@
 
 #define BSA_WAVE 64
 #define BSA_N 64   // tokens per block
+#define BSA_NXCD 8 // XCDs of an MI355X; workgroups are dealt to them round-robin
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
