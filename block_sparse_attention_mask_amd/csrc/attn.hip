@@ -81,12 +81,13 @@ __device__ __forceinline__ void load_tile_lds(const char* gtile, unsigned rs, un
   }
 }
 
-// Wave w of a two-wave workgroup issues instructions [w*NI/2, (w+1)*NI/2) of a tile copy.
-template <int RB, bool VSWZ>
-__device__ __forceinline__ void load_tile_half(const char* gtile, unsigned rs, unsigned lds, int lane, int w) {
+// Wave w of a P-wave workgroup issues instructions [w*NI/P, (w+1)*NI/P) of a tile copy.
+template <int RB, bool VSWZ, int P>
+__device__ __forceinline__ void load_tile_part(const char* gtile, unsigned rs, unsigned lds, int lane, int w) {
   using G = TileGeom<RB>;
   constexpr int RPI = 1024 / RB;
-  constexpr int NH = 64 / RPI / 2;
+  constexpr int NH = 64 / RPI / P;
+  static_assert(NH * RPI * P == 64, "tile copy must split evenly");
 #pragma unroll
   for (int u = 0; u < NH; ++u) {
     const int t = w * NH + u;
@@ -148,58 +149,60 @@ __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lg
 
 // MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
 //
-// One workgroup of two waves per query block; wave w owns queries 32w..32w+31 of the
-// block. The K_j and V_j tiles live once in LDS and are read by both waves; each wave
-// issues half of every tile's DMA instructions.
+// One workgroup of four waves per PAIR of adjacent query blocks (2p, 2p+1): waves 0-1
+// take the 64 queries of block 2p (32 each), waves 2-3 those of block 2p+1. The
+// workgroup walks the union of the two blocks' kv lists in ascending order; every kv
+// tile is copied to LDS once and used by each block whose list holds it (adjacent
+// blocks share most of their kv blocks, so most tiles serve both). A block visits
+// exactly its own tiles, in the same ascending order as it would alone.
 //
-// Pipeline per kv block j (B = workgroup barrier):
-//   wait own K_j half, B | S_j = K_j Q^T | B | DMA K_{j+1} | softmax_j
-//   wait own V_j half, B | O += V_j^T P_j^T | B | DMA V_{j+1}
-// so K_{j+1} streams in during softmax + PV and V_{j+1} during the next S; with two
-// workgroups per SIMD pair the MFMA work of one overlaps the softmax of the other.
+// K/V tiles are double-buffered: tile u+2 is copied into the buffer of tile u as soon
+// as all waves are done with tile u, so every copy has two steps of compute to land.
+// Each wave issues a quarter of every tile copy.
 template <int MODE, int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr,
-                                                       const int32_t* __restrict__ col_idx,
-                                                       const float* __restrict__ q_scale,
-                                                       const float* __restrict__ k_scale) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                     const float* __restrict__ q_scale, const float* __restrict__ k_scale) {
   constexpr int QK_ES = MODE == ATTN_FP8 ? 1 : 2;   // bytes per Q/K element
   constexpr int RBK = D * QK_ES;                    // K tile row bytes
   constexpr int RBV = D * 2;                        // V tile row bytes (bf16)
   constexpr int KT_BYTES = 64 * RBK, VT_BYTES = 64 * RBV;
   constexpr int NSPLIT = MODE == ATTN_SPLIT_F32 ? 2 : 1;
+  constexpr int STAGE = NSPLIT * (KT_BYTES + VT_BYTES);
   constexpr int DT = D / 32;                        // 32-wide d tiles of the output
   constexpr int KS = MODE == ATTN_FP8 ? D / 64 : D / 16;   // k-steps of S = K Q^T
   using KOp = typename std::conditional<MODE == ATTN_FP8, i32x8_t, bf16x8_t>::type;
-  // DMA instructions per wave for one K / one V tile group (all split parts)
-  constexpr int NK_W = NSPLIT * KT_BYTES / 1024 / 2, NV_W = NSPLIT * VT_BYTES / 1024 / 2;
+  // DMA instructions each wave issues per tile (K and V, all split parts)
+  constexpr int NKV_W = STAGE / 1024 / 4;
 
-  __shared__ __attribute__((aligned(1024))) char smem[NSPLIT * (KT_BYTES + VT_BYTES)];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   char BSA_LDS* lds = (char BSA_LDS*)smem;
-  char BSA_LDS* kt_lds[NSPLIT];
-  char BSA_LDS* vt_lds[NSPLIT];
-  unsigned kt_addr[NSPLIT], vt_addr[NSPLIT];
-#pragma unroll
-  for (int x = 0; x < NSPLIT; ++x) {
-    kt_lds[x] = lds + x * KT_BYTES;
-    vt_lds[x] = lds + NSPLIT * KT_BYTES + x * VT_BYTES;
-    kt_addr[x] = (unsigned)(uintptr_t)kt_lds[x];
-    vt_addr[x] = (unsigned)(uintptr_t)vt_lds[x];
-  }
+  auto k_lds = [&](int st, int x) { return lds + st * STAGE + x * KT_BYTES; };
+  auto v_lds = [&](int st, int x) { return lds + st * STAGE + NSPLIT * KT_BYTES + x * VT_BYTES; };
 
   const int l = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave: query half
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pr = wave >> 1, wv = wave & 1;        // block of the pair, query half
+  const int l32 = l & 31, hi = l >> 5;
+
   // Workgroups are dealt to the 8 XCDs round-robin; remap so that XCD x runs the
-  // contiguous range [x*chunk, (x+1)*chunk) of (head, query block) rows: neighbouring
+  // contiguous range [x*chunk, (x+1)*chunk) of (head, pair) work items: neighbouring
   // query blocks share most kv tiles, and then share one L2.
-  const int total = a.B * a.H * a.nb;
+  const int npair = (a.nb + 1) / 2;
+  const int total = a.B * a.H * npair;
   const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
   const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
   if (lin >= total) return;
-  const int i = lin % a.nb, bh = lin / a.nb;
+  const int bh = lin / npair, pidx = lin % npair;
   const int b = bh / a.H, h = bh % a.H;
+  const int iA = 2 * pidx, iB = 2 * pidx + 1;
+  const bool hasB = iB < a.nb;
+  const int rowA = bh * a.nb + iA;
+  const int sA = row_ptr[rowA], eA = row_ptr[rowA + 1];
+  const int sB = hasB ? row_ptr[rowA + 1] : 0, eB = hasB ? row_ptr[rowA + 2] : 0;
+  const int i = pr ? iB : iA;                      // this wave's query block
+  const bool mine_valid = pr == 0 || hasB;
   const int row = bh * a.nb + i;
-  const int start = row_ptr[row], end = row_ptr[row + 1];
-  const int l32 = l & 31, hi = l >> 5;
 
   const char* qbase[NSPLIT];
   const char* kbase[NSPLIT];
@@ -219,22 +222,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const unsigned k_rs32 = (unsigned)k_rs, v_rs32 = (unsigned)v_rs;
 
-  // this wave's half of a tile's DMA instructions
-  auto dma_k = [&](int jt) {
+  // this wave's quarter of the copy of kv tile jt into stage st
+  auto dma_tile = [&](int st, int jt) {
 #pragma unroll
-    for (int x = 0; x < NSPLIT; ++x)
-      load_tile_half<RBK, false>(kbase[x] + (int64_t)jt * 64 * k_rs, k_rs32, kt_addr[x], l, wv);
-  };
-  auto dma_v = [&](int jt) {
-#pragma unroll
-    for (int x = 0; x < NSPLIT; ++x)
-      load_tile_half<RBV, true>(vbase[x] + (int64_t)jt * 64 * v_rs, v_rs32, vt_addr[x], l, wv);
+    for (int x = 0; x < NSPLIT; ++x) {
+      load_tile_part<RBK, false, 4>(kbase[x] + (int64_t)jt * 64 * k_rs, k_rs32, (unsigned)(uintptr_t)k_lds(st, x), l, wave);
+      load_tile_part<RBV, true, 4>(vbase[x] + (int64_t)jt * 64 * v_rs, v_rs32, (unsigned)(uintptr_t)v_lds(st, x), l, wave);
+    }
   };
 
-  // ---- Q^T as the B operand: lane holds query 32 wv + l32 of the block
+  // ---- Q^T as the B operand: lane holds query 32 wv + l32 of block i
   KOp qop[NSPLIT][KS];
   {
-    const int64_t qrow = (int64_t)i * 64 + wv * 32 + l32;
+    const int64_t qrow = (int64_t)(mine_valid ? i : iA) * 64 + wv * 32 + l32;
 #pragma unroll
     for (int x = 0; x < NSPLIT; ++x)
 #pragma unroll
@@ -248,22 +248,41 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
   }
-  const float qsc = MODE == ATTN_FP8 ? q_scale[row] : 1.f;
+  const float qsc = MODE == ATTN_FP8 && mine_valid ? q_scale[row] : 1.f;
 
-  // The kv list is fetched 64 entries at a time into one register (lane e holds entry
-  // cbase + e) and read with readlane, so block indices are wave-uniform scalars; the
-  // fp8 key scales come along the same way. Each fetch is waited for right away.
-  int cbase = start;
-  int ccache = 0;
-  float kscache = 1.f;
-  auto fetch_chunk = [&](int base) {
-    const int e = min(base + l, end - 1);
-    ccache = col_idx[e];
-    if constexpr (MODE == ATTN_FP8) kscache = k_scale[bh * a.nb + ccache];
-    __builtin_amdgcn_s_waitcnt(0);
+  // ---- union walk over the two kv lists (wave-uniform scalar state). Each list is
+  // fetched 64 entries at a time into one register (lane e holds entry base + e) and
+  // read with readlane; the fp8 key scale of an entry comes along the same way.
+  int ia = sA, ib = sB, cbA = sA, cbB = sB;
+  int cacheA = 0, cacheB = 0;
+  float kscA = 1.f, kscB = 1.f;
+  auto fetch = [&](int base, int e, int& cache, float& ksc) {
+    const int x = min(base + l, e - 1);
+    cache = col_idx[x];
+    if constexpr (MODE == ATTN_FP8) ksc = k_scale[bh * a.nb + cache];
   };
-  if (start < end) fetch_chunk(cbase);
-  __builtin_amdgcn_s_waitcnt(0);            // Q and the first kv chunk are in registers
+  if (sA < eA) fetch(cbA, eA, cacheA, kscA);
+  if (sB < eB) fetch(cbB, eB, cacheB, kscB);
+  __builtin_amdgcn_s_waitcnt(0);            // Q and the first list chunks are in registers
+
+  // next union entry: returns the kv block (or -1 when both lists are done), the use
+  // flags (bit 0: block 2p, bit 1: block 2p+1) and the fp8 key scale
+  auto next_entry = [&](int& flags, float& ksc) -> int {
+    const int BIG = 0x7fffffff;
+    if (ia < eA && ia - cbA == 64) { cbA += 64; fetch(cbA, eA, cacheA, kscA); __builtin_amdgcn_s_waitcnt(0); }
+    if (ib < eB && ib - cbB == 64) { cbB += 64; fetch(cbB, eB, cacheB, kscB); __builtin_amdgcn_s_waitcnt(0); }
+    const int ja = ia < eA ? __builtin_amdgcn_readlane(cacheA, ia - cbA) : BIG;
+    const int jb = ib < eB ? __builtin_amdgcn_readlane(cacheB, ib - cbB) : BIG;
+    const int j = min(ja, jb);
+    if (j == BIG) { flags = 0; return -1; }
+    flags = (ja == j ? 1 : 0) | (jb == j ? 2 : 0);
+    if constexpr (MODE == ATTN_FP8)
+      ksc = __int_as_float(ja == j ? __builtin_amdgcn_readlane(__float_as_int(kscA), ia - cbA)
+                                   : __builtin_amdgcn_readlane(__float_as_int(kscB), ib - cbB));
+    ia += ja == j;
+    ib += jb == j;
+    return j;
+  };
 
   f32x16_t oacc[DT];
 #pragma unroll
@@ -273,32 +292,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY, l_run = 0.f;
   const int g16 = l & 15, mbase = 16 * ((l >> 4) & 1);
 
-  if (start < end) {
-    const int j0 = __builtin_amdgcn_readlane(ccache, 0);
-    dma_k(j0);
-    dma_v(j0);
-  }
+  // two-entry look-ahead ring: (j, flags, scale) of steps u and u+1
+  int f0 = 0, f1 = 0;
+  float s0 = 1.f, s1 = 1.f;
+  int j0 = next_entry(f0, s0);
+  int j1 = j0 >= 0 ? next_entry(f1, s1) : -1;
+  if (j0 >= 0) dma_tile(0, j0);
+  if (j1 >= 0) dma_tile(1, j1);
 
-  for (int it = start; it < end; ++it) {
-    const int j = __builtin_amdgcn_readlane(ccache, it - cbase);
-    const float ksc = MODE == ATTN_FP8 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kscache), it - cbase)) : 1.f;
-    const bool has_next = it + 1 < end;
-    if (has_next && it + 1 - cbase == 64) {
-      cbase += 64;
-      wait_all();                            // tiles of j in LDS before the chunk fetch waits anyway
-      fetch_chunk(cbase);
-    }
-    const int jn = has_next ? __builtin_amdgcn_readlane(ccache, it + 1 - cbase) : 0;
-    const int kv0 = j * 64;
-    const bool live_blk = kv0 < a.S_valid;   // a block made only of padding is skipped
+  for (int u = 0; j0 >= 0; ++u) {
+    const int st = u & 1;
+    if (j1 >= 0) wait_vm<NKV_W>(); else wait_vm<0>();   // own share of tile j0 landed
+    wg_barrier();                                        // everybody's share
 
-    wait_vm<NV_W>();                         // own half of K_j landed (V_j may be in flight)
-    wg_barrier();                            // the other half too
-
-    // ---- S^T = K Q^T for this wave's 32 queries: sacc[kt], kv = kt*32 + 8(v/4) + 4 hi + v%4
-    const f32x16_t zero16 = {};
-    f32x16_t sacc[2];
-    if (live_blk) {
+    const int kv0 = j0 * 64;
+    const bool use = ((f0 >> pr) & 1) && kv0 < a.S_valid;
+    if (use) {
+      char BSA_LDS* kt0 = k_lds(st, 0);
+      // ---- S^T = K Q^T for this wave's 32 queries: sacc[kt], kv = kt*32 + 8(v/4) + 4 hi + v%4
+      const f32x16_t zero16 = {};
+      f32x16_t sacc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int r = kt * 32 + l32;
@@ -306,29 +319,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int s = 0; s < KS; ++s) {
           if constexpr (MODE == ATTN_FP8) {
             const int cb = 64 * s + 32 * hi;
-            i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb));
-            i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, cb + 16));
+            i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb));
+            i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb + 16));
             const i32x8_t k0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0, qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0,
                                                                        127, 0, 127);
           } else {
-            const bf16x8_t k0 = *(const bf16x8_t BSA_LDS*)(kt_lds[0] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+            const bf16x8_t k0 = *(const bf16x8_t BSA_LDS*)(kt0 + koff<RBK>(r, (16 * s + 8 * hi) * 2));
             sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0);
             if constexpr (MODE == ATTN_SPLIT_F32) {
-              const bf16x8_t k1 = *(const bf16x8_t BSA_LDS*)(kt_lds[1] + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+              const bf16x8_t k1 = *(const bf16x8_t BSA_LDS*)(k_lds(st, 1) + koff<RBK>(r, (16 * s + 8 * hi) * 2));
               sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[1][s], sacc[kt], 0, 0, 0);
               sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[0][s], sacc[kt], 0, 0, 0);
             }
           }
         }
       }
-    }
-    wait_lgkm0();
-    wg_barrier();                            // both waves are done with K_j
-    if (has_next) dma_k(jn);
-
-    bf16x8_t pop[4];
-    if (live_blk) {
       // ---- mask padded keys of the last block
       if (kv0 + 64 > a.S_valid) {
 #pragma unroll
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
       }
       // ---- online softmax (log2 domain, lazily rescaled)
-      const float c = a.scale_log2 * qsc * ksc;
+      const float c = a.scale_log2 * qsc * s0;
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -359,6 +365,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       const float mr = m_run;
       float ls = 0.f;
+      bf16x8_t pop[4];
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         i32x4_t w;
@@ -373,11 +380,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         pop[sp] = __builtin_bit_cast(bf16x8_t, w);
       }
       l_run += ls;
-    }
-
-    if (has_next) wait_vm<NK_W>(); else wait_vm<0>();   // own half of V_j landed
-    wg_barrier();
-    if (live_blk) {
       // ---- O^T += V^T P^T, V^T read from the row-major V tile with transposing reads
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -387,19 +389,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
 #pragma unroll
           for (int x = 0; x < NSPLIT; ++x) {
-            s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra, cb)));
-            s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt_lds[x] + voff<RBV>(ra + 8, cb)));
+            char BSA_LDS* vt = v_lds(st, x);
+            s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt + voff<RBV>(ra, cb)));
+            s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt + voff<RBV>(ra + 8, cb)));
             oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(v0, v1), pop[sp], oacc[dt], 0, 0, 0);
           }
         }
       }
     }
     wait_lgkm0();
-    wg_barrier();                            // both waves are done with V_j
-    if (has_next) dma_v(jn);
+    wg_barrier();                                        // everybody is done with stage st
+    int f2 = 0;
+    float s2 = 1.f;
+    const int j2 = j1 >= 0 ? next_entry(f2, s2) : -1;
+    if (j2 >= 0) dma_tile(st, j2);
+    j0 = j1; f0 = f1; s0 = s1;
+    j1 = j2; f1 = f2; s1 = s2;
   }
 
   // ---- epilogue: O = O^T / l, written row-major; padded rows and empty rows are 0
+  if (!mine_valid) return;
   const float lt = l_run + partner(l_run);
   const int q = i * 64 + wv * 32 + l32;
   const bool live = q < a.S_valid && lt > 0.f;
@@ -453,9 +462,9 @@ hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, 
 
 template <int MODE, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
-  const int total = a.B * a.H * a.nb;
+  const int total = a.B * a.H * ((a.nb + 1) / 2);
   dim3 grid(((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
-  hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(128), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
+  hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
                      a.k_scale);
   return hipGetLastError();
 }
