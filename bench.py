@@ -158,7 +158,19 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
     ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (scale for the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path shards by "
               f"(batch, head) with no communication, see the design notes)", file=sys.stderr)

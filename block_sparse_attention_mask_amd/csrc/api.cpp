@@ -164,7 +164,8 @@ bsa_status mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, 
 // ---------------------------------------------------------------------------
 size_t csr_workspace_size(int B, int H, int nb) {
   if (B < 1 || H < 1 || nb < 1) return 0;
-  return align256((size_t)B * H * nb * sizeof(int32_t));
+  const size_t rows = (size_t)B * H * nb;
+  return align256((rows + rows / 1024 + 1) * sizeof(int32_t));   // counts + segment sums
 }
 
 static bsa_status check_mask_args(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H, int nb) {

@@ -39,29 +39,58 @@ __global__ __launch_bounds__(256) void csr_count_kernel(const uint8_t* __restric
   if (l == 0) counts[row] = c;
 }
 
-// single workgroup exclusive scan: row_ptr[0..rows]
-__global__ __launch_bounds__(1024) void csr_scan_kernel(const int32_t* __restrict__ counts, int rows,
-                                                        int32_t* __restrict__ row_ptr) {
-  __shared__ int32_t part[1024];
-  const int t = threadIdx.x;
-  const int per = (rows + 1023) / 1024;
-  const int r0 = t * per, r1 = min(rows, r0 + per);
-  int s = 0;
-  for (int r = r0; r < r1; ++r) s += counts[r];
-  part[t] = s;
+// Exclusive scan of the row counts into row_ptr[0..rows], in two passes:
+// csr_block_sum_kernel reduces each 1024-row segment; csr_scan_kernel scans the
+// segment sums (in shared memory) and then its own segment.
+constexpr int SCAN_SEG = 1024;
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* sh, int& total) {
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  const int incl = wave_incl_scan_i32(v);
+  if (l == 63) sh[w] = incl;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {      // Hillis-Steele inclusive scan
-    int v = t >= o ? part[t - o] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  if (t < 16) {
+    int x = sh[t];
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(x, o, 16);
+      if (t >= o) x += y;
+    }
+    sh[16 + t] = x;     // inclusive scan of the wave sums
   }
-  int run = part[t] - s;
-  for (int r = r0; r < r1; ++r) {
-    row_ptr[r] = run;
-    run += counts[r];
-  }
-  if (t == 1023) row_ptr[rows] = part[1023];
+  __syncthreads();
+  total = sh[31];
+  const int r = incl - v + (w ? sh[16 + w - 1] : 0);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void csr_block_sum_kernel(const int32_t* __restrict__ counts, int rows,
+                                                             int32_t* __restrict__ seg_sum) {
+  __shared__ int sh[32];
+  const int r = blockIdx.x * SCAN_SEG + threadIdx.x;
+  int total;
+  block_excl_scan_1024(r < rows ? counts[r] : 0, sh, total);
+  if (threadIdx.x == 0) seg_sum[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(1024) void csr_scan_kernel(const int32_t* __restrict__ counts, int rows,
+                                                        const int32_t* __restrict__ seg_sum, int nseg,
+                                                        int32_t* __restrict__ row_ptr) {
+  __shared__ int sh[32];
+  __shared__ int base_sh;
+  // offset of this segment: sum of the earlier segment sums
+  int part = 0;
+  for (int x = threadIdx.x; x < (int)blockIdx.x; x += SCAN_SEG) part += seg_sum[x];
+  int tot_part;
+  block_excl_scan_1024(part, sh, tot_part);
+  if (threadIdx.x == 0) base_sh = tot_part;
+  __syncthreads();
+  const int base = base_sh;
+  const int r = blockIdx.x * SCAN_SEG + threadIdx.x;
+  const int v = r < rows ? counts[r] : 0;
+  int total;
+  const int ex = block_excl_scan_1024(v, sh, total);
+  if (r < rows) row_ptr[r] = base + ex;
+  if (blockIdx.x == nseg - 1 && threadIdx.x == 0) row_ptr[rows] = base + total;
 }
 
 // one wave per row: ascending kept column indices
@@ -92,7 +121,13 @@ hipError_t launch_csr(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H,
   hipLaunchKernelGGL(csr_count_kernel, dim3(g), dim3(256), 0, st, mask, sb, sh, H, nb, rows, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, st, (const int32_t*)counts, rows, row_ptr);
+  const int nseg = (rows + SCAN_SEG - 1) / SCAN_SEG;
+  int32_t* seg_sum = counts + rows;
+  hipLaunchKernelGGL(csr_block_sum_kernel, dim3(nseg), dim3(1024), 0, st, (const int32_t*)counts, rows, seg_sum);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(nseg), dim3(1024), 0, st, (const int32_t*)counts, rows,
+                     (const int32_t*)seg_sum, nseg, row_ptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(csr_fill_kernel, dim3(g), dim3(256), 0, st, mask, sb, sh, H, nb, rows,

@@ -42,22 +42,30 @@ __device__ __forceinline__ void token_coord(const StaGeom& g, int p, int& t, int
 
 __device__ __forceinline__ int32_t pack_tile(int a, int b, int c) { return (a << 20) | (b << 10) | c; }
 
-// One thread per block: distinct window tiles of its real tokens.
-__global__ __launch_bounds__(64) void sta_tiles_kernel(StaGeom g, int32_t* __restrict__ tiles) {
-  const int i = blockIdx.x * 64 + threadIdx.x;
+// One wave per block, one token per lane: the distinct window tiles of the block's
+// real tokens, in first-occurrence order.
+__global__ __launch_bounds__(256) void sta_tiles_kernel(StaGeom g, int32_t* __restrict__ tiles) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
   if (i >= g.nb) return;
-  int32_t* out = tiles + (int64_t)i * (STA_MAX_TILES + 1);
-  int n = 0;
-  const int p1 = min((i + 1) * BSA_N, g.S_valid);
-  for (int p = i * BSA_N; p < p1; ++p) {
+  const int p = i * BSA_N + l;
+  const bool real = p < g.S_valid;
+  int32_t key = -1;
+  if (real) {
     int t, h, w;
     token_coord(g, p, t, h, w);
-    const int32_t key = pack_tile(t / g.tt, h / g.th, w / g.tw);
-    bool seen = false;
-    for (int x = 0; x < n; ++x) seen |= out[1 + x] == key;
-    if (!seen) out[1 + n++] = key;
+    key = pack_tile(t / g.tt, h / g.th, w / g.tw);
   }
-  out[0] = n;
+  // a lane is the first of its key if no lower lane holds the same key
+  bool first = real;
+  for (int o = 0; o < 63; ++o) {
+    const int other = __shfl(key, o, 64);
+    if (o < l && other == key) first = false;
+  }
+  const uint64_t ball = __ballot(first);
+  int32_t* out = tiles + (int64_t)i * (STA_MAX_TILES + 1);
+  if (first) out[1 + __popcll(ball & ((1ull << l) - 1ull))] = key;
+  if (l == 0) out[0] = __popcll(ball);
 }
 
 // One workgroup per query block i; threads sweep the key blocks j.
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(256) void sta_pairs_kernel(StaGeom g, const int32_t
 }
 
 hipError_t launch_sta(const StaGeom& g, int32_t* tiles_ws, uint8_t* mask_out, hipStream_t st) {
-  hipLaunchKernelGGL(sta_tiles_kernel, dim3((g.nb + 63) / 64), dim3(64), 0, st, g, tiles_ws);
+  hipLaunchKernelGGL(sta_tiles_kernel, dim3((g.nb + 3) / 4), dim3(256), 0, st, g, tiles_ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sta_pairs_kernel, dim3(g.nb), dim3(256), 0, st, g, (const int32_t*)tiles_ws, mask_out);

@@ -265,3 +265,20 @@ def test_attention_f32_d128(gpu_lib):
         O, _ = oracle.block_sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), keep[0, h], 64, Sv)
         err = np.abs(f64(out[0, h]) - O)
         assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR
+
+
+def test_csr_multi_segment(gpu_lib):
+    """More rows than one scan segment (1024), a broadcast plane, and empty rows."""
+    rng = np.random.default_rng(21)
+    m = rng.random((2, 9, 70, 70)) < 0.15
+    m[1, 4, :10] = False
+    t = torch.from_numpy(m.astype(np.uint8)).to(DEV)
+    rp, ci = gpu_lib.mask_to_csr(t)
+    rp_ref, ci_ref = oracle.mask_to_csr(m.reshape(-1, 70))
+    assert np.array_equal(rp.cpu().numpy(), rp_ref)
+    assert np.array_equal(ci.cpu().numpy()[:rp_ref[-1]], ci_ref)
+    plane = torch.from_numpy(m[0, 0].astype(np.uint8)).to(DEV)
+    rp2, ci2 = gpu_lib.mask_to_csr(plane, B=2, H=9)
+    rp2_ref, ci2_ref = oracle.mask_to_csr(np.broadcast_to(m[0, 0], (18, 70, 70)).reshape(-1, 70))
+    assert np.array_equal(rp2.cpu().numpy(), rp2_ref)
+    assert np.array_equal(ci2.cpu().numpy()[:rp2_ref[-1]], ci2_ref)
