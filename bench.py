@@ -29,6 +29,21 @@ def _flops_per_tile(D):
     return 4.0 * 64 * 64 * D
 
 
+def _measured_traffic(workload, fp8=False, dense=False):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, copy-calibrated), or None when the kernel source has
+    changed since they were taken or the workload was not profiled."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["attn_fwd"]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec["sha256_prefix"] or fp8 or dense:
+        return None
+    return rec["traffic_bytes_per_launch"].get(workload)
+
+
 def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     import torch
     import block_sparse_attention_mask_amd as bsa
@@ -208,7 +223,8 @@ def main():
         if thr is not None else None,
         "kept_fraction": round(r["kept_fraction"], 5), "kept_tiles": r["kept_tiles"],
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "frac": round(attn_tflops / peak, 4),
+                     "traffic": _measured_traffic(cfg.name, args.fp8, args.dense),
                      "kernel": "attn_fwd_kernel", "per_launch_flops": kept_flops},
     }
     if not args.no_cpu_baseline:
