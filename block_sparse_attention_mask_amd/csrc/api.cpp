@@ -71,8 +71,8 @@ int bsa_abi_version(void) { return 1; }
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
   if (!s || s->S <= 0 || s->D <= 0) return 0;
-  const size_t nb = (size_t)s->S / 64, bh = (size_t)s->B * s->H;
-  return 2 * align256(bh * nb * (size_t)s->D * sizeof(double));
+  const size_t nbp = ((size_t)s->S / 64 + 15) / 16 * 16, bh = (size_t)s->B * s->H;   // 16-block tiles
+  return 2 * align256(bh * nbp * (size_t)s->D * sizeof(double));
 }
 
 bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
@@ -96,9 +96,9 @@ bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_
   if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
   if (scale <= 0.0) scale = 1.0 / std::sqrt((double)shape->D);
 
-  const size_t bh = (size_t)shape->B * shape->H;
+  const size_t bh = (size_t)shape->B * shape->H, nbp = ((size_t)nb + 15) / 16 * 16;
   double* qbar = (double*)ws;
-  double* kbarT = (double*)((char*)ws + align256(bh * nb * (size_t)shape->D * sizeof(double)));
+  double* kbarT = (double*)((char*)ws + align256(bh * nbp * (size_t)shape->D * sizeof(double)));
   const int64_t qs[3] = {q->sb, q->sh, q->ss}, ks[3] = {k->sb, k->sh, k->ss};
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = bsa::launch_pool(q->dtype == BSA_F32, shape->D, q->ptr, qs, k->ptr, ks, shape->B, shape->H, nb,

@@ -11,21 +11,33 @@
 // GPU formulation (no sort is materialised):
 //   * pool_kernel streams Q and K once and writes exact fp64 block means
 //     (sums of 64 bf16 values are exact in fp64);
-//   * select_kernel computes 16 rows of L = scale * Qbar Kbar^T per workgroup in
-//     fp64 registers, softmaxes them, and finds for each row the "pivot": the
+//   * select_kernel computes 16 rows of L = scale * Qbar Kbar^T per workgroup on the
+//     fp64 MFMA, softmaxes them, and finds for each row the "pivot": the
 //     first entry, in descending (p, -index) order, at which the cumulative mass
 //     reaches 1 - thr. Entries before it and the pivot itself are kept. The pivot
-//     is found by a radix select on the fp64 bit pattern of p (monotone for p >= 0)
-//     using per-bucket mass histograms. Masses are accumulated in 2^-60 fixed
-//     point, so the sums are exact integers and the result does not depend on the
-//     order of the atomic additions (run-to-run deterministic).
+//     is found by a radix select on the 2^-60 fixed-point mass w = floor(p 2^60) of
+//     each entry (monotone in p; distinct for distinct p >= 2^-8, so only entries
+//     closer than 2^-60 to each other are ordered by index), with per-bucket
+//     histograms of count and mass. The sums are exact integers, so the result does
+//     not depend on the order of the atomic additions (run-to-run deterministic).
 #include "common.h"
 #include "launch.h"
 
 namespace bsa {
 
 // ----------------------------------------------------------------------------
-// Pooling: Qbar[bh][i][d] = (1/64) sum_r Q[bh][64 i + r][d];  KbarT[bh][d][i] likewise.
+// Pooled vectors are stored in the operand order of v_mfma_f64_16x16x4_f64: for a
+// tile of 16 blocks (rows of Qbar, or columns of Kbar^T) and k-step s (channels
+// 4s..4s+3), lane l of the MFMA holds block 16*tile + l%16, channel 4s + l/16, so
+// each operand is one coalesced 512-byte load. The layout is [bh][tile][D/4][64].
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ int64_t mf_index(int bh, int nb, int D, int blk, int d) {
+  const int ntile = (nb + 15) / 16;
+  return (((int64_t)bh * ntile + blk / 16) * (D / 4) + d / 4) * 64 + (blk % 16) + 16 * (d % 4);
+}
+
+// ----------------------------------------------------------------------------
+// Pooling: Qbar[bh][i][d] = (1/64) sum_r Q[bh][64 i + r][d], and Kbar likewise.
 // One workgroup per (block i, bh, tensor). Each thread loads 16 bytes per row.
 // ----------------------------------------------------------------------------
 template <typename T, int D>
@@ -76,10 +88,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
 #pragma unroll
     for (int r = 0; r < RPP; ++r) s += part[r][t];
     s *= (1.0 / BSA_N);
-    if (which == 0)
-      qbar[((int64_t)bh * nb + i) * D + t] = s;
-    else
-      kbarT[((int64_t)bh * D + t) * nb + i] = s;
+    double* dst = which == 0 ? qbar : kbarT;
+    dst[mf_index(bh, nb, D, i, t)] = s;
   }
 }
 
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
 // Row selection.
 // ----------------------------------------------------------------------------
 constexpr int SEL_ROWS = 16;
-constexpr int SEL_WAVES = 4;
+constexpr int SEL_WAVES = 8;
 
 enum : int { ROW_ACTIVE = 0, ROW_PIVOT = 1, ROW_ALL = 2, ROW_TIE = 3, ROW_SKIP = 4 };
 
@@ -105,25 +115,42 @@ __device__ __forceinline__ uint64_t fixed_mass(double p) {
   return (uint64_t)(p * 0x1p60);
 }
 
-// digit of key for the current pass; returns -1 when the key is outside the range
+// Radix digits of a fixed-point mass w (the sort key). The first pass is logarithmic:
+// w < 4 gets bucket w; otherwise, with e the position of the leading one, bucket
+// 4 + 4 (e - 2) + (the two bits below the leading one), i.e. the range
+// [(4 + m) << (e - 2), (5 + m) << (e - 2)). Later passes split the current range
+// [lo, lo + 2^span) by its top 8 bits. Returns -1 when w is outside the range.
+__device__ __forceinline__ int first_digit(uint64_t w) {
+  if (w < 4) return (int)w;
+  const int e = 63 - __builtin_clzll(w);
+  return 4 + 4 * (e - 2) + (int)((w >> (e - 2)) & 3);
+}
+__device__ __forceinline__ void first_range(int dg, uint64_t& lo, int& span) {
+  if (dg < 4) { lo = (uint64_t)dg; span = 0; return; }
+  const int e = (dg - 4) / 4 + 2, m = (dg - 4) % 4;
+  lo = (uint64_t)(4 + m) << (e - 2);
+  span = e - 2;
+}
 __device__ __forceinline__ int sel_digit(uint64_t key, const SelRowState& st) {
-  if (st.span < 0) {               // exponent pass: 256 buckets over the fp64 exponent
-    int e = (int)(key >> 52);      // sign bit is 0
-    int d = e - 768;
-    return d < 0 ? 0 : (d > 255 ? 255 : d);
-  }
+  if (st.span < 0) return first_digit(key);
   if (key < st.lo || key - st.lo >= (1ull << st.span)) return -1;
-  int db = st.span < 8 ? st.span : 8;
+  const int db = st.span < 8 ? st.span : 8;
   return (int)((key - st.lo) >> (st.span - db));
 }
 
-template <int C>   // C = column chunks of 64 per wave
-__global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ qbar,
-                                                     const double* __restrict__ kbarT, int nb, int D,
-                                                     double scale, uint64_t T_fixed,
-                                                     const uint8_t* __restrict__ or_mask, int64_t or_sb,
-                                                     int64_t or_sh, int H, uint8_t* __restrict__ mask_out) {
-  __shared__ double qs[SEL_ROWS][128];
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// One workgroup of SEL_WAVES waves per tile of 16 query-block rows of one head.
+// The reduced map of the 16 rows is an MFMA f64 product (16 rows) x (16-column
+// tiles); wave w owns column tiles w, w + SEL_WAVES, ... (NCT of them). In the
+// result layout lane l holds rows {4v + l/16 : v = 0..3} of column 16*tile + l%16,
+// so a row lives in one 16-lane group of every wave.
+template <int NCT, int KS>   // KS = D / 4 k-steps of the f64 MFMA
+__global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __restrict__ qmf,
+                                                               const double* __restrict__ kmf, int nb, int D,
+                                                               double scale, uint64_t T_fixed,
+                                                               const uint8_t* __restrict__ or_mask, int64_t or_sb,
+                                                               int64_t or_sh, int H, uint8_t* __restrict__ mask_out) {
   __shared__ uint64_t hmass[SEL_ROWS][256];
   __shared__ uint32_t hcnt[SEL_ROWS][256];
   __shared__ uint32_t tiebits[SEL_ROWS][64];
@@ -131,102 +158,110 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   __shared__ uint64_t redu[SEL_ROWS][SEL_WAVES];
   __shared__ SelRowState st[SEL_ROWS];
   __shared__ int any_active;
+  __shared__ double qa_lds[32 * 64];   // the 16 rows' Qbar operands, MFMA order
 
-  const int bh = blockIdx.y, row0 = blockIdx.x * SEL_ROWS;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int bh = blockIdx.y, rt = blockIdx.x, row0 = rt * SEL_ROWS;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lc = l & 15;
+  const int ntile = (nb + 15) / 16;
 
-  for (int x = tid; x < SEL_ROWS * D; x += 256) {
-    int r = x / D, d = x % D;
-    qs[r][d] = (row0 + r < nb) ? qbar[((int64_t)bh * nb + row0 + r) * D + d] : 0.0;
-  }
-  __syncthreads();
-
-  // ---- reduced map rows: acc[r][c] = <Qbar_row, Kbar_j>, j = (c*4 + w)*64 + l
-  double acc[SEL_ROWS][C];
+  // ---- reduced map: acc[c] = Qbar(16 rows) . Kbar^T(column tile w + SEL_WAVES c).
+  // All KS operands of a column tile are loaded before its MFMAs (one latency per
+  // tile); columns past nb hold unspecified values and are masked below.
+  f64x4_t acc[NCT];
 #pragma unroll
-  for (int r = 0; r < SEL_ROWS; ++r)
+  for (int c = 0; c < NCT; ++c) acc[c] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  {
+    const double* qa = qmf + ((int64_t)bh * ntile + rt) * KS * 64;
+    for (int x = tid; x < KS * 64; x += SEL_WAVES * 64) qa_lds[x] = row0 + (x & 15) < nb ? qa[x] : 0.0;
+    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[r][c] = 0.0;
-  bool valid[C];
-  int col[C];
+    for (int c = 0; c < NCT; ++c) {
+      const int ct = w + SEL_WAVES * c;
+      if (ct >= ntile) break;
+      const double* kb = kmf + ((int64_t)bh * ntile + ct) * KS * 64 + l;
+      double bv[KS];
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    col[c] = (c * SEL_WAVES + w) * 64 + l;
-    valid[c] = col[c] < nb;
-  }
-  const double* kb = kbarT + (int64_t)bh * D * nb;
-  for (int d = 0; d < D; d += 2) {
-    double k0[C], k1[C];
+      for (int s = 0; s < KS; ++s) bv[s] = kb[s * 64];
+      f64x4_t a4 = acc[c];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      k0[c] = valid[c] ? kb[(int64_t)d * nb + col[c]] : 0.0;
-      k1[c] = valid[c] ? kb[(int64_t)(d + 1) * nb + col[c]] : 0.0;
-    }
-#pragma unroll
-    for (int r = 0; r < SEL_ROWS; ++r) {
-      double q0 = qs[r][d], q1 = qs[r][d + 1];
-#pragma unroll
-      for (int c = 0; c < C; ++c) acc[r][c] = fma(q1, k1[c], fma(q0, k0[c], acc[r][c]));
+      for (int s = 0; s < KS; ++s) a4 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa_lds[s * 64 + l], bv[s], a4, 0, 0, 0);
+      acc[c] = a4;
     }
   }
 
-  // ---- softmax of each row (fp64), max and sum reduced across the 4 waves
+  // column of value (c) in this lane, its validity; rows of value slot v: 4v + g
+  auto colof = [&](int c) { return (w + SEL_WAVES * c) * 16 + lc; };
+
+  // ---- softmax of each row in fp64: max and sum over the 16-lane group, then the waves
 #pragma unroll
-  for (int r = 0; r < SEL_ROWS; ++r) {
+  for (int v = 0; v < 4; ++v) {
     double m = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      acc[r][c] *= scale;
-      if (valid[c]) m = fmax(m, acc[r][c]);
+    for (int c = 0; c < NCT; ++c) {
+      acc[c][v] *= scale;
+      if (colof(c) < nb) m = fmax(m, acc[c][v]);
     }
-    m = wave_max_f64(m);
-    if (l == 0) red[r][w] = m;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmax(m, __shfl_xor(m, o, 64));
+    if (lc == 0) red[4 * v + g][w] = m;
   }
   __syncthreads();
-  double rowmax[SEL_ROWS];
+  double rowmax[4];
 #pragma unroll
-  for (int r = 0; r < SEL_ROWS; ++r)
-    rowmax[r] = fmax(fmax(red[r][0], red[r][1]), fmax(red[r][2], red[r][3]));
-  __syncthreads();
+  for (int v = 0; v < 4; ++v) {
+    double m = red[4 * v + g][0];
 #pragma unroll
-  for (int r = 0; r < SEL_ROWS; ++r) {
-    double s = 0.0;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      double e = valid[c] ? exp(acc[r][c] - rowmax[r]) : 0.0;
-      acc[r][c] = e;
-      s += e;
-    }
-    s = wave_sum_f64(s);
-    if (l == 0) red[r][w] = s;
+    for (int x = 1; x < SEL_WAVES; ++x) m = fmax(m, red[4 * v + g][x]);
+    rowmax[v] = m;
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < SEL_ROWS; ++r) {
-    double tot = ((red[r][0] + red[r][1]) + red[r][2]) + red[r][3];
+  for (int v = 0; v < 4; ++v) {
+    double sum = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const double e = colof(c) < nb ? exp(acc[c][v] - rowmax[v]) : 0.0;
+      acc[c][v] = e;
+      sum += e;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    if (lc == 0) red[4 * v + g][w] = sum;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    double tot = red[4 * v + g][0];
+#pragma unroll
+    for (int x = 1; x < SEL_WAVES; ++x) tot += red[4 * v + g][x];    // fixed order: deterministic
+    const double inv = 1.0 / tot;
     uint64_t ms = 0;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      acc[r][c] = acc[r][c] / tot;           // p >= 0; its bits are the sort key
-      ms += fixed_mass(acc[r][c]);
+    for (int c = 0; c < NCT; ++c) {
+      // from here on the slot holds the fixed-point mass w = floor(p 2^60), the sort key
+      const uint64_t wq = fixed_mass(acc[c][v] * inv);
+      acc[c][v] = __longlong_as_double((long long)wq);
+      ms += wq;
     }
-    ms = wave_sum_u64(ms);
-    if (l == 0) redu[r][w] = ms;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ms += __shfl_xor(ms, o, 64);
+    if (lc == 0) redu[4 * v + g][w] = ms;
   }
   __syncthreads();
   if (tid < SEL_ROWS) {
-    int r = tid;
-    uint64_t total = redu[r][0] + redu[r][1] + redu[r][2] + redu[r][3];
-    SelRowState s;
-    s.lo = 0;
-    s.mass_above = 0;
-    s.span = -1;
-    s.cnt = 0;
-    s.tie_keep = 0;
-    if (row0 + r >= nb) s.status = ROW_SKIP;
-    else if (total < T_fixed) s.status = ROW_ALL;   // every entry is reached before the mass 1 - thr
-    else s.status = ROW_ACTIVE;
-    st[r] = s;
+    const int r = tid;
+    uint64_t total = 0;
+    for (int x = 0; x < SEL_WAVES; ++x) total += redu[r][x];
+    SelRowState n;
+    n.lo = 0;
+    n.mass_above = 0;
+    n.span = -1;
+    n.cnt = 0;
+    n.tie_keep = 0;
+    if (row0 + r >= nb) n.status = ROW_SKIP;
+    else if (total < T_fixed) n.status = ROW_ALL;   // every entry is reached before the mass 1 - thr
+    else n.status = ROW_ACTIVE;
+    st[r] = n;
   }
   if (tid == 0) any_active = 1;
   __syncthreads();
@@ -234,31 +269,32 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   // ---- radix select of the pivot, all rows in lock step
   for (int pass = 0; pass < 9; ++pass) {
     if (!any_active) break;
-    for (int x = tid; x < SEL_ROWS * 256; x += 256) {
+    for (int x = tid; x < SEL_ROWS * 256; x += SEL_WAVES * 64) {
       hmass[x / 256][x % 256] = 0;
       hcnt[x / 256][x % 256] = 0;
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < SEL_ROWS; ++r) {
-      SelRowState s = st[r];
-      if (s.status != ROW_ACTIVE) continue;
+    for (int v = 0; v < 4; ++v) {
+      const int r = 4 * v + g;
+      const SelRowState sr = st[r];
+      if (sr.status != ROW_ACTIVE) continue;
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        if (!valid[c]) continue;
-        uint64_t key = (uint64_t)__double_as_longlong(acc[r][c]);
-        int dg = sel_digit(key, s);
+      for (int c = 0; c < NCT; ++c) {
+        if (colof(c) >= nb) continue;
+        const uint64_t key = (uint64_t)__double_as_longlong(acc[c][v]);
+        const int dg = sel_digit(key, sr);
         if (dg >= 0) {
-          atomicAdd((unsigned long long*)&hmass[r][dg], (unsigned long long)fixed_mass(acc[r][c]));
+          atomicAdd((unsigned long long*)&hmass[r][dg], (unsigned long long)key);
           atomicAdd(&hcnt[r][dg], 1u);
         }
       }
     }
     __syncthreads();
-    // each wave scans 4 rows: lane l owns buckets 255-4l .. 252-4l (descending keys)
+    // each wave scans SEL_ROWS / SEL_WAVES rows: lane l owns buckets 255-4l .. 252-4l
     for (int r = w; r < SEL_ROWS; r += SEL_WAVES) {
-      SelRowState s = st[r];
-      if (s.status != ROW_ACTIVE) continue;
+      const SelRowState sr = st[r];
+      if (sr.status != ROW_ACTIVE) continue;
       uint64_t mb[4];
       uint32_t cb[4];
       uint64_t lt = 0;
@@ -268,11 +304,10 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
         cb[x] = hcnt[r][255 - 4 * l - x];
         lt += mb[x];
       }
-      uint64_t incl = wave_incl_scan_u64(lt);
-      uint64_t before = s.mass_above + (incl - lt);
-      bool cross = before + lt >= T_fixed;
-      uint64_t ball = __ballot(cross);
-      int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
+      const uint64_t incl = wave_incl_scan_u64(lt);
+      const uint64_t before = sr.mass_above + (incl - lt);
+      const uint64_t ball = __ballot(before + lt >= T_fixed);
+      const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
       if (l == L) {
         uint64_t cum = before;
         int xs = 3;
@@ -281,24 +316,23 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
           if (cum + mb[x] >= T_fixed) { xs = x; break; }
           cum += mb[x];
         }
-        int dg = 255 - 4 * l - xs;
-        SelRowState n = s;
+        const int dg = 255 - 4 * l - xs;
+        SelRowState n = sr;
         n.mass_above = cum;
         n.cnt = (int)cb[xs];
-        if (s.span < 0) {
-          n.lo = (uint64_t)(dg + 768) << 52;
-          n.span = 52;
+        if (sr.span < 0) {
+          first_range(dg, n.lo, n.span);
         } else {
-          int db = s.span < 8 ? s.span : 8;
-          n.span = s.span - db;
-          n.lo = s.lo + ((uint64_t)dg << n.span);
+          const int db = sr.span < 8 ? sr.span : 8;
+          n.span = sr.span - db;
+          n.lo = sr.lo + ((uint64_t)dg << n.span);
         }
         if (n.cnt <= 1) n.status = ROW_PIVOT;
         else if (n.span == 0) {
           // identical keys: visited by ascending index, each adds the same mass
-          uint64_t wq = fixed_mass(__longlong_as_double((long long)n.lo));
-          uint64_t need = T_fixed - n.mass_above;          // > 0
-          uint64_t t = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
+          const uint64_t wq = n.lo;
+          const uint64_t need = T_fixed - n.mass_above;          // > 0
+          const uint64_t t = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
           n.tie_keep = (int)(t < (uint64_t)n.cnt ? t : (uint64_t)n.cnt);
           n.status = ROW_TIE;
         }
@@ -307,28 +341,29 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
     }
     __syncthreads();
     if (tid == 0) {
-      int a = 0;
-      for (int r = 0; r < SEL_ROWS; ++r) a |= st[r].status == ROW_ACTIVE;
-      any_active = a;
+      int act = 0;
+      for (int r = 0; r < SEL_ROWS; ++r) act |= st[r].status == ROW_ACTIVE;
+      any_active = act;
     }
     __syncthreads();
   }
 
   // ---- ties: rank tied entries by ascending column index
   bool need_ties = false;
-#pragma unroll
   for (int r = 0; r < SEL_ROWS; ++r) need_ties |= st[r].status == ROW_TIE;
   if (need_ties) {
-    for (int x = tid; x < SEL_ROWS * 64; x += 256) tiebits[x / 64][x % 64] = 0;
+    for (int x = tid; x < SEL_ROWS * 64; x += SEL_WAVES * 64) tiebits[x / 64][x % 64] = 0;
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < SEL_ROWS; ++r) {
+    for (int v = 0; v < 4; ++v) {
+      const int r = 4 * v + g;
       if (st[r].status != ROW_TIE) continue;
-      uint64_t lo = st[r].lo;
+      const uint64_t lo = st[r].lo;
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        if (valid[c] && (uint64_t)__double_as_longlong(acc[r][c]) == lo)
-          atomicOr(&tiebits[r][col[c] >> 5], 1u << (col[c] & 31));
+      for (int c = 0; c < NCT; ++c) {
+        const int j = colof(c);
+        if (j < nb && (uint64_t)__double_as_longlong(acc[c][v]) == lo) atomicOr(&tiebits[r][j >> 5], 1u << (j & 31));
+      }
     }
     __syncthreads();
   }
@@ -336,30 +371,32 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   // ---- write the mask rows (OR'd with the optional mask)
   const int b = bh / H, h = bh % H;
 #pragma unroll
-  for (int r = 0; r < SEL_ROWS; ++r) {
-    SelRowState s = st[r];
-    if (s.status == ROW_SKIP) continue;
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * v + g;
+    const SelRowState sr = st[r];
+    if (sr.status == ROW_SKIP) continue;
     const int row = row0 + r;
     uint8_t* dst = mask_out + ((int64_t)bh * nb + row) * nb;
     const uint8_t* om = or_mask ? or_mask + b * or_sb + h * or_sh + (int64_t)row * nb : nullptr;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      if (!valid[c]) continue;
-      uint64_t key = (uint64_t)__double_as_longlong(acc[r][c]);
+    for (int c = 0; c < NCT; ++c) {
+      const int j = colof(c);
+      if (j >= nb) continue;
+      const uint64_t key = (uint64_t)__double_as_longlong(acc[c][v]);
       bool keep;
-      if (s.status == ROW_ALL) keep = true;
-      else if (s.status == ROW_PIVOT) keep = key >= s.lo;
+      if (sr.status == ROW_ALL) keep = true;
+      else if (sr.status == ROW_PIVOT) keep = key >= sr.lo;
       else {   // ROW_TIE
-        if (key != s.lo) keep = key > s.lo;
+        if (key != sr.lo) keep = key > sr.lo;
         else {
-          int j = col[c], rank = 0;
+          int rank = 0;
           for (int x = 0; x < (j >> 5); ++x) rank += __popc(tiebits[r][x]);
           rank += __popc(tiebits[r][j >> 5] & ((1u << (j & 31)) - 1u));
-          keep = rank < s.tie_keep;
+          keep = rank < sr.tie_keep;
         }
       }
-      if (om && om[col[c]]) keep = true;
-      dst[col[c]] = keep ? 1 : 0;
+      if (om && om[j]) keep = true;
+      dst[j] = keep ? 1 : 0;
     }
   }
 }
@@ -384,26 +421,31 @@ hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* qs, const 
                  : launch_pool_t<u16, 128>(q, qs, k, ks, B, H, nb, qbar, kbarT, st);
 }
 
-template <int C>
-static hipError_t launch_select_c(const double* qbar, const double* kbarT, int B, int H, int nb, int D,
+template <int NCT>
+static hipError_t launch_select_c(const double* qmf, const double* kmf, int B, int H, int nb, int D,
                                   double scale, uint64_t T_fixed, const uint8_t* or_mask, int64_t or_sb,
                                   int64_t or_sh, uint8_t* mask_out, hipStream_t st) {
   dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS, B * H);
-  hipLaunchKernelGGL((select_kernel<C>), grid, dim3(256), 0, st, qbar, kbarT, nb, D, scale, T_fixed, or_mask,
-                     or_sb, or_sh, H, mask_out);
+  if (D == 64)
+    hipLaunchKernelGGL((select_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
+                       or_mask, or_sb, or_sh, H, mask_out);
+  else
+    hipLaunchKernelGGL((select_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
+                       or_mask, or_sb, or_sh, H, mask_out);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const double* qbar, const double* kbarT, int B, int H, int nb, int D, double scale,
+hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                          uint8_t* mask_out, hipStream_t st) {
-  const int chunks = (nb + 63) / 64;
-  const int C = (chunks + SEL_WAVES - 1) / SEL_WAVES;
+  const int ntile = (nb + 15) / 16;
+  const int nct = (ntile + SEL_WAVES - 1) / SEL_WAVES;
 #define BSA_SEL_CASE(n) \
-  case n: return launch_select_c<n>(qbar, kbarT, B, H, nb, D, scale, T_fixed, or_mask, or_sb, or_sh, mask_out, st);
-  switch (C) {
-    BSA_SEL_CASE(1) BSA_SEL_CASE(2) BSA_SEL_CASE(3) BSA_SEL_CASE(4)
-    BSA_SEL_CASE(5) BSA_SEL_CASE(6) BSA_SEL_CASE(7) BSA_SEL_CASE(8)
+  case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, or_mask, or_sb, or_sh, mask_out, st);
+  switch (nct) {
+    BSA_SEL_CASE(1) BSA_SEL_CASE(2) BSA_SEL_CASE(3) BSA_SEL_CASE(4) BSA_SEL_CASE(5) BSA_SEL_CASE(6)
+    BSA_SEL_CASE(7) BSA_SEL_CASE(8) BSA_SEL_CASE(9) BSA_SEL_CASE(10) BSA_SEL_CASE(11) BSA_SEL_CASE(12)
+    BSA_SEL_CASE(13) BSA_SEL_CASE(14) BSA_SEL_CASE(15) BSA_SEL_CASE(16)
     default: return hipErrorInvalidValue;
   }
 #undef BSA_SEL_CASE
