@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/bsa.h"
+#include "bsa.h"
 #include "launch.h"
 
 namespace {

@@ -312,29 +312,37 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
       // ---- S^T = K Q^T for this wave's 32 queries: sacc[kt], kv = kt*32 + 8(v/4) + 4 hi + v%4
       const f32x16_t zero16 = {};
       f32x16_t sacc[2];
+      KOp kk[2][KS];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int r = kt * 32 + l32;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
+          const int r = kt * 32 + l32;
           if constexpr (MODE == ATTN_FP8) {
             const int cb = 64 * s + 32 * hi;
             i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb));
             i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb + 16));
-            const i32x8_t k0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0, qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0,
-                                                                       127, 0, 127);
+            kk[kt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           } else {
-            const bf16x8_t k0 = *(const bf16x8_t BSA_LDS*)(kt0 + koff<RBK>(r, (16 * s + 8 * hi) * 2));
-            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0);
+            kk[kt][s] = *(const bf16x8_t BSA_LDS*)(kt0 + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+          }
+        }
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          if constexpr (MODE == ATTN_FP8) {
+            sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kk[kt][s], qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0, 127, 0, 127);
+          } else {
+            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[kt][s], qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0);
             if constexpr (MODE == ATTN_SPLIT_F32) {
+              const int r = kt * 32 + l32;
               const bf16x8_t k1 = *(const bf16x8_t BSA_LDS*)(k_lds(st, 1) + koff<RBK>(r, (16 * s + 8 * hi) * 2));
-              sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[1][s], sacc[kt], 0, 0, 0);
+              sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[kt][s], qop[1][s], sacc[kt], 0, 0, 0);
               sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[0][s], sacc[kt], 0, 0, 0);
             }
           }
         }
-      }
       // ---- mask padded keys of the last block
       if (kv0 + 64 > a.S_valid) {
 #pragma unroll
@@ -382,11 +390,11 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
       l_run += ls;
       // ---- O^T += V^T P^T, V^T read from the row-major V tile with transposing reads
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
+      for (int sp = 0; sp < 4; ++sp) {
+        const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
 #pragma unroll
-        for (int sp = 0; sp < 4; ++sp) {
-          const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
+        for (int dt = 0; dt < DT; ++dt) {
+          const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
 #pragma unroll
           for (int x = 0; x < NSPLIT; ++x) {
             char BSA_LDS* vt = v_lds(st, x);
