@@ -156,9 +156,10 @@ __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lg
 // blocks share most of their kv blocks, so most tiles serve both). A block visits
 // exactly its own tiles, in the same ascending order as it would alone.
 //
-// K/V tiles are double-buffered: tile u+2 is copied into the buffer of tile u as soon
-// as all waves are done with tile u, so every copy has two steps of compute to land.
-// Each wave issues a quarter of every tile copy.
+// K/V tiles are double-buffered with one barrier per step: a wave passes the barrier
+// that opens step u once its own part of tile u has landed, and only after finishing
+// step u-1, so right after it tile u+1 is copied into the buffer step u-1 read and has
+// all of step u's compute to land. Each wave issues a quarter of every tile copy.
 template <int MODE, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
@@ -172,8 +173,6 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   constexpr int DT = D / 32;                        // 32-wide d tiles of the output
   constexpr int KS = MODE == ATTN_FP8 ? D / 64 : D / 16;   // k-steps of S = K Q^T
   using KOp = typename std::conditional<MODE == ATTN_FP8, i32x8_t, bf16x8_t>::type;
-  // DMA instructions each wave issues per tile (K and V, all split parts)
-  constexpr int NKV_W = STAGE / 1024 / 4;
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   char BSA_LDS* lds = (char BSA_LDS*)smem;
@@ -298,12 +297,12 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   int j0 = next_entry(f0, s0);
   int j1 = j0 >= 0 ? next_entry(f1, s1) : -1;
   if (j0 >= 0) dma_tile(0, j0);
-  if (j1 >= 0) dma_tile(1, j1);
 
   for (int u = 0; j0 >= 0; ++u) {
     const int st = u & 1;
-    if (j1 >= 0) wait_vm<NKV_W>(); else wait_vm<0>();   // own share of tile j0 landed
-    wg_barrier();                                        // everybody's share
+    wait_vm<0>();                                        // own share of tile j0 landed
+    wg_barrier();                                        // everybody's share; step u-1 done everywhere
+    if (j1 >= 0) dma_tile(st ^ 1, j1);                   // into the buffer step u-1 used
 
     const int kv0 = j0 * 64;
     const bool use = ((f0 >> pr) & 1) && kv0 < a.S_valid;
@@ -405,12 +404,10 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
         }
       }
     }
-    wait_lgkm0();
-    wg_barrier();                                        // everybody is done with stage st
+    wait_lgkm0();                                        // reads of stage st done before the next barrier
     int f2 = 0;
     float s2 = 1.f;
     const int j2 = j1 >= 0 ? next_entry(f2, s2) : -1;
-    if (j2 >= 0) dma_tile(st, j2);
     j0 = j1; f0 = f1; s0 = s1;
     j1 = j2; f1 = f2; s1 = s2;
   }
