@@ -65,7 +65,7 @@ def load(path: Optional[str] = None):
         "sta_build_mask": (i32, [PS, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
         "mask_or": (i32, [vp, vp, i64, vp, i64, vp]),
         "csr_workspace_size": (sz, [i32, i32, i32]),
-        "bsa_mask_to_csr": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, sz, vp]),
+        "bsa_mask_to_csr": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "attn_workspace_size": (sz, [PS, i32]),
         "block_sparse_attn_fwd": (i32, [PT, PT, PT, PS, vp, i64, i64, vp, vp, dbl, PT, vp, vp, sz, vp]),
         "attn_csr_workspace_size": (sz, [PS, i32]),
@@ -179,9 +179,12 @@ def mask_or(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None
 
 def mask_to_csr(mask: torch.Tensor, B: Optional[int] = None, H: Optional[int] = None,
                 row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None,
-                ws: Optional[torch.Tensor] = None):
+                ws: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
+                return_order: bool = False):
     """Per-query-block kv lists of a [B,H,nb,nb] mask (or one [nb,nb] plane broadcast
-    over B, H) -> (row_ptr int32 [B*H*nb+1], col_idx int32 [B*H*nb*nb])."""
+    over B, H) -> (row_ptr int32 [B*H*nb+1], col_idx int32 [B*H*nb*nb]); with
+    return_order (or an `order` buffer) also the rows sorted by kept count,
+    descending, ties by row index (int32 [B*H*nb])."""
     lib = load()
     ptr, sb, sh, m = _mask_strides(mask)
     B = B or m.shape[0]
@@ -194,8 +197,13 @@ def mask_to_csr(mask: torch.Tensor, B: Optional[int] = None, H: Optional[int] = 
         col_idx = torch.empty(rows * nb, dtype=torch.int32, device=m.device)
     if ws is None:
         ws = _ws(lib.csr_workspace_size(B, H, nb), m.device)
-    _check(lib.bsa_mask_to_csr(ptr, sb, sh, B, H, nb, row_ptr.data_ptr(), col_idx.data_ptr(), ws.data_ptr(),
-                               ws.numel(), _stream(m.device)))
+    if return_order and order is None:
+        order = torch.empty(rows, dtype=torch.int32, device=m.device)
+    _check(lib.bsa_mask_to_csr(ptr, sb, sh, B, H, nb, row_ptr.data_ptr(), col_idx.data_ptr(),
+                               order.data_ptr() if order is not None else None, ws.data_ptr(), ws.numel(),
+                               _stream(m.device)))
+    if order is not None:
+        return row_ptr, col_idx, order
     return row_ptr, col_idx
 
 

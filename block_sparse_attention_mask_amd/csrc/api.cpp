@@ -31,6 +31,20 @@ bsa_status hip_status(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static thread_local int dev_cached = -1, cus_cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != dev_cached) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    dev_cached = dev;
+    cus_cached = cus;
+  }
+  return cus_cached;
+}
+
 size_t dtype_size(bsa_dtype t) { return t == BSA_F32 ? 4 : (t == BSA_BF16 ? 2 : 1); }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -66,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 1; }
+int bsa_abi_version(void) { return 2; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -165,7 +179,8 @@ bsa_status mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, 
 size_t csr_workspace_size(int B, int H, int nb) {
   if (B < 1 || H < 1 || nb < 1) return 0;
   const size_t rows = (size_t)B * H * nb;
-  return align256((rows + rows / 1024 + 1) * sizeof(int32_t));   // counts + segment sums
+  return align256((rows + rows / 1024 + 1) * sizeof(int32_t)) +   // counts + segment sums
+         align256(bsa::lpt_rows_ws_ints((int)rows, nb + 1) * sizeof(int32_t));   // order
 }
 
 static bsa_status check_mask_args(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H, int nb) {
@@ -178,15 +193,21 @@ static bsa_status check_mask_args(const uint8_t* mask, int64_t sb, int64_t sh, i
 }
 
 bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H, int nb,
-                           int32_t* row_ptr, int32_t* col_idx, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+                           int32_t* row_ptr, int32_t* col_idx, int32_t* order, void* ws, size_t ws_bytes,
+                           bsa_stream_t stream) {
   g_err.clear();
   bsa_status st;
   if ((st = check_mask_args(mask, mask_sb, mask_sh, B, H, nb)) != BSA_OK) return st;
   if (!row_ptr || !col_idx) return fail(BSA_EINVAL, "row_ptr / col_idx is NULL");
+  const int rows = B * H * nb;
+  if (order && bsa::lpt_rows_ws_ints(rows, nb + 1) == 0)
+    return fail(BSA_EUNSUPPORTED, "order: nb=%d too large for the count sort (at most 16382)", nb);
   const size_t need = csr_workspace_size(B, H, nb);
   if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
-  return hip_status(bsa::launch_csr(mask, mask_sb, mask_sh, B, H, nb, row_ptr, col_idx, (int32_t*)ws,
-                                    (hipStream_t)stream), "csr launch");
+  hipError_t e = bsa::launch_csr(mask, mask_sb, mask_sh, B, H, nb, row_ptr, col_idx, (int32_t*)ws, (hipStream_t)stream);
+  if (e != hipSuccess || !order) return hip_status(e, "csr launch");
+  int32_t* sort_ws = (int32_t*)((char*)ws + align256(((size_t)rows + rows / 1024 + 1) * sizeof(int32_t)));
+  return hip_status(bsa::launch_lpt_rows(row_ptr, rows, nb, sort_ws, order, (hipStream_t)stream), "order launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -194,9 +215,17 @@ static size_t split_bytes(const bsa_shape* s) {
   return align256((size_t)s->B * s->H * s->S * s->D * 2);
 }
 
+// work order of the attention kernel (keys, histograms, order)
+static size_t sched_bytes(const bsa_shape* s) {
+  const int nb = s->S / 64;
+  if (nb > bsa::PAIR_SCHED_MAX_NB) return 0;
+  const size_t npair = (size_t)s->B * s->H * ((nb + 1) / 2);
+  return align256(bsa::pair_sched_ws_ints(s->B * s->H, nb) * 4) + align256(npair * 4);
+}
+
 size_t attn_csr_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
-  if (!s || s->S <= 0 || s->D <= 0) return 0;
-  return qk_dtype == BSA_F32 ? 6 * split_bytes(s) : 0;   // hi/lo bf16 copies of f32 q, k, v
+  if (!s || s->S <= 0 || s->D <= 0 || s->B < 1 || s->H < 1) return 0;
+  return sched_bytes(s) + (qk_dtype == BSA_F32 ? 6 * split_bytes(s) : 0);   // + hi/lo bf16 copies of f32 q, k, v
 }
 
 size_t attn_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
@@ -208,7 +237,7 @@ size_t attn_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
 
 static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const bsa_shape* shape,
                               const int32_t* row_ptr, const int32_t* col_idx, const float* q_scale,
-                              const float* k_scale, double scale, const bsa_tensor* o, float* lse, void* split_ws,
+                              const float* k_scale, double scale, const bsa_tensor* o, float* lse, void* ws,
                               hipStream_t hs) {
   bsa::AttnArgs a = {};
   bsa::AttnMode mode;
@@ -225,6 +254,22 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   a.q_scale = q_scale; a.k_scale = k_scale;
   a.B = shape->B; a.H = shape->H; a.nb = shape->S / 64; a.S = shape->S; a.S_valid = shape->S_valid; a.D = shape->D;
   a.scale_log2 = (float)(scale * 1.4426950408889634);
+  const size_t sb_sched = sched_bytes(shape);
+  // The longest-first order pays off when the work items make only a few rounds over
+  // the workgroup slots (2 per compute unit), where the tail is a large part of the
+  // run. With many rounds the default order is better: it keeps the items of one head
+  // together on one XCD, sharing its L2.
+  const int nb_ = shape->S / 64;
+  const int64_t items = (int64_t)shape->B * shape->H * ((nb_ + 1) / 2);
+  if (sb_sched && items <= 4 * 2 * (int64_t)device_cus()) {
+    const int nb = shape->S / 64, BH = shape->B * shape->H;
+    int32_t* sws = (int32_t*)ws;
+    int32_t* order = (int32_t*)((char*)ws + align256(bsa::pair_sched_ws_ints(BH, nb) * 4));
+    hipError_t e = bsa::launch_pair_schedule(row_ptr, col_idx, BH, nb, sws, order, hs);
+    if (e != hipSuccess) return hip_status(e, "schedule launch");
+    a.pair_order = order;
+  }
+  void* split_ws = (char*)ws + sb_sched;
   if (mode == bsa::ATTN_SPLIT_F32) {
     const size_t sb = split_bytes(shape);
     uint16_t* p[6];
@@ -298,10 +343,9 @@ bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, c
   if ((st = check_attn(q, k, v, shape, q_scale, k_scale, o)) != BSA_OK) return st;
   if (!std::isfinite(scale)) return fail(BSA_EINVAL, "scale is not finite");
   if (!row_ptr || !col_idx) return fail(BSA_EINVAL, "row_ptr / col_idx is NULL");
-  if (q->dtype == BSA_F32) {
-    const size_t need = attn_csr_workspace_size(shape, q->dtype);
-    if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
-  }
+  const size_t need = attn_csr_workspace_size(shape, q->dtype);
+  if (need && (!ws || ws_bytes < need)) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
   return attn_common(q, k, v, shape, row_ptr, col_idx, q_scale, k_scale, scale, o, lse, ws, (hipStream_t)stream);
 }
 

@@ -184,14 +184,23 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   const int pr = wave >> 1, wv = wave & 1;        // block of the pair, query half
   const int l32 = l & 31, hi = l >> 5;
 
-  // Workgroups are dealt to the 8 XCDs round-robin; remap so that XCD x runs the
-  // contiguous range [x*chunk, (x+1)*chunk) of (head, pair) work items: neighbouring
-  // query blocks share most kv tiles, and then share one L2.
+  // Work item (head, pair) of this workgroup. With a work order (pairs by decreasing
+  // union size), workgroup x takes item order[x]: workgroups start in index order as
+  // slots free up, so the longest items go first and short ones fill the tail.
+  // Without one: workgroups are dealt to the 8 XCDs round-robin; remap so that XCD x
+  // runs the contiguous range [x*chunk, (x+1)*chunk) of items: neighbouring query
+  // blocks share most kv tiles, and then share one L2.
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
-  const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
-  const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
-  if (lin >= total) return;
+  int lin;
+  if (a.pair_order) {
+    if ((int)blockIdx.x >= total) return;
+    lin = a.pair_order[blockIdx.x];
+  } else {
+    const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
+    lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
+    if (lin >= total) return;
+  }
   const int bh = lin / npair, pidx = lin % npair;
   const int b = bh / a.H, h = bh % a.H;
   const int iA = 2 * pidx, iB = 2 * pidx + 1;

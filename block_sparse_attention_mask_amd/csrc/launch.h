@@ -32,6 +32,15 @@ hipError_t launch_mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8
                           hipStream_t st);
 hipError_t launch_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H, int nb,
                       int32_t* row_ptr, int32_t* col_idx, int32_t* counts_ws, hipStream_t st);
+// rows sorted by kept count (descending, ties by row index); workspace in int32s,
+// 0 when nb is too large for the sort
+size_t lpt_rows_ws_ints(int rows, int nk);
+hipError_t launch_lpt_rows(const int32_t* row_ptr, int rows, int nb, int32_t* ws, int32_t* order, hipStream_t st);
+// attention work order: query-block pairs by decreasing union size (nb <= PAIR_SCHED_MAX_NB)
+constexpr int PAIR_SCHED_MAX_NB = 4096;   // per-wave list copy in 64 KB of shared memory
+size_t pair_sched_ws_ints(int BH, int nb);
+hipError_t launch_pair_schedule(const int32_t* row_ptr, const int32_t* col_idx, int BH, int nb, int32_t* ws,
+                                int32_t* order, hipStream_t st);
 
 // attn.hip
 struct AttnArgs {
@@ -43,6 +52,7 @@ struct AttnArgs {
   void* o; int64_t o_sb, o_sh, o_ss;
   float* lse;
   const int32_t* row_ptr; const int32_t* col_idx;
+  const int32_t* pair_order;   // work order of the (head, query-block pair) items, or NULL
   const float* q_scale; const float* k_scale;
   int B, H, nb, S, S_valid, D;
   float scale_log2;      // softmax scale * log2(e)

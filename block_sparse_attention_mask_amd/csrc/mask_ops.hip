@@ -135,4 +135,222 @@ hipError_t launch_csr(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Longest-first orders (a work list sorted by decreasing cost, so that the longest
+// items start first and the short ones fill the tail).
+
+// Descending exclusive scan of n counters by one block of 1024 threads:
+// out[c] = sum of cnt[c'] over c' > c. Thread t handles a contiguous chunk.
+__device__ void desc_excl_scan_block(const int32_t* cnt, int n, int32_t* out, int* sh) {
+  const int per = (n + 1023) / 1024;
+  const int c1 = n - 1 - threadIdx.x * per;          // chunk: c1, c1-1, ..., c1-per+1 (descending)
+  int part = 0;
+  for (int e = 0; e < per; ++e) {
+    const int c = c1 - e;
+    if (c >= 0) part += cnt[c];
+  }
+  int total;
+  int run = block_excl_scan_1024(part, sh, total);
+  for (int e = 0; e < per; ++e) {
+    const int c = c1 - e;
+    if (c >= 0) { out[c] = run; run += cnt[c]; }
+  }
+}
+
+// Rows (b,h,i) sorted by kept count, descending, ties by ascending row index: a
+// stable counting sort over blocks of LPT_W waves (64 rows each).
+//   lpt_hist_kernel    per-block count histograms hist[blk][c]
+//   lpt_scan_kernel    per count c, exclusive scan over the blocks (in place), and
+//                      gstart[c] = number of rows with a larger count
+//   lpt_scatter_kernel rank inside a block: equal counts of one wave ranked by lane,
+//                      earlier waves of the block before later ones
+__global__ __launch_bounds__(1024) void lpt_hist_kernel(const int32_t* __restrict__ row_ptr, int rows, int nk,
+                                                        int per_blk, int32_t* __restrict__ hist) {
+  extern __shared__ int h[];
+  for (int c = threadIdx.x; c < nk; c += blockDim.x) h[c] = 0;
+  __syncthreads();
+  const int r = blockIdx.x * per_blk + threadIdx.x;
+  if (threadIdx.x < per_blk && r < rows) atomicAdd(&h[row_ptr[r + 1] - row_ptr[r]], 1);
+  __syncthreads();
+  int32_t* out = hist + (int64_t)blockIdx.x * nk;
+  for (int c = threadIdx.x; c < nk; c += blockDim.x) out[c] = h[c];
+}
+
+__global__ __launch_bounds__(1024) void lpt_scan_kernel(int32_t* __restrict__ hist, int nblk, int nk,
+                                                        int32_t* __restrict__ tot, int32_t* __restrict__ gstart) {
+  __shared__ int sh[32];
+  for (int c = threadIdx.x; c < nk; c += 1024) {
+    int run = 0;
+    int b = 0;
+    for (; b + 4 <= nblk; b += 4) {
+      const int t0 = hist[(int64_t)b * nk + c], t1 = hist[(int64_t)(b + 1) * nk + c];
+      const int t2 = hist[(int64_t)(b + 2) * nk + c], t3 = hist[(int64_t)(b + 3) * nk + c];
+      hist[(int64_t)b * nk + c] = run;
+      hist[(int64_t)(b + 1) * nk + c] = run + t0;
+      hist[(int64_t)(b + 2) * nk + c] = run + t0 + t1;
+      hist[(int64_t)(b + 3) * nk + c] = run + t0 + t1 + t2;
+      run += t0 + t1 + t2 + t3;
+    }
+    for (; b < nblk; ++b) {
+      const int t = hist[(int64_t)b * nk + c];
+      hist[(int64_t)b * nk + c] = run;
+      run += t;
+    }
+    tot[c] = run;
+  }
+  __threadfence_block();
+  __syncthreads();
+  desc_excl_scan_block(tot, nk, gstart, sh);
+}
+
+__global__ __launch_bounds__(1024) void lpt_scatter_kernel(const int32_t* __restrict__ row_ptr, int rows, int nk,
+                                                           const int32_t* __restrict__ hist,
+                                                           const int32_t* __restrict__ gstart,
+                                                           int32_t* __restrict__ order) {
+  extern __shared__ int cnt[];                       // [waves][nk]
+  const int nw = blockDim.x >> 6;
+  for (int x = threadIdx.x; x < nw * nk; x += blockDim.x) cnt[x] = 0;
+  __syncthreads();
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  const int c = r < rows ? row_ptr[r + 1] - row_ptr[r] : -1;
+  // rank among the lanes of this wave with the same count and a lower lane
+  int rank = 0;
+  uint64_t todo = __ballot(c >= 0);
+  while (todo) {
+    const int lc = __shfl(c, __ffsll((unsigned long long)todo) - 1, 64);
+    const uint64_t m = __ballot(c == lc);
+    if (c == lc) rank = __popcll(m & ((1ull << l) - 1ull));
+    if (l == 0) cnt[w * nk + lc] = __popcll(m);
+    todo &= ~m;
+  }
+  __syncthreads();
+  if (c >= 0) {
+    int before = 0;
+    for (int w2 = 0; w2 < w; ++w2) before += cnt[w2 * nk + c];
+    order[gstart[c] + hist[(int64_t)blockIdx.x * nk + c] + before + rank] = r;
+  }
+}
+
+int lpt_rows_block(int nk) {
+  // waves per block: the per-wave count table has to fit in 64 KB of shared memory
+  int w = (64 * 1024) / (nk * 4);
+  return w > 16 ? 16 : w;
+}
+
+size_t lpt_rows_ws_ints(int rows, int nk) {
+  const int w = lpt_rows_block(nk);
+  if (w < 1) return 0;
+  const int nblk = (rows + 64 * w - 1) / (64 * w);
+  return (size_t)nblk * nk + 2 * (size_t)nk;
+}
+
+hipError_t launch_lpt_rows(const int32_t* row_ptr, int rows, int nb, int32_t* ws, int32_t* order, hipStream_t st) {
+  const int nk = nb + 1;
+  const int w = lpt_rows_block(nk);
+  if (w < 1) return hipErrorInvalidValue;
+  const int per_blk = 64 * w;
+  const int nblk = (rows + per_blk - 1) / per_blk;
+  int32_t* hist = ws;
+  int32_t* tot = ws + (size_t)nblk * nk;
+  int32_t* gstart = tot + nk;
+  hipLaunchKernelGGL(lpt_hist_kernel, dim3(nblk), dim3(per_blk), nk * 4, st, row_ptr, rows, nk, per_blk, hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lpt_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nblk, nk, tot, gstart);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lpt_scatter_kernel, dim3(nblk), dim3(per_blk), w * nk * 4, st, row_ptr, rows, nk,
+                     (const int32_t*)hist, (const int32_t*)gstart, order);
+  return hipGetLastError();
+}
+
+// Work order of the attention kernel, whose work item is a pair of adjacent query
+// blocks (2p, 2p+1) walking the union of their kv lists: pairs by decreasing union
+// size. Ties are left in arbitrary order (the output does not depend on the order).
+//   pair_key_kernel      one wave per pair: |A u B| = |A| + |B| - |A n B|, each entry of
+//                        A looked up in B (staged in shared memory) by binary search;
+//                        histogram of the sizes
+//   pair_scatter_kernel  slot = (number of pairs with a larger size) + arrival rank
+constexpr int PAIR_WAVES = 4;
+__global__ __launch_bounds__(256) void sched_zero_kernel(int32_t* __restrict__ p, int n) {
+  for (int x = blockIdx.x * 256 + threadIdx.x; x < n; x += gridDim.x * 256) p[x] = 0;
+}
+
+__global__ __launch_bounds__(256) void pair_key_kernel(const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ col_idx, int BH, int nb,
+                                                       int32_t* __restrict__ keys, int32_t* __restrict__ hist) {
+  extern __shared__ int lb[];                        // [PAIR_WAVES][nb]: list of block 2p+1
+  const int npair = (nb + 1) / 2;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int p = blockIdx.x * PAIR_WAVES + w;
+  if (p >= BH * npair) return;
+  const int bh = p / npair, i = 2 * (p % npair);
+  const int rA = bh * nb + i;
+  const int sA = row_ptr[rA], eA = row_ptr[rA + 1];
+  int key = eA - sA;
+  if (i + 1 < nb) {
+    const int sB = eA, eB = row_ptr[rA + 2];
+    const int nB = eB - sB;
+    int* B = lb + w * nb;
+    for (int x = l; x < nB; x += 64) B[x] = col_idx[sB + x];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int inter = 0;
+    for (int x = sA + l; x < eA; x += 64) {
+      const int v = col_idx[x];
+      int lo = 0, hi = nB;                           // first position with B[pos] >= v
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (B[mid] < v) lo = mid + 1; else hi = mid;
+      }
+      inter += lo < nB && B[lo] == v;
+    }
+    key += nB - wave_sum_i32(inter);
+  }
+  if (l == 0) {
+    keys[p] = key;
+    atomicAdd(&hist[key], 1);
+  }
+}
+
+__global__ __launch_bounds__(1024) void pair_scatter_kernel(const int32_t* __restrict__ keys, int n, int nk,
+                                                            const int32_t* __restrict__ hist,
+                                                            int32_t* __restrict__ cursor,
+                                                            int32_t* __restrict__ order) {
+  extern __shared__ int gs[];                        // [nk]
+  __shared__ int sh[32];
+  desc_excl_scan_block(hist, nk, gs, sh);
+  __syncthreads();
+  const int p = blockIdx.x * 1024 + threadIdx.x;
+  if (p < n) {
+    const int k = keys[p];
+    order[gs[k] + atomicAdd(&cursor[k], 1)] = p;
+  }
+}
+
+size_t pair_sched_ws_ints(int BH, int nb) {
+  const size_t npair = (size_t)BH * ((nb + 1) / 2);
+  return npair + 2 * (size_t)(nb + 1);
+}
+
+hipError_t launch_pair_schedule(const int32_t* row_ptr, const int32_t* col_idx, int BH, int nb, int32_t* ws,
+                                int32_t* order, hipStream_t st) {
+  const int npair = BH * ((nb + 1) / 2), nk = nb + 1;
+  int32_t* keys = ws;
+  int32_t* hist = ws + npair;
+  int32_t* cursor = hist + nk;
+  hipLaunchKernelGGL(sched_zero_kernel, dim3((2 * nk + 255) / 256), dim3(256), 0, st, hist, 2 * nk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_key_kernel, dim3((npair + PAIR_WAVES - 1) / PAIR_WAVES), dim3(64 * PAIR_WAVES),
+                     PAIR_WAVES * nb * 4, st, row_ptr, col_idx, BH, nb, keys, hist);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_scatter_kernel, dim3((npair + 1023) / 1024), dim3(1024), nk * 4, st,
+                     (const int32_t*)keys, npair, nk, (const int32_t*)hist, cursor, order);
+  return hipGetLastError();
+}
+
 }  // namespace bsa

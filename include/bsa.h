@@ -138,12 +138,15 @@ bsa_status mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, 
  *   row_ptr    int32 [B*H*nb + 1]; row r = (b*H + h)*nb + i
  *   col_idx    int32 [B*H*nb*nb] capacity; row r's kept kv blocks, ascending, are
  *              col_idx[row_ptr[r] .. row_ptr[r+1])
+ *   order      optional (NULL = none) int32 [B*H*nb]: the rows sorted by kept count,
+ *              largest first, equal counts by ascending row index (a longest-first
+ *              work list); nb at most 16382, else BSA_EUNSUPPORTED
  *   ws         at least csr_workspace_size(B, H, nb) bytes
  * ------------------------------------------------------------------------- */
 size_t csr_workspace_size(int B, int H, int nb);
 bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H,
-                           int nb, int32_t* row_ptr, int32_t* col_idx, void* ws, size_t ws_bytes,
-                           bsa_stream_t stream);
+                           int nb, int32_t* row_ptr, int32_t* col_idx, int32_t* order, void* ws,
+                           size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Block-sparse attention forward [FA: exact tiled attention with online softmax,
@@ -168,7 +171,13 @@ bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh
  * base pointers 16-byte aligned).
  * block_sparse_attn_fwd_csr takes kv lists already built by bsa_mask_to_csr (for
  * masks reused across calls) and needs attn_csr_workspace_size(shape, q->dtype)
- * bytes (zero for bf16 and fp8 inputs; ws may then be NULL).
+ * bytes, 256-byte aligned (the work order below and, for f32 inputs, the hi/lo
+ * bf16 copies; ws may be NULL only when that size is 0).
+ * Work order: one workgroup per pair of adjacent query blocks. When the pairs make
+ * at most four rounds over the device's workgroup slots (and nb <= 4096), both entry
+ * points first rank the pairs by the size of the union of their two kv lists and
+ * start the largest first, so that short pairs fill the tail; otherwise the pairs
+ * of a head run together on one XCD.
  * ------------------------------------------------------------------------- */
 size_t attn_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
 bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,

@@ -18,8 +18,8 @@ brute force, textbook identities or library routines (see those files).
 from .nabla import block_pool, reduced_map, row_softmax, cdf_select, nabla_mask, nabla_masks
 from .sta import sta_block_mask, sta_token_mask
 from .attention import block_sparse_attention
-from .csr import mask_or, mask_to_csr
+from .csr import mask_or, mask_to_csr, longest_first_order
 
 __all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask",
            "nabla_masks", "sta_block_mask", "sta_token_mask", "block_sparse_attention",
-           "mask_or", "mask_to_csr"]
+           "mask_or", "mask_to_csr", "longest_first_order"]

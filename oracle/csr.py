@@ -25,3 +25,13 @@ def mask_to_csr(mask):
         row_ptr.append(row_ptr[-1] + len(nz))
     col_idx = np.concatenate(cols) if cols else np.zeros(0, dtype=np.int64)
     return np.asarray(row_ptr, dtype=np.int64), col_idx.astype(np.int64)
+
+
+def longest_first_order(mask):
+    """mask bool [R, nb] -> int64 [R]: the rows by kept count, largest first, rows of
+    equal count in ascending index order (a longest-processing-time-first work list
+    for the per-row lists above)."""
+    counts = np.asarray(mask, dtype=bool).sum(axis=1)
+    rows = list(range(len(counts)))
+    rows.sort(key=lambda r: (-int(counts[r]), r))
+    return np.asarray(rows, dtype=np.int64)

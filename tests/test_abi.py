@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_abi_version() == 2
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
@@ -88,8 +88,8 @@ def test_sta_rejects_bad_geometry(lib):
 def test_mask_or_and_csr_reject(lib):
     assert lib.mask_or(4096, 4096, 10, 8192, 3, None) == 1
     assert lib.mask_or(None, 4096, 10, 8192, 10, None) == 1
-    assert lib.bsa_mask_to_csr(4096, -1, 0, 1, 1, 4, 8192, 8192, 8192, 1 << 20, None) == 1
-    assert lib.bsa_mask_to_csr(4096, 0, 0, 1, 1, 4, 8192, 8192, 8192, 0, None) == 3
+    assert lib.bsa_mask_to_csr(4096, -1, 0, 1, 1, 4, 8192, 8192, None, 8192, 1 << 20, None) == 1
+    assert lib.bsa_mask_to_csr(4096, 0, 0, 1, 1, 4, 8192, 8192, None, 8192, 0, None) == 3
 
 
 def test_attention_rejects(lib):

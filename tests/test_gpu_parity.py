@@ -128,10 +128,11 @@ def test_mask_or_and_csr(gpu_lib):
     assert np.array_equal(u.cpu().numpy().astype(bool), ref)
     z = torch.zeros_like(ta)
     z[0, 1] = 1
-    rp, ci = gpu_lib.mask_to_csr(ta)
+    rp, ci, order = gpu_lib.mask_to_csr(ta, return_order=True)
     rp_ref, ci_ref = oracle.mask_to_csr(a.reshape(-1, 37))
     assert np.array_equal(rp.cpu().numpy(), rp_ref)
     assert np.array_equal(ci.cpu().numpy()[:rp_ref[-1]], ci_ref)
+    assert np.array_equal(order.cpu().numpy(), oracle.longest_first_order(a.reshape(-1, 37)))
 
 
 # ----------------------------------------------------------------------------- attention
@@ -273,12 +274,39 @@ def test_csr_multi_segment(gpu_lib):
     m = rng.random((2, 9, 70, 70)) < 0.15
     m[1, 4, :10] = False
     t = torch.from_numpy(m.astype(np.uint8)).to(DEV)
-    rp, ci = gpu_lib.mask_to_csr(t)
+    rp, ci, order = gpu_lib.mask_to_csr(t, return_order=True)
     rp_ref, ci_ref = oracle.mask_to_csr(m.reshape(-1, 70))
     assert np.array_equal(rp.cpu().numpy(), rp_ref)
     assert np.array_equal(ci.cpu().numpy()[:rp_ref[-1]], ci_ref)
+    assert np.array_equal(order.cpu().numpy(), oracle.longest_first_order(m.reshape(-1, 70)))
     plane = torch.from_numpy(m[0, 0].astype(np.uint8)).to(DEV)
-    rp2, ci2 = gpu_lib.mask_to_csr(plane, B=2, H=9)
-    rp2_ref, ci2_ref = oracle.mask_to_csr(np.broadcast_to(m[0, 0], (18, 70, 70)).reshape(-1, 70))
+    rp2, ci2, order2 = gpu_lib.mask_to_csr(plane, B=2, H=9, return_order=True)
+    m2 = np.broadcast_to(m[0, 0], (18, 70, 70)).reshape(-1, 70)
+    rp2_ref, ci2_ref = oracle.mask_to_csr(m2)
     assert np.array_equal(rp2.cpu().numpy(), rp2_ref)
     assert np.array_equal(ci2.cpu().numpy()[:rp2_ref[-1]], ci2_ref)
+    assert np.array_equal(order2.cpu().numpy(), oracle.longest_first_order(m2))
+
+
+def test_longest_first_order_large(gpu_lib):
+    """Several sort blocks and many equal counts (rows of a 40-head, nb=1182 mask with
+    counts from a narrow band), and the largest nb the order supports in one head."""
+    rng = np.random.default_rng(5)
+    nb = 1182
+    counts = rng.integers(380, 420, size=(40, nb))
+    m = np.zeros((40, nb, nb), bool)
+    for hh in range(40):
+        for i in range(nb):
+            m[hh, i, rng.choice(nb, counts[hh, i], replace=False)] = True
+    t = torch.from_numpy(m.astype(np.uint8)).to(DEV).view(1, 40, nb, nb)
+    rp, ci, order = gpu_lib.mask_to_csr(t, return_order=True)
+    torch.cuda.synchronize()
+    ref = oracle.longest_first_order(m.reshape(-1, nb))
+    assert np.array_equal(order.cpu().numpy(), ref)
+    nb2 = 16382
+    plane = torch.zeros(nb2, nb2, dtype=torch.uint8, device=DEV)
+    plane[:, :7] = 1
+    plane[::3, 7:40] = 1
+    rp, ci, order = gpu_lib.mask_to_csr(plane, B=1, H=1, return_order=True)
+    ref = np.concatenate([np.arange(0, nb2, 3), np.setdiff1d(np.arange(nb2), np.arange(0, nb2, 3))])
+    assert np.array_equal(order.cpu().numpy(), ref)

@@ -111,3 +111,27 @@ def test_csr_round_trip():
         assert np.all(np.diff(cols) > 0)
         back[r, cols] = True
     assert np.array_equal(back, m)
+
+
+def test_longest_first_order_worked_example():
+    # row counts 2, 0, 3, 2, 3, 1 -> by count descending, equal counts by index:
+    # rows 2, 4 (3 kept), 0, 3 (2 kept), 5 (1 kept), 1 (0 kept); worked by hand
+    m = np.zeros((6, 4), bool)
+    m[0, [0, 3]] = True
+    m[2, [0, 1, 2]] = True
+    m[3, [1, 2]] = True
+    m[4, [1, 2, 3]] = True
+    m[5, [3]] = True
+    assert oracle.longest_first_order(m).tolist() == [2, 4, 0, 3, 5, 1]
+
+
+def test_longest_first_order_invariants():
+    rng = np.random.default_rng(3)
+    m = rng.random((300, 9)) < 0.4           # few distinct counts: many ties
+    order = oracle.longest_first_order(m)
+    counts = m.sum(1)
+    assert sorted(order.tolist()) == list(range(300))          # a permutation
+    c = counts[order]
+    assert np.all(np.diff(c) <= 0)                              # largest first
+    same = np.diff(c) == 0
+    assert np.all(np.diff(order)[same] > 0)                     # ties by index
