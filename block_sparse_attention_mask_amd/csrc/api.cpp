@@ -215,12 +215,11 @@ static size_t split_bytes(const bsa_shape* s) {
   return align256((size_t)s->B * s->H * s->S * s->D * 2);
 }
 
-// work order of the attention kernel (keys, histograms, order)
+// work order of the attention kernel
 static size_t sched_bytes(const bsa_shape* s) {
-  const int nb = s->S / 64;
-  if (nb > bsa::PAIR_SCHED_MAX_NB) return 0;
-  const size_t npair = (size_t)s->B * s->H * ((nb + 1) / 2);
-  return align256(bsa::pair_sched_ws_ints(s->B * s->H, nb) * 4) + align256(npair * 4);
+  const int nb = s->S / 64, BH = s->B * s->H;
+  if (!bsa::pair_schedule_fits(BH, nb)) return 0;
+  return align256((size_t)bsa::pair_schedule_slots(BH, nb) * 4);
 }
 
 size_t attn_csr_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
@@ -257,17 +256,15 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   const size_t sb_sched = sched_bytes(shape);
   // The longest-first order pays off when the work items make only a few rounds over
   // the workgroup slots (2 per compute unit), where the tail is a large part of the
-  // run. With many rounds the default order is better: it keeps the items of one head
-  // together on one XCD, sharing its L2.
-  const int nb_ = shape->S / 64;
-  const int64_t items = (int64_t)shape->B * shape->H * ((nb_ + 1) / 2);
+  // run. With many rounds the default order does as well without the extra launch.
+  const int nb = shape->S / 64, BH = shape->B * shape->H;
+  const int64_t items = (int64_t)BH * ((nb + 1) / 2);
   if (sb_sched && items <= 4 * 2 * (int64_t)device_cus()) {
-    const int nb = shape->S / 64, BH = shape->B * shape->H;
-    int32_t* sws = (int32_t*)ws;
-    int32_t* order = (int32_t*)((char*)ws + align256(bsa::pair_sched_ws_ints(BH, nb) * 4));
-    hipError_t e = bsa::launch_pair_schedule(row_ptr, col_idx, BH, nb, sws, order, hs);
+    int32_t* order = (int32_t*)ws;
+    hipError_t e = bsa::launch_pair_schedule(row_ptr, BH, nb, order, hs);
     if (e != hipSuccess) return hip_status(e, "schedule launch");
     a.pair_order = order;
+    a.n_slots = bsa::pair_schedule_slots(BH, nb);
   }
   void* split_ws = (char*)ws + sb_sched;
   if (mode == bsa::ATTN_SPLIT_F32) {

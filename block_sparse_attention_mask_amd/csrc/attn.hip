@@ -184,18 +184,19 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   const int pr = wave >> 1, wv = wave & 1;        // block of the pair, query half
   const int l32 = l & 31, hi = l >> 5;
 
-  // Work item (head, pair) of this workgroup. With a work order (pairs by decreasing
-  // union size), workgroup x takes item order[x]: workgroups start in index order as
-  // slots free up, so the longest items go first and short ones fill the tail.
-  // Without one: workgroups are dealt to the 8 XCDs round-robin; remap so that XCD x
-  // runs the contiguous range [x*chunk, (x+1)*chunk) of items: neighbouring query
-  // blocks share most kv tiles, and then share one L2.
+  // Work item (head, pair) of this workgroup. Workgroups are dealt to the 8 XCDs
+  // round-robin; XCD x runs a contiguous range of items: neighbouring query blocks
+  // share most kv tiles, and then share one L2. With a work order, workgroup x takes
+  // item order[x] (or none, -1): the order puts each range longest first, and
+  // workgroups start in index order as slots free up, so short items fill the tail.
+  // Without one: the range of XCD x is [x*chunk, (x+1)*chunk) in natural order.
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
   int lin;
   if (a.pair_order) {
-    if ((int)blockIdx.x >= total) return;
+    if ((int)blockIdx.x >= a.n_slots) return;
     lin = a.pair_order[blockIdx.x];
+    if (lin < 0) return;
   } else {
     const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
     lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
@@ -477,7 +478,7 @@ hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, 
 template <int MODE, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * ((a.nb + 1) / 2);
-  dim3 grid(((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
+  dim3 grid(a.pair_order ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
   hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
                      a.k_scale);
   return hipGetLastError();

@@ -36,11 +36,13 @@ hipError_t launch_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int
 // 0 when nb is too large for the sort
 size_t lpt_rows_ws_ints(int rows, int nk);
 hipError_t launch_lpt_rows(const int32_t* row_ptr, int rows, int nb, int32_t* ws, int32_t* order, hipStream_t st);
-// attention work order: query-block pairs by decreasing union size (nb <= PAIR_SCHED_MAX_NB)
-constexpr int PAIR_SCHED_MAX_NB = 4096;   // per-wave list copy in 64 KB of shared memory
-size_t pair_sched_ws_ints(int BH, int nb);
-hipError_t launch_pair_schedule(const int32_t* row_ptr, const int32_t* col_idx, int BH, int nb, int32_t* ws,
-                                int32_t* order, hipStream_t st);
+// attention work order: per-XCD ranges of query-block pairs, longest first; fits for
+// few items and small nb (one workgroup sorts them in shared memory)
+constexpr int PAIR_SCHED_MAX_NB = 512;    // two [8][nb+1] int tables in 64 KB of shared memory
+constexpr int PAIR_SCHED_MAX_ITEMS = 8192;
+bool pair_schedule_fits(int BH, int nb);
+int pair_schedule_slots(int BH, int nb);   // entries of the order = workgroups to launch
+hipError_t launch_pair_schedule(const int32_t* row_ptr, int BH, int nb, int32_t* order, hipStream_t st);
 
 // attn.hip
 struct AttnArgs {
@@ -52,7 +54,8 @@ struct AttnArgs {
   void* o; int64_t o_sb, o_sh, o_ss;
   float* lse;
   const int32_t* row_ptr; const int32_t* col_idx;
-  const int32_t* pair_order;   // work order of the (head, query-block pair) items, or NULL
+  const int32_t* pair_order;   // work order of the (head, query-block pair) items, or NULL;
+  int n_slots;                 // its length (entries -1: no item)
   const float* q_scale; const float* k_scale;
   int B, H, nb, S, S_valid, D;
   float scale_log2;      // softmax scale * log2(e)

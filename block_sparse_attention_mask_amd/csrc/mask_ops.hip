@@ -266,90 +266,91 @@ hipError_t launch_lpt_rows(const int32_t* row_ptr, int rows, int nb, int32_t* ws
 }
 
 // Work order of the attention kernel, whose work item is a pair of adjacent query
-// blocks (2p, 2p+1) walking the union of their kv lists: pairs by decreasing union
-// size. Ties are left in arbitrary order (the output does not depend on the order).
-//   pair_key_kernel      one wave per pair: |A u B| = |A| + |B| - |A n B|, each entry of
-//                        A looked up in B (staged in shared memory) by binary search;
-//                        histogram of the sizes
-//   pair_scatter_kernel  slot = (number of pairs with a larger size) + arrival rank
-constexpr int PAIR_WAVES = 4;
-__global__ __launch_bounds__(256) void sched_zero_kernel(int32_t* __restrict__ p, int n) {
-  for (int x = blockIdx.x * 256 + threadIdx.x; x < n; x += gridDim.x * 256) p[x] = 0;
-}
-
-__global__ __launch_bounds__(256) void pair_key_kernel(const int32_t* __restrict__ row_ptr,
-                                                       const int32_t* __restrict__ col_idx, int BH, int nb,
-                                                       int32_t* __restrict__ keys, int32_t* __restrict__ hist) {
-  extern __shared__ int lb[];                        // [PAIR_WAVES][nb]: list of block 2p+1
-  const int npair = (nb + 1) / 2;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int p = blockIdx.x * PAIR_WAVES + w;
-  if (p >= BH * npair) return;
-  const int bh = p / npair, i = 2 * (p % npair);
-  const int rA = bh * nb + i;
-  const int sA = row_ptr[rA], eA = row_ptr[rA + 1];
-  int key = eA - sA;
-  if (i + 1 < nb) {
-    const int sB = eA, eB = row_ptr[rA + 2];
-    const int nB = eB - sB;
-    int* B = lb + w * nb;
-    for (int x = l; x < nB; x += 64) B[x] = col_idx[sB + x];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    int inter = 0;
-    for (int x = sA + l; x < eA; x += 64) {
-      const int v = col_idx[x];
-      int lo = 0, hi = nB;                           // first position with B[pos] >= v
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (B[mid] < v) lo = mid + 1; else hi = mid;
-      }
-      inter += lo < nB && B[lo] == v;
-    }
-    key += nB - wave_sum_i32(inter);
-  }
-  if (l == 0) {
-    keys[p] = key;
-    atomicAdd(&hist[key], 1);
-  }
-}
-
-__global__ __launch_bounds__(1024) void pair_scatter_kernel(const int32_t* __restrict__ keys, int n, int nk,
-                                                            const int32_t* __restrict__ hist,
-                                                            int32_t* __restrict__ cursor,
-                                                            int32_t* __restrict__ order) {
-  extern __shared__ int gs[];                        // [nk]
-  __shared__ int sh[32];
-  desc_excl_scan_block(hist, nk, gs, sh);
+// blocks (2p, 2p+1) walking the union of their kv lists. The items are cut into 8
+// contiguous ranges, one per XCD (workgroups are dealt to the XCDs round-robin, so
+// workgroup x runs on XCD x % 8): neighbouring query blocks keep sharing one L2. Inside
+// a range the items go longest first, by max(|list 2p|, |list 2p+1|); equal keys in
+// arbitrary order (the output does not depend on the order). Slot x of the order holds
+// the item of position x / 8 in range x % 8, or -1.
+// One workgroup of 1024 threads does it all in shared memory: per-range key
+// histograms, a descending scan per range, and a scatter with shared-memory atomics.
+constexpr int SCHED_RANGES = 8;
+__global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __restrict__ row_ptr, int BH, int nb,
+                                                             int32_t* __restrict__ order) {
+  extern __shared__ int sm[];
+  const int nk = nb + 1, npair = (nb + 1) / 2, items = BH * npair;
+  const int maxg = (items + SCHED_RANGES - 1) / SCHED_RANGES;
+  int* hist = sm;                                    // [ranges][nk]
+  int* cur = sm + SCHED_RANGES * nk;                 // [ranges][nk]: descending starts, then cursors
+  __shared__ int part[SCHED_RANGES][129];
+  __shared__ int gsize[SCHED_RANGES];
+  const int t = threadIdx.x;
+  for (int x = t; x < 2 * SCHED_RANGES * nk; x += 1024) sm[x] = 0;
   __syncthreads();
-  const int p = blockIdx.x * 1024 + threadIdx.x;
-  if (p < n) {
-    const int k = keys[p];
-    order[gs[k] + atomicAdd(&cursor[k], 1)] = p;
+  constexpr int PER = PAIR_SCHED_MAX_ITEMS / 1024;
+  int key[PER], grp[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int it = t + r * 1024;
+    key[r] = -1;
+    if (it < items) {
+      const int bh = it / npair, i = 2 * (it % npair);
+      const int rA = bh * nb + i;
+      const int cA = row_ptr[rA + 1] - row_ptr[rA];
+      const int cB = i + 1 < nb ? row_ptr[rA + 2] - row_ptr[rA + 1] : 0;
+      key[r] = max(cA, cB);
+      grp[r] = (int)(((int64_t)it * SCHED_RANGES) / items);
+      atomicAdd(&hist[grp[r] * nk + key[r]], 1);
+    }
   }
+  __syncthreads();
+  // descending exclusive scan of each range's histogram: 128 threads per range, each
+  // summing a chunk of keys (largest keys first), then a scan of the 128 chunk sums
+  {
+    const int g = t >> 7, c = t & 127;
+    const int per = (nk + 127) / 128;
+    const int k1 = nk - 1 - c * per;                 // chunk: k1, k1-1, ..., k1-per+1
+    int sum = 0;
+    for (int e = 0; e < per; ++e)
+      if (k1 - e >= 0) sum += hist[g * nk + k1 - e];
+    part[g][c] = sum;
+    __syncthreads();
+    if (c == 0) {
+      int run = 0;
+      for (int x = 0; x < 128; ++x) { const int v = part[g][x]; part[g][x] = run; run += v; }
+      gsize[g] = run;
+    }
+    __syncthreads();
+    int run = part[g][c];
+    for (int e = 0; e < per; ++e)
+      if (k1 - e >= 0) { cur[g * nk + k1 - e] = run; run += hist[g * nk + k1 - e]; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    if (key[r] >= 0) {
+      const int pos = atomicAdd(&cur[grp[r] * nk + key[r]], 1);
+      order[pos * SCHED_RANGES + grp[r]] = t + r * 1024;
+    }
+  }
+  // slots past the end of a range
+  for (int x = t; x < maxg * SCHED_RANGES; x += 1024)
+    if (x / SCHED_RANGES >= gsize[x % SCHED_RANGES]) order[x] = -1;
 }
 
-size_t pair_sched_ws_ints(int BH, int nb) {
-  const size_t npair = (size_t)BH * ((nb + 1) / 2);
-  return npair + 2 * (size_t)(nb + 1);
+bool pair_schedule_fits(int BH, int nb) {
+  return (int64_t)BH * ((nb + 1) / 2) <= PAIR_SCHED_MAX_ITEMS && nb + 1 <= PAIR_SCHED_MAX_NB + 1;
 }
 
-hipError_t launch_pair_schedule(const int32_t* row_ptr, const int32_t* col_idx, int BH, int nb, int32_t* ws,
-                                int32_t* order, hipStream_t st) {
-  const int npair = BH * ((nb + 1) / 2), nk = nb + 1;
-  int32_t* keys = ws;
-  int32_t* hist = ws + npair;
-  int32_t* cursor = hist + nk;
-  hipLaunchKernelGGL(sched_zero_kernel, dim3((2 * nk + 255) / 256), dim3(256), 0, st, hist, 2 * nk);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pair_key_kernel, dim3((npair + PAIR_WAVES - 1) / PAIR_WAVES), dim3(64 * PAIR_WAVES),
-                     PAIR_WAVES * nb * 4, st, row_ptr, col_idx, BH, nb, keys, hist);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pair_scatter_kernel, dim3((npair + 1023) / 1024), dim3(1024), nk * 4, st,
-                     (const int32_t*)keys, npair, nk, (const int32_t*)hist, cursor, order);
+int pair_schedule_slots(int BH, int nb) {
+  const int items = BH * ((nb + 1) / 2);
+  return ((items + SCHED_RANGES - 1) / SCHED_RANGES) * SCHED_RANGES;
+}
+
+hipError_t launch_pair_schedule(const int32_t* row_ptr, int BH, int nb, int32_t* order, hipStream_t st) {
+  const int nk = nb + 1;
+  hipLaunchKernelGGL(pair_schedule_kernel, dim3(1), dim3(1024), 2 * SCHED_RANGES * nk * 4, st, row_ptr, BH, nb,
+                     order);
   return hipGetLastError();
 }
 

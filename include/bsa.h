@@ -173,11 +173,11 @@ bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh
  * masks reused across calls) and needs attn_csr_workspace_size(shape, q->dtype)
  * bytes, 256-byte aligned (the work order below and, for f32 inputs, the hi/lo
  * bf16 copies; ws may be NULL only when that size is 0).
- * Work order: one workgroup per pair of adjacent query blocks. When the pairs make
- * at most four rounds over the device's workgroup slots (and nb <= 4096), both entry
- * points first rank the pairs by the size of the union of their two kv lists and
- * start the largest first, so that short pairs fill the tail; otherwise the pairs
- * of a head run together on one XCD.
+ * Work order: one workgroup per pair of adjacent query blocks; the pairs are cut
+ * into 8 contiguous ranges, one per XCD. When the pairs make at most four rounds over
+ * the device's workgroup slots (and nb <= 512), both entry points first sort each
+ * range by the longer of the pair's two kv lists and start the longest first, so
+ * that short pairs fill the tail.
  * ------------------------------------------------------------------------- */
 size_t attn_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
 bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
