@@ -72,6 +72,8 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     csr_ws = torch.empty(max(256, lib.csr_workspace_size(cfg.B, cfg.H, nb)), dtype=torch.uint8, device=dev)
     attn_ws = torch.empty(max(256, lib.attn_csr_workspace_size(ctypes.byref(shp), bsa._dtype_code(qa))),
                           dtype=torch.uint8, device=dev)
+    n_slots = lib.attn_work_order_slots(ctypes.byref(shp))
+    work_order = torch.empty(n_slots, dtype=torch.int32, device=dev) if n_slots > 0 else None
 
     def step(ev=None):
         if ev is not None:
@@ -89,10 +91,11 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
         if ev is not None:
             ev[1].record()
         rp, ci = bsa.mask_to_csr(m, B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
+        wo = bsa.attn_work_order(qa, rp, s_valid=cfg.S_valid, out=work_order) if work_order is not None else None
         if ev is not None:
             ev[2].record()
         bsa.block_sparse_attn_fwd_csr(qa, ka, v, rp, ci, s_valid=cfg.S_valid, q_scale=qs, k_scale=ks, out=out,
-                                      ws=attn_ws)
+                                      ws=attn_ws, work_order=wo)
         if ev is not None:
             ev[3].record()
         return m, rp
@@ -100,18 +103,24 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # timed region: whole steps back to back, events only at its two ends
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_all0.record()
     for s in range(steps):
-        m, rp = step(evs[s])
+        m, rp = step()
     t_all1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = t_all0.elapsed_time(t_all1)
+    # phase breakdown in a second pass of the same steps, with events between the phases
+    # (each event adds a few microseconds of its own, so it is kept out of the timed region)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
     mask_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     csr_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps

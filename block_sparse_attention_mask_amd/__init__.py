@@ -23,7 +23,8 @@ _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPA
 # every function the C header declares, in declaration order
 EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "sta_workspace_size", "sta_build_mask", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "attn_workspace_size", "block_sparse_attn_fwd",
-           "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "bsa_last_error", "bsa_abi_version"]
+           "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
+           "bsa_last_error", "bsa_abi_version"]
 
 
 class BsaError(RuntimeError):
@@ -69,7 +70,9 @@ def load(path: Optional[str] = None):
         "attn_workspace_size": (sz, [PS, i32]),
         "block_sparse_attn_fwd": (i32, [PT, PT, PT, PS, vp, i64, i64, vp, vp, dbl, PT, vp, vp, sz, vp]),
         "attn_csr_workspace_size": (sz, [PS, i32]),
-        "block_sparse_attn_fwd_csr": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
+        "block_sparse_attn_fwd_csr": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
+        "attn_work_order_slots": (i32, [PS]),
+        "attn_work_order": (i32, [PS, vp, vp, vp]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_abi_version": (i32, []),
     }
@@ -245,9 +248,27 @@ def block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
     return plan.out
 
 
+def attn_work_order(q: torch.Tensor, row_ptr: torch.Tensor, s_valid: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """Work order of the attention kernel for the kv lists row_ptr (int32 [slots], -1 =
+    no item), or None when the shape runs in the default order."""
+    lib = load()
+    shp = _shape(q, s_valid)
+    n = lib.attn_work_order_slots(ctypes.byref(shp))
+    if n < 0:
+        raise BsaError(lib.bsa_last_error().decode())
+    if n == 0:
+        return None
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=q.device)
+    _check(lib.attn_work_order(ctypes.byref(shp), row_ptr.data_ptr(), out.data_ptr(), _stream(q.device)))
+    return out
+
+
 def block_sparse_attn_fwd_csr(q, k, v, row_ptr, col_idx, scale=None, s_valid=None, q_scale=None, k_scale=None,
-                              return_lse=False, out=None, lse=None, ws=None):
-    """Attention over prebuilt kv lists (see mask_to_csr)."""
+                              return_lse=False, out=None, lse=None, ws=None, work_order=None):
+    """Attention over prebuilt kv lists (see mask_to_csr), optionally with a work order
+    from attn_work_order (computed internally when None)."""
     lib = load()
     shp = _shape(q, s_valid)
     code = _dtype_code(q)
@@ -261,7 +282,8 @@ def block_sparse_attn_fwd_csr(q, k, v, row_ptr, col_idx, scale=None, s_valid=Non
     tq, tk, tv, to = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     _check(lib.block_sparse_attn_fwd_csr(
         ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(shp), row_ptr.data_ptr(),
-        col_idx.data_ptr(), q_scale.data_ptr() if q_scale is not None else None,
+        col_idx.data_ptr(), work_order.data_ptr() if work_order is not None else None,
+        q_scale.data_ptr() if q_scale is not None else None,
         k_scale.data_ptr() if k_scale is not None else None, float(scale) if scale else 0.0, ctypes.byref(to),
         lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(), _stream(q.device)))
     return (out, lse) if return_lse else out

@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 2; }
+int bsa_abi_version(void) { return 3; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -215,12 +215,18 @@ static size_t split_bytes(const bsa_shape* s) {
   return align256((size_t)s->B * s->H * s->S * s->D * 2);
 }
 
-// work order of the attention kernel
-static size_t sched_bytes(const bsa_shape* s) {
+// Work order of the attention kernel. The longest-first order pays off when the work
+// items make only a few rounds over the workgroup slots (2 per compute unit), where
+// the tail is a large part of the run. With many rounds the default order does as well
+// without the extra launch.
+static int work_order_slots(const bsa_shape* s) {
   const int nb = s->S / 64, BH = s->B * s->H;
   if (!bsa::pair_schedule_fits(BH, nb)) return 0;
-  return align256((size_t)bsa::pair_schedule_slots(BH, nb) * 4);
+  const int64_t items = (int64_t)BH * ((nb + 1) / 2);
+  if (items > 4 * 2 * (int64_t)device_cus()) return 0;
+  return bsa::pair_schedule_slots(BH, nb);
 }
+static size_t sched_bytes(const bsa_shape* s) { return align256((size_t)work_order_slots(s) * 4); }
 
 size_t attn_csr_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
   if (!s || s->S <= 0 || s->D <= 0 || s->B < 1 || s->H < 1) return 0;
@@ -235,9 +241,9 @@ size_t attn_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
 }
 
 static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const bsa_shape* shape,
-                              const int32_t* row_ptr, const int32_t* col_idx, const float* q_scale,
-                              const float* k_scale, double scale, const bsa_tensor* o, float* lse, void* ws,
-                              hipStream_t hs) {
+                              const int32_t* row_ptr, const int32_t* col_idx, const int32_t* work_order,
+                              const float* q_scale, const float* k_scale, double scale, const bsa_tensor* o,
+                              float* lse, void* ws, hipStream_t hs) {
   bsa::AttnArgs a = {};
   bsa::AttnMode mode;
   if (q->dtype == BSA_BF16) mode = bsa::ATTN_BF16;
@@ -254,17 +260,15 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   a.B = shape->B; a.H = shape->H; a.nb = shape->S / 64; a.S = shape->S; a.S_valid = shape->S_valid; a.D = shape->D;
   a.scale_log2 = (float)(scale * 1.4426950408889634);
   const size_t sb_sched = sched_bytes(shape);
-  // The longest-first order pays off when the work items make only a few rounds over
-  // the workgroup slots (2 per compute unit), where the tail is a large part of the
-  // run. With many rounds the default order does as well without the extra launch.
-  const int nb = shape->S / 64, BH = shape->B * shape->H;
-  const int64_t items = (int64_t)BH * ((nb + 1) / 2);
-  if (sb_sched && items <= 4 * 2 * (int64_t)device_cus()) {
-    int32_t* order = (int32_t*)ws;
-    hipError_t e = bsa::launch_pair_schedule(row_ptr, BH, nb, order, hs);
-    if (e != hipSuccess) return hip_status(e, "schedule launch");
-    a.pair_order = order;
-    a.n_slots = bsa::pair_schedule_slots(BH, nb);
+  const int slots = work_order_slots(shape);
+  if (slots) {
+    if (!work_order) {
+      hipError_t e = bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, (int32_t*)ws, hs);
+      if (e != hipSuccess) return hip_status(e, "schedule launch");
+      work_order = (const int32_t*)ws;
+    }
+    a.pair_order = work_order;
+    a.n_slots = slots;
   }
   void* split_ws = (char*)ws + sb_sched;
   if (mode == bsa::ATTN_SPLIT_F32) {
@@ -328,13 +332,30 @@ bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = bsa::launch_csr(mask, mask_sb, mask_sh, shape->B, shape->H, nb, row_ptr, col_idx, counts, hs);
   if (e != hipSuccess) return hip_status(e, "csr launch");
-  return attn_common(q, k, v, shape, row_ptr, col_idx, q_scale, k_scale, scale, o, lse, w, hs);
+  return attn_common(q, k, v, shape, row_ptr, col_idx, nullptr, q_scale, k_scale, scale, o, lse, w, hs);
+}
+
+int attn_work_order_slots(const bsa_shape* shape) {
+  g_err.clear();
+  if (check_shape(shape, false) != BSA_OK) return -1;
+  return work_order_slots(shape);
+}
+
+bsa_status attn_work_order(const bsa_shape* shape, const int32_t* row_ptr, int32_t* order, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape, false)) != BSA_OK) return st;
+  if (!row_ptr || !order) return fail(BSA_EINVAL, "row_ptr / order is NULL");
+  if (!work_order_slots(shape)) return fail(BSA_EUNSUPPORTED, "this shape runs in the default order (0 slots)");
+  return hip_status(bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, order, (hipStream_t)stream),
+                    "work order launch");
 }
 
 bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
                                      const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
-                                     const float* q_scale, const float* k_scale, double scale, const bsa_tensor* o,
-                                     float* lse, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+                                     const int32_t* work_order, const float* q_scale, const float* k_scale,
+                                     double scale, const bsa_tensor* o, float* lse, void* ws, size_t ws_bytes,
+                                     bsa_stream_t stream) {
   g_err.clear();
   bsa_status st;
   if ((st = check_attn(q, k, v, shape, q_scale, k_scale, o)) != BSA_OK) return st;
@@ -343,7 +364,8 @@ bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, c
   const size_t need = attn_csr_workspace_size(shape, q->dtype);
   if (need && (!ws || ws_bytes < need)) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
-  return attn_common(q, k, v, shape, row_ptr, col_idx, q_scale, k_scale, scale, o, lse, ws, (hipStream_t)stream);
+  return attn_common(q, k, v, shape, row_ptr, col_idx, work_order, q_scale, k_scale, scale, o, lse, ws,
+                     (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -114,9 +114,101 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(const uint8_t* __restrict
   }
 }
 
+// Small masks (few rows, nb a multiple of 16, nb <= 512; contiguous [B,H,nb,nb] or
+// one [nb,nb] plane for every head) in one launch instead of four. Workgroup x owns rows [64x, 64x + 64). It counts the kept entries of all
+// earlier rows itself (16-byte chunks, a row is nb/16 chunks, 16 loads in flight per
+// thread, 1024 threads; the mask is small, so the repeated reads stay in L2), stages its own rows
+// in shared memory, counts them with wave ballots, scans the counts, and writes
+// row_ptr and the ascending kept indices.
+constexpr int CSR_SMALL_ROWS = 4096;
+constexpr int CSR_SMALL_NB = 512;
+constexpr int CSR_SMALL_RPW = 64;                     // rows per workgroup
+__global__ __launch_bounds__(1024) void csr_small_kernel(const uint8_t* __restrict__ mask, int64_t sb, int64_t sh,
+                                                        int H, int nb, int rows, int32_t* __restrict__ row_ptr,
+                                                        int32_t* __restrict__ col_idx) {
+  __shared__ __attribute__((aligned(16))) uint8_t own[CSR_SMALL_RPW * CSR_SMALL_NB];
+  __shared__ int rc[CSR_SMALL_RPW];
+  __shared__ int red[16];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int row0 = blockIdx.x * CSR_SMALL_RPW;
+  const int nown = min(CSR_SMALL_RPW, rows - row0);
+  const int cpr = nb / 16;
+  // 16-byte chunk c of the row-major [rows][nb] mask: contiguous, or one plane repeated
+  const int plane = nb * nb;
+  auto chunk = [&](int c) {
+    const int off = sb == 0 ? (c * 16) % plane : c * 16;
+    return *(const i32x4_t*)(mask + off);
+  };
+  auto nz16 = [](i32x4_t v) {                          // nonzero bytes of a chunk
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned x = (unsigned)v[e];
+      n += __popc((((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u);
+    }
+    return n;
+  };
+  // ---- stage the own rows
+  for (int c = t; c < nown * cpr; c += 1024) *(i32x4_t*)(own + c * 16) = chunk(row0 * cpr + c);
+  // ---- kept entries before row0
+  constexpr int NL = 16;
+  int part = 0;
+  const int nchunk = row0 * cpr;
+  for (int c0 = 0; c0 < nchunk; c0 += 1024 * NL) {
+    i32x4_t v[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int c = c0 + t + k * 1024;
+      v[k] = c < nchunk ? chunk(c) : i32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < NL; ++k) part += nz16(v[k]);
+  }
+  part = wave_sum_i32(part);
+  if (l == 0) red[w] = part;
+  __syncthreads();
+  // ---- own rows: counts by ballot (wave w takes rows w, w + 16, ...)
+  for (int r = w; r < nown; r += 16) {
+    int cnt = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) cnt += __popcll(__ballot(j0 + l < nb && own[r * nb + j0 + l] != 0));
+    if (l == 0) rc[r] = cnt;
+  }
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) base += red[x];
+  if (w == 0) {                                        // exclusive scan of the row counts
+    const int x = l < nown ? rc[l] : 0;
+    const int incl = wave_incl_scan_i32(x);
+    if (l < nown) row_ptr[row0 + l] = base + incl - x;
+    if (row0 + l == rows - 1) row_ptr[rows] = base + incl;
+    if (l < nown) rc[l] = base + incl - x;
+  }
+  __syncthreads();
+  for (int r = w; r < nown; r += 16) {
+    int32_t* out = col_idx + rc[r];
+    int pos = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+      const bool f = j0 + l < nb && own[r * nb + j0 + l] != 0;
+      const uint64_t ball = __ballot(f);
+      if (f) out[pos + __popcll(ball & ((1ull << l) - 1ull))] = j0 + l;
+      pos += __popcll(ball);
+    }
+  }
+}
+
 hipError_t launch_csr(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H, int nb, int32_t* row_ptr,
                       int32_t* col_idx, int32_t* counts, hipStream_t st) {
   const int rows = B * H * nb;
+  const bool dense = (H == 1 || sh == (int64_t)nb * nb) && (B == 1 || sb == (int64_t)H * nb * nb) && (sb || sh);
+  const bool plane = sb == 0 && sh == 0;
+  if (nb % 16 == 0 && ((uintptr_t)mask & 15) == 0 && (dense || plane) && rows <= CSR_SMALL_ROWS &&
+      nb <= CSR_SMALL_NB) {
+    if (dense) sb = 1;                                 // kernel: sb == 0 means one repeated plane
+    hipLaunchKernelGGL(csr_small_kernel, dim3((rows + CSR_SMALL_RPW - 1) / CSR_SMALL_RPW), dim3(1024), 0, st, mask, sb,
+                       sh, H, nb, rows, row_ptr, col_idx);
+    return hipGetLastError();
+  }
   const unsigned g = (unsigned)((rows + 3) / 4);
   hipLaunchKernelGGL(csr_count_kernel, dim3(g), dim3(256), 0, st, mask, sb, sh, H, nb, rows, counts);
   hipError_t e = hipGetLastError();
@@ -282,7 +374,7 @@ __global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __re
   const int maxg = (items + SCHED_RANGES - 1) / SCHED_RANGES;
   int* hist = sm;                                    // [ranges][nk]
   int* cur = sm + SCHED_RANGES * nk;                 // [ranges][nk]: descending starts, then cursors
-  __shared__ int part[SCHED_RANGES][129];
+  __shared__ int part[SCHED_RANGES][2];
   __shared__ int gsize[SCHED_RANGES];
   const int t = threadIdx.x;
   for (int x = t; x < 2 * SCHED_RANGES * nk; x += 1024) sm[x] = 0;
@@ -313,15 +405,13 @@ __global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __re
     int sum = 0;
     for (int e = 0; e < per; ++e)
       if (k1 - e >= 0) sum += hist[g * nk + k1 - e];
-    part[g][c] = sum;
+    // exclusive scan of the 128 chunk sums of the range: two waves, then the first
+    // wave's total added to the second
+    const int incl = wave_incl_scan_i32(sum);
+    if ((c & 63) == 63) part[g][c >> 6] = incl;
     __syncthreads();
-    if (c == 0) {
-      int run = 0;
-      for (int x = 0; x < 128; ++x) { const int v = part[g][x]; part[g][x] = run; run += v; }
-      gsize[g] = run;
-    }
-    __syncthreads();
-    int run = part[g][c];
+    int run = incl - sum + (c >= 64 ? part[g][0] : 0);
+    if (c == 127) gsize[g] = run + sum;
     for (int e = 0; e < per; ++e)
       if (k1 - e >= 0) { cur[g * nk + k1 - e] = run; run += hist[g * nk + k1 - e]; }
   }

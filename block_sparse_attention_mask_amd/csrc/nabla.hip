@@ -38,9 +38,12 @@ __device__ __forceinline__ int64_t mf_index(int bh, int nb, int D, int blk, int 
 
 // ----------------------------------------------------------------------------
 // Pooling: Qbar[bh][i][d] = (1/64) sum_r Q[bh][64 i + r][d], and Kbar likewise.
-// One workgroup per (block i, bh, tensor). Each thread loads 16 bytes per row.
+// One workgroup per two consecutive blocks of one (bh, tensor); each thread issues
+// all of its 16-byte loads (8 rows x 2 blocks) before converting any. NT: streaming
+// (non-temporal) loads, for inputs much larger than the last-level cache.
 // ----------------------------------------------------------------------------
-template <typename T, int D>
+constexpr int POOL_BPW = 2;   // blocks per workgroup
+template <typename T, int D, bool NT>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
                                                    int64_t q_ss, const T* __restrict__ k, int64_t k_sb,
                                                    int64_t k_sh, int64_t k_ss, int H, int nb,
@@ -49,47 +52,58 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
   constexpr int TPR = D / E;               // threads per row
   constexpr int RPP = 256 / TPR;           // rows per pass
   constexpr int PASSES = BSA_N / RPP;
-  __shared__ double part[RPP][D];
+  __shared__ double part[POOL_BPW][RPP][D];
 
-  const int i = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  const int i0 = blockIdx.x * POOL_BPW, bh = blockIdx.y, which = blockIdx.z;
   const int b = bh / H, h = bh % H;
-  const T* src = which == 0 ? q + b * q_sb + h * q_sh + (int64_t)i * BSA_N * q_ss
-                            : k + b * k_sb + h * k_sh + (int64_t)i * BSA_N * k_ss;
+  const T* base = which == 0 ? q + b * q_sb + h * q_sh : k + b * k_sb + h * k_sh;
   const int64_t ss = which == 0 ? q_ss : k_ss;
   const int t = threadIdx.x, cg = t % TPR, r0 = t / TPR;
 
-  double acc[E];
+  i32x4_t raw[POOL_BPW][PASSES];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.0;
-  // issue all loads first, then convert
-  i32x4_t raw[PASSES];
+  for (int bb = 0; bb < POOL_BPW; ++bb) {
+    const int i = min(i0 + bb, nb - 1);     // a missing last block re-reads block nb-1 (not stored)
+    const T* src = base + (int64_t)i * BSA_N * ss;
 #pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps)
-    raw[ps] = *(const i32x4_t*)(src + (int64_t)(r0 + ps * RPP) * ss + cg * E);
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) {
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        unsigned u = (unsigned)raw[ps][w];
-        acc[2 * w] += (double)__uint_as_float(u << 16);
-        acc[2 * w + 1] += (double)__uint_as_float(u & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc[w] += (double)__int_as_float(raw[ps][w]);
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const i32x4_t* ptr = (const i32x4_t*)(src + (int64_t)(r0 + ps * RPP) * ss + cg * E);
+      if constexpr (NT) raw[bb][ps] = __builtin_nontemporal_load(ptr);
+      else raw[bb][ps] = *ptr;
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) part[r0][cg * E + e] = acc[e];
+  for (int bb = 0; bb < POOL_BPW; ++bb) {
+    double acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          unsigned u = (unsigned)raw[bb][ps][w];
+          acc[2 * w] += (double)__uint_as_float(u << 16);
+          acc[2 * w + 1] += (double)__uint_as_float(u & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[w] += (double)__int_as_float(raw[bb][ps][w]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) part[bb][r0][cg * E + e] = acc[e];
+  }
   __syncthreads();
-  if (t < D) {
+  for (int x = t; x < POOL_BPW * D; x += 256) {
+    const int bb = x / D, d = x % D, i = i0 + bb;
+    if (i >= nb) continue;
     double s = 0.0;
 #pragma unroll
-    for (int r = 0; r < RPP; ++r) s += part[r][t];
+    for (int r = 0; r < RPP; ++r) s += part[bb][r][d];
     s *= (1.0 / BSA_N);
     double* dst = which == 0 ? qbar : kbarT;
-    dst[mf_index(bh, nb, D, i, t)] = s;
+    dst[mf_index(bh, nb, D, i, d)] = s;
   }
 }
 
@@ -407,9 +421,15 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
 template <typename T, int D>
 static hipError_t launch_pool_t(const void* q, const int64_t* qs, const void* k, const int64_t* ks, int B,
                                 int H, int nb, double* qbar, double* kbarT, hipStream_t st) {
-  dim3 grid(nb, B * H, 2);
-  hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1], qs[2],
-                     (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT);
+  dim3 grid((nb + POOL_BPW - 1) / POOL_BPW, B * H, 2);
+  // inputs far larger than the 256 MB last-level cache are streamed past it
+  const bool nt = 2.0 * B * H * nb * BSA_N * D * sizeof(T) > 512.0 * (1 << 20);
+  if (nt)
+    hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1], qs[2],
+                       (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT);
+  else
+    hipLaunchKernelGGL((pool_kernel<T, D, false>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1], qs[2],
+                       (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT);
   return hipGetLastError();
 }
 

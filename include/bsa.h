@@ -171,13 +171,19 @@ bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh
  * base pointers 16-byte aligned).
  * block_sparse_attn_fwd_csr takes kv lists already built by bsa_mask_to_csr (for
  * masks reused across calls) and needs attn_csr_workspace_size(shape, q->dtype)
- * bytes, 256-byte aligned (the work order below and, for f32 inputs, the hi/lo
- * bf16 copies; ws may be NULL only when that size is 0).
+ * bytes, 256-byte aligned (room for the work order below and, for f32 inputs, the
+ * hi/lo bf16 copies; ws may be NULL only when that size is 0).
+ *
  * Work order: one workgroup per pair of adjacent query blocks; the pairs are cut
  * into 8 contiguous ranges, one per XCD. When the pairs make at most four rounds over
- * the device's workgroup slots (and nb <= 512), both entry points first sort each
- * range by the longer of the pair's two kv lists and start the longest first, so
- * that short pairs fill the tail.
+ * the device's workgroup slots and nb <= 512, each range is sorted by the longer of
+ * the pair's two kv lists and started longest first, so that short pairs fill the
+ * tail. attn_work_order_slots(shape) gives the length of that order (0: the shape
+ * runs in the natural order; -1: invalid shape); attn_work_order writes it for the
+ * kv lists row_ptr into order (int32 [slots]; entry x is the pair index
+ * (b*H + h) * ceil(nb/2) + p started by workgroup x, or -1). Pass it as work_order to
+ * block_sparse_attn_fwd_csr to reuse it; with work_order NULL the entry points
+ * compute it themselves (in ws). The order never changes the results.
  * ------------------------------------------------------------------------- */
 size_t attn_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
 bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
@@ -191,9 +197,14 @@ size_t attn_csr_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
 bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
                                      const bsa_shape* shape,
                                      const int32_t* row_ptr, const int32_t* col_idx,
+                                     const int32_t* work_order,
                                      const float* q_scale, const float* k_scale, double scale,
                                      const bsa_tensor* o, float* lse,
                                      void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+int attn_work_order_slots(const bsa_shape* shape);
+bsa_status attn_work_order(const bsa_shape* shape, const int32_t* row_ptr, int32_t* order,
+                           bsa_stream_t stream);
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char* bsa_last_error(void);

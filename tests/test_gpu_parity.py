@@ -107,6 +107,9 @@ def test_sta_mask_parity(gpu_lib, cid):
     ((3, 5, 7), "row", None, (2, 2, 3), (3, 3, 3)),
     ((5, 6, 7), "tile", (2, 4, 4), (2, 4, 4), (1, 3, 5)),
     ((4, 9, 10), "tile", (3, 4, 4), (2, 3, 5), (3, 1, 3)),
+    # blocks aligned with the tiles (one and two blocks per tile): the single-kernel path
+    ((4, 16, 16), "tile", (2, 8, 4), (2, 8, 4), (1, 3, 5)),
+    ((6, 16, 24), "tile", (2, 8, 8), (2, 8, 8), (3, 3, 1)),
 ])
 def test_sta_ragged_geometries(gpu_lib, grid, order, otile, tile, window):
     Sv = int(np.prod(grid))
@@ -286,6 +289,62 @@ def test_csr_multi_segment(gpu_lib):
     assert np.array_equal(rp2.cpu().numpy(), rp2_ref)
     assert np.array_equal(ci2.cpu().numpy()[:rp2_ref[-1]], ci2_ref)
     assert np.array_equal(order2.cpu().numpy(), oracle.longest_first_order(m2))
+
+
+def test_csr_small_single_launch(gpu_lib):
+    """Masks small enough for the one-workgroup builder (nb a multiple of 16): empty and
+    full rows, nonzero values other than 1, a broadcast plane, and the largest size."""
+    rng = np.random.default_rng(33)
+    m = (rng.random((2, 3, 96, 96)) < 0.3).astype(np.uint8) * rng.integers(1, 255, (2, 3, 96, 96)).astype(np.uint8)
+    m[0, 2, 7] = 0
+    m[1, 0, 50] = 9
+    t = torch.from_numpy(m).to(DEV)
+    rp, ci = gpu_lib.mask_to_csr(t)
+    rp_ref, ci_ref = oracle.mask_to_csr(m.reshape(-1, 96) != 0)
+    assert np.array_equal(rp.cpu().numpy(), rp_ref)
+    assert np.array_equal(ci.cpu().numpy()[:rp_ref[-1]], ci_ref)
+    plane = torch.from_numpy(m[1, 1]).to(DEV)
+    rp2, ci2 = gpu_lib.mask_to_csr(plane, B=1, H=5)
+    m2 = np.broadcast_to(m[1, 1] != 0, (5, 96, 96)).reshape(-1, 96)
+    rp2_ref, ci2_ref = oracle.mask_to_csr(m2)
+    assert np.array_equal(rp2.cpu().numpy(), rp2_ref)
+    assert np.array_equal(ci2.cpu().numpy()[:rp2_ref[-1]], ci2_ref)
+    big = rng.random((1, 32, 128, 128)) < 0.4          # 4096 rows: the size limit
+    tb = torch.from_numpy(big.astype(np.uint8)).to(DEV)
+    rp3, ci3 = gpu_lib.mask_to_csr(tb)
+    rp3_ref, ci3_ref = oracle.mask_to_csr(big.reshape(-1, 128))
+    assert np.array_equal(rp3.cpu().numpy(), rp3_ref)
+    assert np.array_equal(ci3.cpu().numpy()[:rp3_ref[-1]], ci3_ref)
+
+
+def test_attention_work_order(gpu_lib):
+    """The attention work order: every pair exactly once, XCD range x % 8 of slot x a
+    contiguous run of pairs, each range by decreasing longer-list length; results
+    identical with the order passed in, computed inside, and through the dense entry."""
+    cfg = get_config(2)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    plane = _gpu_sta(gpu_lib, cfg)
+    mask = gpu_lib.nabla_build_mask(q, k, cfg.thrs[0], or_mask=plane)
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    order = gpu_lib.attn_work_order(q, rp)
+    assert order is not None
+    o = order.cpu().numpy()
+    counts = np.diff(rp.cpu().numpy())
+    npair = cfg.nb // 2
+    items = cfg.B * cfg.H * npair
+    assert sorted(o[o >= 0].tolist()) == list(range(items))
+    for x in range(8):
+        rng_items = o[x::8]
+        rng_items = rng_items[rng_items >= 0]
+        assert np.all(np.diff(np.sort(rng_items)) == 1)            # a contiguous run
+        bh, p = rng_items // npair, rng_items % npair
+        key = np.maximum(counts[bh * cfg.nb + 2 * p], counts[bh * cfg.nb + 2 * p + 1])
+        assert np.all(np.diff(key) <= 0)                            # longest first
+    a = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, work_order=order)
+    b = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci)
+    c = gpu_lib.block_sparse_attn_fwd(q, k, v, mask)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
 
 
 def test_longest_first_order_large(gpu_lib):
