@@ -216,14 +216,14 @@ static size_t split_bytes(const bsa_shape* s) {
 }
 
 // Work order of the attention kernel. The longest-first order pays off when the work
-// items make only a few rounds over the workgroup slots (2 per compute unit), where
+// items make only a few rounds over the workgroup slots (3 per compute unit), where
 // the tail is a large part of the run. With many rounds the default order does as well
 // without the extra launch.
 static int work_order_slots(const bsa_shape* s) {
   const int nb = s->S / 64, BH = s->B * s->H;
   if (!bsa::pair_schedule_fits(BH, nb)) return 0;
   const int64_t items = (int64_t)BH * ((nb + 1) / 2);
-  if (items > 4 * 2 * (int64_t)device_cus()) return 0;
+  if (items > 4 * 3 * (int64_t)device_cus()) return 0;
   return bsa::pair_schedule_slots(BH, nb);
 }
 static size_t sched_bytes(const bsa_shape* s) { return align256((size_t)work_order_slots(s) * 4); }

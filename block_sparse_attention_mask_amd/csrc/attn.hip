@@ -156,12 +156,15 @@ __device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lg
 // blocks share most of their kv blocks, so most tiles serve both). A block visits
 // exactly its own tiles, in the same ascending order as it would alone.
 //
-// K/V tiles are double-buffered with one barrier per step: a wave passes the barrier
-// that opens step u once its own part of tile u has landed, and only after finishing
-// step u-1, so right after it tile u+1 is copied into the buffer step u-1 read and has
-// all of step u's compute to land. Each wave issues a quarter of every tile copy.
+// Buffers: two K slots and one V slot (48 KB at D = 128 bf16), so that three
+// workgroups share a CU (168 VGPRs) and a third wave per SIMD hides latency. Step u:
+// each wave waits for its own part of K(u), then the barrier that opens the step (every
+// wave has finished step u-1, so the V slot and the other K slot are free); V(u) and
+// K(u+1) are copied next; S and the softmax of tile u run while V(u) lands; a second
+// barrier makes all parts of V(u) visible before PV. K(u+1) has a whole step to land.
+// Each wave issues a quarter of every tile copy.
 template <int MODE, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                      const float* __restrict__ q_scale, const float* __restrict__ k_scale) {
   constexpr int QK_ES = MODE == ATTN_FP8 ? 1 : 2;   // bytes per Q/K element
@@ -174,10 +177,11 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   constexpr int KS = MODE == ATTN_FP8 ? D / 64 : D / 16;   // k-steps of S = K Q^T
   using KOp = typename std::conditional<MODE == ATTN_FP8, i32x8_t, bf16x8_t>::type;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // two K slots, one V slot
+  __shared__ __attribute__((aligned(1024))) char smem[NSPLIT * (2 * KT_BYTES + VT_BYTES)];
   char BSA_LDS* lds = (char BSA_LDS*)smem;
-  auto k_lds = [&](int st, int x) { return lds + st * STAGE + x * KT_BYTES; };
-  auto v_lds = [&](int st, int x) { return lds + st * STAGE + NSPLIT * KT_BYTES + x * VT_BYTES; };
+  auto k_lds = [&](int st, int x) { return lds + (st * NSPLIT + x) * KT_BYTES; };
+  auto v_lds = [&](int st, int x) { (void)st; return lds + 2 * NSPLIT * KT_BYTES + x * VT_BYTES; };
 
   const int l = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -232,13 +236,17 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   const unsigned k_rs32 = (unsigned)k_rs, v_rs32 = (unsigned)v_rs;
 
   // this wave's quarter of the copy of kv tile jt into stage st
-  auto dma_tile = [&](int st, int jt) {
+  auto dma_k = [&](int st, int jt) {
 #pragma unroll
-    for (int x = 0; x < NSPLIT; ++x) {
+    for (int x = 0; x < NSPLIT; ++x)
       load_tile_part<RBK, false, 4>(kbase[x] + (int64_t)jt * 64 * k_rs, k_rs32, (unsigned)(uintptr_t)k_lds(st, x), l, wave);
-      load_tile_part<RBV, true, 4>(vbase[x] + (int64_t)jt * 64 * v_rs, v_rs32, (unsigned)(uintptr_t)v_lds(st, x), l, wave);
-    }
   };
+  auto dma_v = [&](int jt) {
+#pragma unroll
+    for (int x = 0; x < NSPLIT; ++x)
+      load_tile_part<RBV, true, 4>(vbase[x] + (int64_t)jt * 64 * v_rs, v_rs32, (unsigned)(uintptr_t)v_lds(0, x), l, wave);
+  };
+  constexpr int NK_W = NSPLIT * KT_BYTES / 1024 / 4;
 
   // ---- Q^T as the B operand: lane holds query 32 wv + l32 of block i
   KOp qop[NSPLIT][KS];
@@ -306,21 +314,23 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   float s0 = 1.f, s1 = 1.f;
   int j0 = next_entry(f0, s0);
   int j1 = j0 >= 0 ? next_entry(f1, s1) : -1;
-  if (j0 >= 0) dma_tile(0, j0);
+  if (j0 >= 0) dma_k(0, j0);
 
   for (int u = 0; j0 >= 0; ++u) {
     const int st = u & 1;
-    wait_vm<0>();                                        // own share of tile j0 landed
+    wait_vm<0>();                                        // own share of K(u) landed
     wg_barrier();                                        // everybody's share; step u-1 done everywhere
-    if (j1 >= 0) dma_tile(st ^ 1, j1);                   // into the buffer step u-1 used
+    dma_v(j0);                                           // V(u) into the V slot (read by step u-1)
+    if (j1 >= 0) dma_k(st ^ 1, j1);                      // K(u+1) into the K slot step u-1 used
 
     const int kv0 = j0 * 64;
     const bool use = ((f0 >> pr) & 1) && kv0 < a.S_valid;
+    f32x16_t sacc[2];
+    bf16x8_t pop[4];
     if (use) {
       char BSA_LDS* kt0 = k_lds(st, 0);
       // ---- S^T = K Q^T for this wave's 32 queries: sacc[kt], kv = kt*32 + 8(v/4) + 4 hi + v%4
       const f32x16_t zero16 = {};
-      f32x16_t sacc[2];
       KOp kk[2][KS];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -382,7 +392,6 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
       }
       const float mr = m_run;
       float ls = 0.f;
-      bf16x8_t pop[4];
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         i32x4_t w;
@@ -397,6 +406,10 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
         pop[sp] = __builtin_bit_cast(bf16x8_t, w);
       }
       l_run += ls;
+    }
+    if (j1 >= 0) wait_vm<NK_W>(); else wait_vm<0>();    // own share of V(u) landed
+    wg_barrier();                                        // everybody's share
+    if (use) {
       // ---- O^T += V^T P^T, V^T read from the row-major V tile with transposing reads
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
@@ -414,7 +427,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
         }
       }
     }
-    wait_lgkm0();                                        // reads of stage st done before the next barrier
+    wait_lgkm0();                                        // reads of this step's slots done before the next barrier
     int f2 = 0;
     float s2 = 1.f;
     const int j2 = j1 >= 0 ? next_entry(f2, s2) : -1;

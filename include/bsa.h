@@ -176,7 +176,7 @@ bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh
  *
  * Work order: one workgroup per pair of adjacent query blocks; the pairs are cut
  * into 8 contiguous ranges, one per XCD. When the pairs make at most four rounds over
- * the device's workgroup slots and nb <= 512, each range is sorted by the longer of
+ * the device's workgroup slots (3 per compute unit) and nb <= 512, each range is sorted by the longer of
  * the pair's two kv lists and started longest first, so that short pairs fill the
  * tail. attn_work_order_slots(shape) gives the length of that order (0: the shape
  * runs in the natural order; -1: invalid shape); attn_work_order writes it for the
