@@ -10,6 +10,7 @@ is for the dominant kernel (the attention kernel), timed with HIP events on the 
 it runs on; `cpu_baseline` times the fp64 oracle on a bounded sample of the same work.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--dense] [--no-cpu-baseline]
+    python bench.py --sweep [--config 5]    (threshold sweep table, bf16 and fp8 Q/K)
 """
 import argparse
 import json
@@ -172,6 +173,80 @@ def run_cpu_baseline(cfg, thr, budget_s=15.0):
                       f"in fp64 numpy ({dt:.1f} s)"}
 
 
+def run_sweep(cfg_id, steps, warmup):
+    """Threshold sweep (the combined-sweep workload): for each thr, with bf16 and with fp8
+    Q/K, the kept fraction, step and attention time, effective TFLOP/s over kept tiles,
+    speedup over dense attention of the same shape, the error of sampled query blocks
+    against the fp64 oracle with the same mask, and how far that oracle output lies from
+    the fp64 dense output (what the sparsification itself changes). Prints a markdown
+    table and one JSON line per row."""
+    import numpy as np
+    import torch
+    import oracle
+    import block_sparse_attention_mask_amd as bsa
+    from synth import get_config, make_inputs, quantize_fp8_blocks
+
+    cfg = get_config(cfg_id)
+    fpt = _flops_per_tile(cfg.D)
+    q, k, v = make_inputs(cfg, seed=0, device="cuda:0")
+    heads = [0, cfg.H - 1]
+    blocks = [0, cfg.nb // 2, cfg.nb - 1]                  # includes the partly padded last block
+    rows = []
+    for fp8 in (False, True):
+        qa, ka, qs, ks = q, k, None, None
+        if fp8:
+            qa, qs = quantize_fp8_blocks(q)
+            ka, ks = quantize_fp8_blocks(k)
+        peak = BF16_PEAK_TFLOPS if not fp8 else 4.0 / (2.0 / FP8_PEAK_TFLOPS + 2.0 / BF16_PEAK_TFLOPS)
+        dense = run_gpu(cfg, steps, warmup, None, dense=True, fp8=fp8)
+        dense_tf = dense["kept_tiles"] * fpt / (dense["attn_ms"] * 1e-3) / 1e12
+        rows.append({"qk": "fp8" if fp8 else "bf16", "thr": "dense", "kept_fraction": 1.0,
+                     "step_ms": dense["attn_ms"], "attn_ms": dense["attn_ms"], "attn_tflops": dense_tf,
+                     "frac_peak": dense_tf / peak, "speedup_vs_dense": 1.0, "max_err": None, "mean_err": None,
+                     "sampled_kept_blocks": None, "max_sparsify_err": None})
+        for thr in cfg.thrs:
+            r = run_gpu(cfg, steps, warmup, thr, fp8=fp8)
+            tf = r["kept_tiles"] * fpt / (r["attn_ms"] * 1e-3) / 1e12
+            # error of sampled query blocks against the fp64 oracle, with the GPU's mask
+            mask = r["mask"].to("cuda:0")
+            out = bsa.block_sparse_attn_fwd(qa, ka, v, mask, s_valid=cfg.S_valid, q_scale=qs, k_scale=ks)
+            torch.cuda.synchronize()
+            errs, sparsify = [], []
+            for h in heads:
+                if fp8:
+                    qd = (qa[0, h].view(torch.float8_e4m3fn).double().view(cfg.nb, 64, cfg.D) * qs[0, h].double()[:, None, None]).view(cfg.S, cfg.D)
+                    kd = (ka[0, h].view(torch.float8_e4m3fn).double().view(cfg.nb, 64, cfg.D) * ks[0, h].double()[:, None, None]).view(cfg.S, cfg.D)
+                else:
+                    qd, kd = q[0, h].double(), k[0, h].double()
+                O, _ = oracle.block_sparse_attention(qd.cpu().numpy(), kd.cpu().numpy(), v[0, h].double().cpu().numpy(),
+                                                     r["mask"][0, h].numpy().astype(bool), 64, cfg.S_valid, q_blocks=blocks)
+                Od, _ = oracle.block_sparse_attention(qd.cpu().numpy(), kd.cpu().numpy(), v[0, h].double().cpu().numpy(),
+                                                      np.ones((cfg.nb, cfg.nb), bool), 64, cfg.S_valid, q_blocks=blocks)
+                for i in blocks:
+                    sl = slice(i * 64, min((i + 1) * 64, cfg.S_valid))
+                    errs.append(np.abs(out[0, h, sl].double().cpu().numpy() - O[sl]))
+                    sparsify.append(np.abs(O[sl] - Od[sl]))
+            e = np.concatenate([x.ravel() for x in errs])
+            sp = np.concatenate([x.ravel() for x in sparsify])
+            sampled_kept = int(sum(int(r["mask"][0, h, i].sum()) for h in heads for i in blocks))
+            rows.append({"qk": "fp8" if fp8 else "bf16", "thr": thr, "kept_fraction": r["kept_fraction"],
+                         "step_ms": r["ms_per_step"], "attn_ms": r["attn_ms"], "attn_tflops": tf,
+                         "frac_peak": tf / peak, "speedup_vs_dense": dense["attn_ms"] / r["ms_per_step"],
+                         "max_err": float(e.max()), "mean_err": float(e.mean()), "sampled_kept_blocks": sampled_kept,
+                         "max_sparsify_err": float(sp.max())})
+    print(f"| Q/K | thr | kept | step ms | attn ms | attn TFLOP/s | of peak | speedup vs dense (step) | max err | mean err "
+          f"| kv blocks of the sampled rows | max oracle sparse - dense |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for x in rows:
+        err = "" if x["max_err"] is None else f"{x['max_err']:.2e} | {x['mean_err']:.2e}"
+        print(f"| {x['qk']} | {x['thr']} | {100 * x['kept_fraction']:.1f}% | {x['step_ms']:.2f} | {x['attn_ms']:.2f} | "
+              f"{x['attn_tflops']:.0f} | {100 * x['frac_peak']:.1f}% | {x['speedup_vs_dense']:.2f}x | "
+              f"{err if err else '- | -'} | {x['sampled_kept_blocks'] if x['sampled_kept_blocks'] is not None else '-'} | "
+              f"{'-' if x['max_sparsify_err'] is None else format(x['max_sparsify_err'], '.2e')} |")
+    for x in rows:
+        print(json.dumps({"sweep": cfg.name, **{kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in x.items()}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +257,8 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
     ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="threshold sweep of the config (default 5) with bf16 and fp8 Q/K: table, not the bench line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -200,6 +277,9 @@ def main():
               f"(batch, head) with no communication, see the design notes)", file=sys.stderr)
         sys.exit(2)
 
+    if args.sweep:
+        run_sweep(args.config if args.config != 2 else 5, min(args.steps, 5), min(args.warmup, 2))
+        return
     from synth import get_config
     cfg = get_config(args.config)
     thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
