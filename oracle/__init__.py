@@ -10,6 +10,7 @@ pages by eye:
                 descending sort, exclusive cumulative mass, threshold at 1 - thr
   sta.py        static sliding-tile block mask (tile window, clipped at borders)
   attention.py  softmax attention restricted to the kept N x N blocks
+  attention_bwd.py  its gradients dQ, dK, dV (plain derivative of the same definition)
   csr.py        union of masks and the per-query-block kv index lists
 
 Pins: every function is checked by `tests/test_oracle_*.py` against closed forms,
@@ -18,8 +19,10 @@ brute force, textbook identities or library routines (see those files).
 from .nabla import block_pool, reduced_map, row_softmax, cdf_select, nabla_mask, nabla_masks
 from .sta import sta_block_mask, sta_token_mask
 from .attention import block_sparse_attention
+from .attention_bwd import block_sparse_attention_bwd
 from .csr import mask_or, mask_to_csr, longest_first_order
 
 __all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask",
            "nabla_masks", "sta_block_mask", "sta_token_mask", "block_sparse_attention",
+           "block_sparse_attention_bwd",
            "mask_or", "mask_to_csr", "longest_first_order"]
