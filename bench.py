@@ -38,8 +38,8 @@ def _measured_traffic(workload, fp8=False, dense=False):
     import hashlib
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["attn_fwd"]
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-    except (OSError, KeyError, ValueError):
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     if hashlib.sha256(src).hexdigest()[:16] != rec["sha256_prefix"] or fp8 or dense:
         return None

@@ -8,8 +8,9 @@
 // cross-wave communication is needed; NABLA (Pith review, "What carries the
 // argument"): the binary block mask tells the operator which N x N blocks to compute.
 //
-// Work decomposition: one wave (one workgroup) per query block of 64 tokens; the wave
-// walks that block's kv list. Per kv block:
+// Work decomposition: one 4-wave workgroup per pair of adjacent query blocks, two
+// waves (32 queries each) per block; the workgroup walks the union of the two kv
+// lists. Per kv block:
 //   * the 64 x D K and V tiles are copied global -> LDS with direct-to-LDS 16-byte
 //     loads, each 1 KB instruction fully coalesced; 16-byte chunks are XOR-swizzled
 //     inside a row so that the MFMA operand reads below are bank-conflict free;
@@ -25,127 +26,14 @@
 
 #include "common.h"
 #include "launch.h"
+#include "lds_tile.h"
 
 namespace bsa {
-
-// ---- LDS tile geometry ------------------------------------------------------
-// A tile row holds RB = D * elem bytes = NCH 16-byte chunks. 256 bytes of LDS span
-// all 64 banks, i.e. 16 chunks; rows shorter than that share a bank line.
-template <int RB>
-struct TileGeom {
-  static constexpr int NCH = RB / 16;           // chunks per row
-  static constexpr int RPL = 16 / NCH;          // rows per 256-byte bank line
-  // K-style swizzle: 16 consecutive rows at the same chunk hit 16 distinct chunk slots
-  static __device__ __forceinline__ int swz_k(int r) { return (r / RPL) % NCH; }
-  // V-style swizzle: 4 consecutive rows x 4 consecutive chunks hit 16 distinct slots
-  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) % (NCH / 4)); }
-};
-
-// One direct-to-LDS 16-byte load per lane: lane L's 16 bytes at gbase + voff land at
-// LDS address lds + 16 L. Issued from inline asm so that the compiler does not put a
-// blanket wait for every outstanding load in front of each LDS read; the kernel
-// waits for exactly the tiles it needs (wait_vm). The instruction has no register
-// result; its address operands are read at issue. M0 (the LDS base of the DMA) is
-// saved and restored around it.
-__device__ __forceinline__ void dma16(const char* gbase, unsigned voff, unsigned lds) {
-  unsigned sv;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(sv)
-      : "v"(voff), "s"(gbase), "s"(lds)
-      : "memory");
-}
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Copy a 64-row tile (row stride rs bytes) global -> LDS in 1 KB instructions, each
-// fully coalesced; 16-byte chunk c of row r is stored at chunk slot c ^ swizzle(r).
-template <int RB, bool VSWZ>
-__device__ __forceinline__ void load_tile_lds(const char* gtile, unsigned rs, unsigned lds, int lane) {
-  using G = TileGeom<RB>;
-  constexpr int RPI = 1024 / RB;                // rows per 1 KB instruction
-  constexpr int NI = 64 / RPI;
-#pragma unroll
-  for (int t = 0; t < NI; ++t) {
-    const int r = t * RPI + lane / G::NCH;
-    const int c = (lane % G::NCH) ^ (VSWZ ? G::swz_v(r) : G::swz_k(r));
-    dma16(gtile, (unsigned)r * rs + (unsigned)c * 16u, lds + t * 1024);
-  }
-}
-
-// Wave w of a P-wave workgroup issues instructions [w*NI/P, (w+1)*NI/P) of a tile copy.
-template <int RB, bool VSWZ, int P>
-__device__ __forceinline__ void load_tile_part(const char* gtile, unsigned rs, unsigned lds, int lane, int w) {
-  using G = TileGeom<RB>;
-  constexpr int RPI = 1024 / RB;
-  constexpr int NH = 64 / RPI / P;
-  static_assert(NH * RPI * P == 64, "tile copy must split evenly");
-#pragma unroll
-  for (int u = 0; u < NH; ++u) {
-    const int t = w * NH + u;
-    const int r = t * RPI + lane / G::NCH;
-    const int c = (lane % G::NCH) ^ (VSWZ ? G::swz_v(r) : G::swz_k(r));
-    dma16(gtile, (unsigned)r * rs + (unsigned)c * 16u, lds + t * 1024);
-  }
-}
-
-// byte offset of (row r, byte column cb) in a K-swizzled / V-swizzled tile
-template <int RB>
-__device__ __forceinline__ int koff(int r, int cb) {
-  using G = TileGeom<RB>;
-  return r * RB + (((cb >> 4) ^ G::swz_k(r)) << 4) + (cb & 15);
-}
-template <int RB>
-__device__ __forceinline__ int voff(int r, int cb) {
-  using G = TileGeom<RB>;
-  return r * RB + (((cb >> 4) ^ G::swz_v(r)) << 4) + (cb & 15);
-}
-
-__device__ __forceinline__ float partner(float x) {
-  // value of x in lane (l ^ 32)
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return lane_id() < 32 ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
-}
-
-// Eight consecutive accumulator values -> one bf16x8 MFMA operand (round to nearest even).
-// The operand is assembled from packed 32-bit words and cast as a whole vector: building
-// a bf16 vector element by element is mis-compiled by the current toolchain.
-__device__ __forceinline__ bf16x8_t pack_bf16x8(const f32x16_t& s, int base) {
-  i32x4_t w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    w[e] = (int)((unsigned)f32_to_bf16_bits(s[base + 2 * e]) |
-                 ((unsigned)f32_to_bf16_bits(s[base + 2 * e + 1]) << 16));
-  return __builtin_bit_cast(bf16x8_t, w);
-}
-
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ bf16x8_t join_bf16x8(s16x4_t a, s16x4_t b) {
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
-__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
 
 // The running maximum is only moved when a tile's maximum exceeds it by more than
 // RESCALE_TAU (log2 units): the probabilities then stay below 2^TAU, far inside the
 // fp32 range, and the rescale of the output accumulators is skipped on most tiles.
 constexpr float RESCALE_TAU = 8.f;
-
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 // MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
 //
