@@ -10,7 +10,7 @@ library is not built, every call raises.
 """
 import ctypes
 import os
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -24,7 +24,7 @@ _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPA
 EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "sta_workspace_size", "sta_build_mask", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "attn_workspace_size", "block_sparse_attn_fwd",
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
-           "bsa_last_error", "bsa_abi_version"]
+           "attn_bwd_workspace_size", "block_sparse_attn_bwd", "bsa_last_error", "bsa_abi_version"]
 
 
 class BsaError(RuntimeError):
@@ -73,6 +73,8 @@ def load(path: Optional[str] = None):
         "block_sparse_attn_fwd_csr": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
         "attn_work_order_slots": (i32, [PS]),
         "attn_work_order": (i32, [PS, vp, vp, vp]),
+        "attn_bwd_workspace_size": (sz, [PS]),
+        "block_sparse_attn_bwd": (i32, [PT, PT, PT, PT, PT, vp, PS, vp, i64, i64, dbl, PT, PT, PT, vp, sz, vp]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_abi_version": (i32, []),
     }
@@ -287,3 +289,31 @@ def block_sparse_attn_fwd_csr(q, k, v, row_ptr, col_idx, scale=None, s_valid=Non
         k_scale.data_ptr() if k_scale is not None else None, float(scale) if scale else 0.0, ctypes.byref(to),
         lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(), _stream(q.device)))
     return (out, lse) if return_lse else out
+
+
+def block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
+                          lse: torch.Tensor, mask: torch.Tensor, scale: Optional[float] = None,
+                          s_valid: Optional[int] = None, grad_dtype: Optional[torch.dtype] = None,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                          ws: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of block_sparse_attn_fwd for the upstream gradient `do`.
+
+    q, k, v, o, do: bf16 [B,H,S,D]; lse: the forward's float32 [B,H,S] output; mask and
+    scale as in the forward. Gradients are bf16 (default) or float32 (grad_dtype).
+    """
+    lib = load()
+    shape = _shape(q, s_valid)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
+    gdt = grad_dtype or torch.bfloat16
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=gdt, device=q.device) for _ in range(3))
+    if ws is None:
+        ws = _ws(lib.attn_bwd_workspace_size(ctypes.byref(shape)), q.device)
+    ptr, sb, sh, _m = _mask_strides(mask)
+    t = [_tensor(x) for x in (q, k, v, o, do) + tuple(out)]
+    _check(lib.block_sparse_attn_bwd(*(ctypes.byref(x) for x in t[:5]), lse.data_ptr(), ctypes.byref(shape),
+                                     ptr, sb, sh, float(scale) if scale else 0.0,
+                                     *(ctypes.byref(x) for x in t[5:]), ws.data_ptr(), ws.numel(),
+                                     _stream(q.device)))
+    return out

@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 3; }
+int bsa_abi_version(void) { return 4; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -366,6 +366,90 @@ bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, c
   if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
   return attn_common(q, k, v, shape, row_ptr, col_idx, work_order, q_scale, k_scale, scale, o, lse, ws,
                      (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+static size_t bwd_ld_bytes(const bsa_shape* s) { return align256(((size_t)s->B * s->H * s->S + 64) * 8); }
+
+size_t attn_bwd_workspace_size(const bsa_shape* s) {
+  if (!s || s->S <= 0 || s->B < 1 || s->H < 1) return 0;
+  const size_t nb = s->S / 64, rows = (size_t)s->B * s->H * nb;
+  return bwd_ld_bytes(s) + align256(rows * nb) + 2 * (align256((rows + 1) * 4) + align256(rows * nb * 4)) +
+         csr_workspace_size(s->B, s->H, (int)nb);
+}
+
+bsa_status block_sparse_attn_bwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                 const bsa_tensor* o, const bsa_tensor* d_o, const float* lse,
+                                 const bsa_shape* shape, const uint8_t* mask, int64_t mask_sb, int64_t mask_sh,
+                                 double scale, const bsa_tensor* dq, const bsa_tensor* dk, const bsa_tensor* dv,
+                                 void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  const bsa_tensor* in[5] = {q, k, v, o, d_o};
+  const char* in_name[5] = {"q", "k", "v", "o", "d_o"};
+  for (int x = 0; x < 5; ++x) {
+    if ((st = check_tensor(in_name[x], in[x], shape)) != BSA_OK) return st;
+    if (in[x]->dtype != BSA_BF16) return fail(BSA_EUNSUPPORTED, "backward: %s must be bf16", in_name[x]);
+  }
+  const bsa_tensor* out[3] = {dq, dk, dv};
+  const char* out_name[3] = {"dq", "dk", "dv"};
+  for (int x = 0; x < 3; ++x) {
+    if ((st = check_tensor(out_name[x], out[x], shape)) != BSA_OK) return st;
+    if (out[x]->dtype != dq->dtype || (dq->dtype != BSA_BF16 && dq->dtype != BSA_F32))
+      return fail(BSA_EINVAL, "backward: dq, dk, dv must all be bf16 or all f32");
+  }
+  if (!lse || ((uintptr_t)lse & 3)) return fail(BSA_EINVAL, "lse is NULL or not 4-byte aligned");
+  if (!std::isfinite(scale)) return fail(BSA_EINVAL, "scale is not finite");
+  const int nb = shape->S / 64;
+  if ((st = check_mask_args(mask, mask_sb, mask_sh, shape->B, shape->H, nb)) != BSA_OK) return st;
+  const size_t need = attn_bwd_workspace_size(shape);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+  if (scale <= 0.0) scale = 1.0 / std::sqrt((double)shape->D);
+
+  bsa::BwdArgs a = {};
+  a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
+  a.k = k->ptr; a.k_sb = k->sb; a.k_sh = k->sh; a.k_ss = k->ss;
+  a.v = v->ptr; a.v_sb = v->sb; a.v_sh = v->sh; a.v_ss = v->ss;
+  a.o = o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
+  a.d_o = d_o->ptr; a.do_sb = d_o->sb; a.do_sh = d_o->sh; a.do_ss = d_o->ss;
+  a.lse = lse;
+  a.dq = (void*)dq->ptr; a.dq_sb = dq->sb; a.dq_sh = dq->sh; a.dq_ss = dq->ss;
+  a.dk = (void*)dk->ptr; a.dk_sb = dk->sb; a.dk_sh = dk->sh; a.dk_ss = dk->ss;
+  a.dv = (void*)dv->ptr; a.dv_sb = dv->sb; a.dv_sh = dv->sh; a.dv_ss = dv->ss;
+  a.B = shape->B; a.H = shape->H; a.nb = nb; a.S = shape->S; a.S_valid = shape->S_valid; a.D = shape->D;
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+
+  const size_t rows = (size_t)shape->B * shape->H * nb;
+  char* w = (char*)ws;
+  float2* ld = (float2*)w;
+  w += bwd_ld_bytes(shape);
+  uint8_t* mt = (uint8_t*)w;
+  w += align256(rows * nb);
+  int32_t* row_ptr = (int32_t*)w;
+  w += align256((rows + 1) * 4);
+  int32_t* col_idx = (int32_t*)w;
+  w += align256(rows * nb * 4);
+  int32_t* col_ptr = (int32_t*)w;
+  w += align256((rows + 1) * 4);
+  int32_t* row_idx = (int32_t*)w;
+  w += align256(rows * nb * 4);
+  int32_t* counts = (int32_t*)w;
+
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = bsa::launch_bwd_prep(a, ld, hs);
+  if (e != hipSuccess) return hip_status(e, "backward prep launch");
+  e = bsa::launch_csr(mask, mask_sb, mask_sh, shape->B, shape->H, nb, row_ptr, col_idx, counts, hs);
+  if (e != hipSuccess) return hip_status(e, "csr launch");
+  e = bsa::launch_mask_transpose(mask, mask_sb, mask_sh, shape->B, shape->H, nb, mt, hs);
+  if (e != hipSuccess) return hip_status(e, "mask transpose launch");
+  e = bsa::launch_csr(mt, (int64_t)shape->H * nb * nb, (int64_t)nb * nb, shape->B, shape->H, nb, col_ptr, row_idx,
+                      counts, hs);
+  if (e != hipSuccess) return hip_status(e, "csr launch (transposed)");
+  return hip_status(bsa::launch_bwd(a, dq->dtype == BSA_F32, row_ptr, col_idx, col_ptr, row_idx, ld, hs),
+                    "backward launch");
 }
 
 }  // extern "C"

@@ -65,4 +65,28 @@ hipError_t launch_attn(const AttnArgs& a, AttnMode mode, hipStream_t st);
 hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, int B, int H, int S, int D,
                             uint16_t* hi, uint16_t* lo, hipStream_t st);
 
+// attn_bwd.hip (bf16 q, k, v, o, dO; dq, dk, dv bf16 or f32; strides in elements)
+struct BwdArgs {
+  const void* q; int64_t q_sb, q_sh, q_ss;
+  const void* k; int64_t k_sb, k_sh, k_ss;
+  const void* v; int64_t v_sb, v_sh, v_ss;
+  const void* o; int64_t o_sb, o_sh, o_ss;
+  const void* d_o; int64_t do_sb, do_sh, do_ss;
+  const float* lse;      // [B, H, S] natural log, as the forward writes it
+  void* dq; int64_t dq_sb, dq_sh, dq_ss;
+  void* dk; int64_t dk_sb, dk_sh, dk_ss;
+  void* dv; int64_t dv_sb, dv_sh, dv_ss;
+  int B, H, nb, S, S_valid, D;
+  float scale;           // softmax scale
+  float scale_log2;      // scale * log2(e)
+};
+// (lse2, delta) per query into ld [B*H*S (+64 entries of padding read by the tile copies)]
+hipError_t launch_bwd_prep(const BwdArgs& a, float2* ld, hipStream_t st);
+// mt [B*H, nb, nb] contiguous = the mask transposed per head
+hipError_t launch_mask_transpose(const uint8_t* m, int64_t sb, int64_t sh, int B, int H, int nb, uint8_t* mt,
+                               hipStream_t st);
+// dK, dV from the per-key-block query lists (col_ptr, row_idx), then dQ from the kv lists
+hipError_t launch_bwd(const BwdArgs& a, bool f32_out, const int32_t* row_ptr, const int32_t* col_idx,
+                      const int32_t* col_ptr, const int32_t* row_idx, const float2* ld, hipStream_t st);
+
 }  // namespace bsa

@@ -206,6 +206,38 @@ int attn_work_order_slots(const bsa_shape* shape);
 bsa_status attn_work_order(const bsa_shape* shape, const int32_t* row_ptr, int32_t* order,
                            bsa_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention backward [FA: exact tiled attention trains Transformers
+ * and extends to block-sparse attention; NABLA review, "Editorial extensions": a DiT
+ * trains with the NABLA block mask]. The gradients of the forward above, for the
+ * same mask, from the upstream gradient dO:
+ *   P = softmax over allowed keys,  dV = P^T dO,  dP = dO V^T,
+ *   delta_p = <dO_p, O_p>,  dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Query rows >= S_valid and query rows with no allowed key (lse = -inf) carry no
+ * gradient: their dQ rows are 0 and they add nothing to dK, dV; key rows >= S_valid
+ * get dK = dV = 0. The probabilities are recomputed from lse; no atomics are used, so
+ * the results are the same on every run.
+ *
+ *   q, k, v    bf16 [B,H,S,D], D in {64, 128} (the forward's inputs)
+ *   o          bf16 [B,H,S,D], the forward's output for these inputs and this mask
+ *   d_o        bf16 [B,H,S,D], the gradient of the loss with respect to o
+ *   lse        float [B,H,S] contiguous, the forward's lse output
+ *   mask       the forward's block mask (same layout and strides as there)
+ *   scale      softmax scale; <= 0 selects 1/sqrt(D) (must match the forward)
+ *   dq, dk, dv outputs [B,H,S,D], all three bf16 or all three f32; every row written
+ *   ws         at least attn_bwd_workspace_size(shape) bytes, 256-byte aligned (holds
+ *              delta, the transposed mask and both index lists)
+ * Row alignment as for the forward. Errors: BSA_EINVAL for bad pointers, strides or
+ * dtypes, BSA_EUNSUPPORTED for other dtypes or D, BSA_EWORKSPACE for a short ws.
+ * ------------------------------------------------------------------------- */
+size_t attn_bwd_workspace_size(const bsa_shape* shape);
+bsa_status block_sparse_attn_bwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                 const bsa_tensor* o, const bsa_tensor* d_o, const float* lse,
+                                 const bsa_shape* shape,
+                                 const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, double scale,
+                                 const bsa_tensor* dq, const bsa_tensor* dk, const bsa_tensor* dv,
+                                 void* ws, size_t ws_bytes, bsa_stream_t stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* bsa_last_error(void);
 

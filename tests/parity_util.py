@@ -78,3 +78,18 @@ def sample_blocks(keep: np.ndarray, per_head: int, seed: int = 0, full_heads=())
                 pick.add(int(rng.integers(nb)))
             out += [(b, h, i) for i in sorted(pick)]
     return out
+
+# Gradient tolerances (bf16 inputs, bf16 MFMA operands P and dS, fp32 accumulation):
+# the forward's bounds applied to each gradient tensor scaled to unit maximum, i.e.
+# max |err| <= 2e-2 * max |ref| and mean |err| <= 2e-3 * max |ref| per head.
+GRAD_MAX_REL = 2e-2
+GRAD_MEAN_REL = 2e-3
+
+
+def grad_errors(gpu: torch.Tensor, ref: np.ndarray, rows):
+    """(max |err|, mean |err|, max |ref|) of gpu[rows] against ref[rows] ([S, D] per head)."""
+    g = f64(gpu)[rows]
+    r = ref[rows]
+    assert np.isfinite(r).all()
+    e = np.abs(g - r)
+    return float(e.max()), float(e.mean()), float(np.abs(r).max())

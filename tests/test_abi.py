@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 3
+    assert lib.bsa_abi_version() == 4
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
@@ -111,3 +111,24 @@ def test_attention_rejects(lib):
     assert call(args(ws=4097)) == 1
     f32 = lib.attn_workspace_size(ctypes.byref(shape), bsa.BSA_F32)
     assert f32 > ws            # f32 inputs need room for their bf16 hi/lo copies
+
+
+def _bwd(lib, shape, q=None, o=None, dq=None, dk=None, lse=4096, mask=4096, ws_bytes=1 << 40):
+    t = [q or _t(), _t(), _t(), o or _t(), _t()]
+    g = [dq or _t(), dk or _t(), _t()]
+    return lib.block_sparse_attn_bwd(*(ctypes.byref(x) for x in t), lse, ctypes.byref(shape), mask, 0, 0, 0.0,
+                                     *(ctypes.byref(x) for x in g), 8192, ws_bytes, None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    assert _bwd(lib, shape, q=_t(dtype=bsa.BSA_FP8_E4M3FN)) == 2
+    assert "bf16" in lib.bsa_last_error().decode()
+    assert _bwd(lib, shape, o=_t(ptr=258)) == 1
+    assert _bwd(lib, shape, dq=_t(dtype=bsa.BSA_F32)) == 1              # dq f32, dk bf16
+    assert "all three" in lib.bsa_last_error().decode() or "all f32" in lib.bsa_last_error().decode()
+    assert _bwd(lib, shape, lse=None) == 1
+    assert _bwd(lib, shape, mask=None) == 1
+    assert _bwd(lib, shape, ws_bytes=16) == 3
+    assert _bwd(lib, bsa.Shape(1, 2, 256, 256, 96, 64)) == 2
+    assert lib.attn_bwd_workspace_size(ctypes.byref(shape)) > 0
