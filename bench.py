@@ -174,6 +174,103 @@ def run_cpu_baseline(cfg, thr, budget_s=15.0):
                       f"in fp64 numpy ({dt:.1f} s)"}
 
 
+def run_backward(cfg, steps, warmup, thr, cpu_baseline=True):
+    """Backward pass (dq, dk, dv) of the block-sparse attention for the config's mask.
+
+    The mask, the forward output and lse are built once; the timed region is K calls
+    of block_sparse_attn_bwd (delta pre-pass, both index lists, dK/dV and dQ kernels).
+    Effective TFLOP/s counts the usual five 64x64xD products per kept tile (S, dP, dV,
+    dK, dQ = 2.5x the forward's flops); the kernels compute S and dP twice (once for
+    dK/dV, once for dQ), which that count leaves out."""
+    import torch
+    import block_sparse_attention_mask_amd as bsa
+    from synth import make_inputs
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(cfg, seed=0, device=dev)
+    do = torch.randn(q.shape, generator=torch.Generator(device="cpu").manual_seed(1)).to(torch.bfloat16).to(dev)
+    plane = None
+    if cfg.sta is not None:
+        plane = bsa.sta_build_mask(cfg.S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                                   order_tile=cfg.order_tile, device=dev)
+    mask = bsa.nabla_build_mask(q, k, thr, or_mask=plane) if thr is not None else plane
+    o, lse = bsa.block_sparse_attn_fwd(q, k, v, mask, s_valid=cfg.S_valid, return_lse=True)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    import ctypes
+    shp = bsa.Shape(cfg.B, cfg.H, cfg.S, cfg.S_valid, cfg.D, 64)
+    ws = torch.empty(max(256, bsa.load().attn_bwd_workspace_size(ctypes.byref(shp))), dtype=torch.uint8, device=dev)
+
+    def bwd():
+        bsa.block_sparse_attn_bwd(q, k, v, o, do, lse, mask, s_valid=cfg.S_valid, out=grads, ws=ws)
+
+    def fwd():
+        bsa.block_sparse_attn_fwd(q, k, v, mask, s_valid=cfg.S_valid, return_lse=True)
+
+    res = {}
+    for name, fn in (("bwd", bwd), ("fwd", fwd)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    m = mask.expand(cfg.B, cfg.H, cfg.nb, cfg.nb) if mask.dim() == 2 else mask
+    kept = int(m.sum().item())
+    fpt = _flops_per_tile(cfg.D)
+    tf = 2.5 * kept * fpt / (res["bwd"] * 1e-3) / 1e12
+    line = {
+        "metric": "sparse attn backward effective TFLOP/s (kept tiles, 5 products per tile)",
+        "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(res["bwd"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Q/K/V with smooth positional term; dO ~ N(0,1))",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S, "S_valid": cfg.S_valid, "D": cfg.D,
+                   "thr": thr, "sta": cfg.sta is not None, "pass": "backward"},
+        "fwd_ms_same_call_path": round(res["fwd"], 4), "bwd_over_fwd": round(res["bwd"] / res["fwd"], 3),
+        "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "kept_tiles": kept,
+        "kept_fraction": round(kept / (cfg.B * cfg.H * cfg.nb * cfg.nb), 5),
+    }
+    if cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline_bwd(cfg, m[0].cpu().numpy().astype(bool))
+    print(json.dumps(line), flush=True)
+
+
+def run_cpu_baseline_bwd(cfg, keep0, budget_s=15.0):
+    """The fp64 gradient oracle (as it stands) on a bounded sample: runs of 8 query blocks
+    of head 0 with their dq (the oracle then forms S, P V, dP and dS K for those rows:
+    4 of the 64x64xD products per kept tile), until the budget is spent."""
+    import numpy as np
+    import oracle
+    from synth import make_inputs, get_config
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    c1 = get_config(cfg.cid, heads=1)
+    q, k, v = make_inputs(c1, seed=0, device="cpu")
+    qh, kh, vh = (x[0, 0].double().numpy() for x in (q, k, v))
+    do = np.random.default_rng(1).standard_normal((cfg.S, cfg.D))
+    flops, blocks_done = 0.0, 0
+    t0 = time.perf_counter()
+    for i0 in range(0, cfg.nb, 8):
+        blocks = list(range(i0, min(cfg.nb, i0 + 8)))
+        oracle.block_sparse_attention_bwd(qh, kh, vh, do, keep0[0], 64, cfg.S_valid, q_blocks=blocks, kv_blocks=[])
+        flops += 2.0 * keep0[0][blocks].sum() * _flops_per_tile(cfg.D)
+        blocks_done += len(blocks)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{cfg.name}: dq of {blocks_done} query blocks of head 0 in fp64 numpy ({dt:.1f} s; "
+                      f"4 products per kept tile)"}
+
+
 def run_sweep(cfg_id, steps, warmup):
     """Threshold sweep (the combined-sweep workload): for each thr, with bf16 and with fp8
     Q/K, the kept fraction, step and attention time, effective TFLOP/s over kept tiles,
@@ -262,6 +359,8 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
     ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dq, dk, dv) of the config instead of the forward step")
     ap.add_argument("--sweep", action="store_true",
                     help="threshold sweep of the config (default 5) with bf16 and fp8 Q/K: table, not the bench line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -284,6 +383,12 @@ def main():
 
     if args.sweep:
         run_sweep(args.config if args.config != 2 else 5, min(args.steps, 5), min(args.warmup, 2))
+        return
+    if args.backward:
+        from synth import get_config
+        cfg = get_config(args.config)
+        thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
+        run_backward(cfg, args.steps, args.warmup, thr, cpu_baseline=not args.no_cpu_baseline)
         return
     from synth import get_config
     cfg = get_config(args.config)
