@@ -79,10 +79,14 @@ def sample_blocks(keep: np.ndarray, per_head: int, seed: int = 0, full_heads=())
             out += [(b, h, i) for i in sorted(pick)]
     return out
 
-# Gradient tolerances (bf16 inputs, bf16 MFMA operands P and dS, fp32 accumulation):
-# the forward's bounds applied to each gradient tensor scaled to unit maximum, i.e.
-# max |err| <= 2e-2 * max |ref| and mean |err| <= 2e-3 * max |ref| per head.
-GRAD_MAX_REL = 2e-2
+# Gradient tolerances per head, relative to the largest reference gradient. Three
+# roundings enter: P and dS as bf16 MFMA operands (unit roundoff 2^-9), the bf16 output,
+# and delta = <dO, O> formed from the forward's bf16 output O. Since sum_k dS_qk = 0, dQ
+# and dK are sums with cancellation, so these roundings are relative to the absolute
+# terms, not to the result: each of the first and the last moves dQ by up to ~1% of
+# max |dQ| on the 2B-DiT shape (fp64 emulation of the roundings), hence
+# max |err| <= 4e-2 * max |ref|; the mean bound is the forward's, 2e-3 * max |ref|.
+GRAD_MAX_REL = 4e-2
 GRAD_MEAN_REL = 2e-3
 
 

@@ -2,7 +2,7 @@
 
 The GPU forward supplies o and lse (the backward's contract); the oracle recomputes
 everything in fp64 from the same bf16 inputs and the same mask. Per head and per
-gradient: max |err| <= 2e-2 max |ref| and mean |err| <= 2e-3 max |ref|, over every row
+gradient: max |err| <= 4e-2 max |ref| and mean |err| <= 2e-3 max |ref|, over every row
 where the oracle is cheap, else over sampled query blocks (dq) and key blocks (dk, dv)
 that always include the first, middle and last (padded) ones.
 """
