@@ -12,6 +12,7 @@ pages by eye:
   attention.py  softmax attention restricted to the kept N x N blocks
   attention_bwd.py  its gradients dQ, dK, dV (plain derivative of the same definition)
   csr.py        union of masks and the per-query-block kv index lists
+  fp8.py        e4m3fn encoding and per-block fp8 quantisation of Q and K
 
 Pins: every function is checked by `tests/test_oracle_*.py` against closed forms,
 brute force, textbook identities or library routines (see those files).
@@ -21,8 +22,10 @@ from .sta import sta_block_mask, sta_token_mask
 from .attention import block_sparse_attention
 from .attention_bwd import block_sparse_attention_bwd
 from .csr import mask_or, mask_to_csr, longest_first_order
+from .fp8 import decode_e4m3fn, encode_e4m3fn, quantize_blocks
 
 __all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask",
            "nabla_masks", "sta_block_mask", "sta_token_mask", "block_sparse_attention",
            "block_sparse_attention_bwd",
-           "mask_or", "mask_to_csr", "longest_first_order"]
+           "mask_or", "mask_to_csr", "longest_first_order", "decode_e4m3fn", "encode_e4m3fn",
+           "quantize_blocks"]

@@ -1,0 +1,70 @@
+"""fp8 e4m3fn block quantisation of Q and K, fp64/fp32 reference (test infrastructure only).
+
+Source: FlashAttention-3 abstract (Daily Papers listing): block quantisation for
+FP8 attention; the combined-sweep workload quantises Q and K to fp8 e4m3 with one
+scale per 64-token block. The e4m3fn format (OCP 8-bit floating point): sign bit,
+4 exponent bits with bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, no infinities,
+S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+
+Reading (the pages fix only "per-block scale"): scale = amax / 448 over the 64 x D
+values of the block, computed in fp32 (an all-zero block gets scale 1); each value
+is divided by the scale in fp32 (correctly rounded) and encoded round-to-nearest-even
+(ties to the code with an even mantissa), saturating at +-448. Both the rounding of
+the quotient and the choice of the code are taken in fp32, the precision the GPU
+takes them in.
+"""
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def e4m3fn_values() -> np.ndarray:
+    """Value of every code 0..255 (NaN for the two NaN codes), from the format definition."""
+    vals = np.empty(256)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = s * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_VALS = e4m3fn_values()
+_POS_CODES = np.arange(0, 0x7F)                 # +0 .. +448, ascending values
+_POS_VALS = _VALS[_POS_CODES]
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """Nearest e4m3fn code of each value (ties to the even code), saturating at +-448;
+    NaN -> 0x7F. Signed zeros keep their sign."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_POS_VALS, a, side="left"), 0, len(_POS_VALS) - 1)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_VALS[lo]
+    d_hi = _POS_VALS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
+    code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    return _VALS[np.asarray(codes, dtype=np.uint8)]
+
+
+def quantize_blocks(x, n: int = 64):
+    """x [..., S, D] (any float) -> (codes uint8 [..., S, D], scales float32 [..., S/n])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    *lead, S, D = x32.shape
+    blk = x32.reshape(*lead, S // n, n, D)
+    amax = np.abs(blk).max(axis=(-2, -1))
+    scales = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = (blk / scales[..., None, None]).astype(np.float32)
+    codes = encode_e4m3fn(q).reshape(*lead, S, D)
+    return codes, scales

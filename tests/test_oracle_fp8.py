@@ -1,0 +1,85 @@
+"""Pins for the fp8 e4m3fn block quantiser of the oracle (CPU only).
+
+The encoder searches the table of code values built from the format definition;
+it is checked against torch's own float8_e4m3fn cast (a library routine) on values
+of every kind inside the format's range, and by round trips and closed-form
+properties; the block quantiser against its defining properties.
+"""
+import numpy as np
+import torch
+
+from oracle.fp8 import decode_e4m3fn, e4m3fn_values, encode_e4m3fn, quantize_blocks
+
+
+def _torch_codes(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(x32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_format_table():
+    v = e4m3fn_values()
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0
+    assert v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6 and v[0x38] == 1.0
+    fin = v[np.isfinite(v)]
+    assert len(fin) == 254 and len(set(np.abs(fin))) == 127     # +-0 .. 448
+
+
+def test_round_trip_of_every_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(encode_e4m3fn(decode_e4m3fn(codes)), codes)
+
+
+def test_matches_torch_cast_inside_the_range():
+    rng = np.random.default_rng(0)
+    v = e4m3fn_values()
+    pos = np.sort(v[np.isfinite(v) & (v >= 0)])
+    mids = (pos[1:] + pos[:-1]) / 2                              # exact ties (representable in fp32)
+    x = np.concatenate([
+        rng.uniform(-463.9, 463.9, 20000),
+        rng.normal(0, 1, 20000),
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 5000),                  # subnormal range
+        mids, -mids, pos, -pos,
+        np.nextafter(mids, 0), np.nextafter(mids, 1000),           # just below / above each tie
+        [0.0, -0.0, 447.9, 448.0, 450.0, 463.99, -463.99],
+    ]).astype(np.float32)
+    ours = encode_e4m3fn(x)
+    assert np.array_equal(ours, _torch_codes(x))
+
+
+def test_saturation_and_nan():
+    x = np.array([464.0, 500.0, 1e30, -1e30, np.inf, -np.inf, np.nan], dtype=np.float32)
+    assert list(encode_e4m3fn(x)) == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE, 0x7F]
+
+
+def test_block_quantiser_properties():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 3, 256, 64)).astype(np.float32) * rng.uniform(0.01, 100, (2, 3, 1, 1))
+    x[0, 1, 64:128] = 0.0                                          # an all-zero block
+    codes, scales = quantize_blocks(x, 64)
+    assert codes.dtype == np.uint8 and scales.dtype == np.float32 and scales.shape == (2, 3, 4)
+    assert scales[0, 1, 1] == 1.0 and np.all(codes[0, 1, 64:128] == 0)
+    blk = x.reshape(2, 3, 4, 64, 64)
+    cb = codes.reshape(2, 3, 4, 64, 64)
+    for idx in np.ndindex(2, 3, 4):
+        if not np.any(blk[idx]):
+            continue
+        assert scales[idx] == np.float32(np.abs(blk[idx]).max()) / np.float32(448.0)
+        amax_pos = np.unravel_index(np.abs(blk[idx]).argmax(), (64, 64))
+        assert cb[idx][amax_pos] & 0x7F == 0x7E                    # the block maximum maps to 448
+        dec = decode_e4m3fn(cb[idx]) * scales[idx]
+        err = np.abs(dec - blk[idx])
+        # half a mantissa step: 2^-4 relative in the normal range, 2^-10 * scale below it
+        assert np.all(err <= np.maximum(np.abs(blk[idx]) * 2.0 ** -4, scales[idx] * 2.0 ** -10) * (1 + 1e-6))
+
+
+def test_block_quantiser_equals_torch_reference_path():
+    # scale and quotient in fp32, then torch's float8 cast: the same definition by library routines
+    rng = np.random.default_rng(2)
+    x = torch.from_numpy(rng.standard_normal((1, 2, 192, 128)).astype(np.float32)).to(torch.bfloat16)
+    codes, scales = quantize_blocks(x.float().numpy(), 64)
+    xf = x.float().reshape(1, 2, 3, 64, 128)
+    amax = xf.abs().amax(dim=(3, 4))
+    ts = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    tq = (xf / ts[..., None, None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(1, 2, 192, 128)
+    assert np.array_equal(scales, ts.numpy())
+    assert np.array_equal(codes, tq.numpy())
