@@ -21,7 +21,8 @@ BSA_F32, BSA_BF16, BSA_FP8_E4M3FN = 0, 1, 2
 _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPACE", 4: "BSA_EHIP"}
 
 # every function the C header declares, in declaration order
-EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "sta_workspace_size", "sta_build_mask", "mask_or",
+EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "quantize_fp8_blocks", "nabla_build_mask_fp8",
+           "sta_workspace_size", "sta_build_mask", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "attn_workspace_size", "block_sparse_attn_fwd",
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
            "attn_bwd_workspace_size", "block_sparse_attn_bwd", "bsa_last_error", "bsa_abi_version"]
@@ -62,6 +63,8 @@ def load(path: Optional[str] = None):
     sig = {
         "nabla_workspace_size": (sz, [PS]),
         "nabla_build_mask": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, sz, vp]),
+        "quantize_fp8_blocks": (i32, [PT, PS, PT, vp, vp]),
+        "nabla_build_mask_fp8": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, PT, vp, PT, vp, vp, sz, vp]),
         "sta_workspace_size": (sz, [PS]),
         "sta_build_mask": (i32, [PS, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
         "mask_or": (i32, [vp, vp, i64, vp, i64, vp]),
@@ -150,6 +153,53 @@ def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Option
                                 float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(), ws.data_ptr(),
                                 ws.numel(), _stream(q.device)))
     return out
+
+
+def _fp8_buffers(x: torch.Tensor, out=None):
+    if out is not None:
+        return out
+    B, H, S, _ = x.shape
+    return (torch.empty(x.shape, dtype=torch.uint8, device=x.device),
+            torch.empty(B, H, S // 64, dtype=torch.float32, device=x.device))
+
+
+def quantize_fp8_blocks(x: torch.Tensor, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """fp8 e4m3fn codes (uint8 [B,H,S,D]) and per-block scales (float32 [B,H,S/64]) of x."""
+    lib = load()
+    shp = _shape(x, None)
+    codes, scales = _fp8_buffers(x, out)
+    if not scales.is_contiguous() or scales.dtype != torch.float32:
+        raise ValueError("scales must be contiguous float32 [B, H, S/64]")
+    tx, tc = _tensor(x), _tensor(codes)
+    _check(lib.quantize_fp8_blocks(ctypes.byref(tx), ctypes.byref(shp), ctypes.byref(tc), scales.data_ptr(),
+                                   _stream(x.device)))
+    return codes, scales
+
+
+def nabla_build_mask_fp8(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Optional[float] = None,
+                         or_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                         q8_out=None, k8_out=None):
+    """nabla_build_mask plus the fp8 block quantisation of q and k from the same read.
+
+    Returns (mask, (q codes, q scales), (k codes, k scales))."""
+    lib = load()
+    B, H, S, D = q.shape
+    nb = S // 64
+    shp = _shape(q, None)
+    if out is None:
+        out = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device)
+    q8, qs = _fp8_buffers(q, q8_out)
+    k8, ks = _fp8_buffers(k, k8_out)
+    ws = _ws(lib.nabla_workspace_size(ctypes.byref(shp)), q.device)
+    om, osb, osh = None, 0, 0
+    if or_mask is not None:
+        om, osb, osh, _keep = _mask_strides(or_mask)
+    tq, tk, tq8, tk8 = _tensor(q), _tensor(k), _tensor(q8), _tensor(k8)
+    _check(lib.nabla_build_mask_fp8(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
+                                    float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(),
+                                    ctypes.byref(tq8), qs.data_ptr(), ctypes.byref(tk8), ks.data_ptr(),
+                                    ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return out, (q8, qs), (k8, ks)
 
 
 def sta_build_mask(S: int, S_valid: int, grid: Sequence[int], tile: Sequence[int], window: Sequence[int],

@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 4; }
+int bsa_abi_version(void) { return 5; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -89,10 +89,10 @@ size_t nabla_workspace_size(const bsa_shape* s) {
   return 2 * align256(bh * nbp * (size_t)s->D * sizeof(double));
 }
 
-bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
-                            double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh, uint8_t* mask_out,
-                            void* ws, size_t ws_bytes, bsa_stream_t stream) {
-  g_err.clear();
+static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                               double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                               uint8_t* mask_out, const bsa::Fp8Out* f8, void* ws, size_t ws_bytes,
+                               bsa_stream_t stream) {
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
   if ((st = check_tensor("q", q, shape)) != BSA_OK) return st;
@@ -116,12 +116,68 @@ bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_
   const int64_t qs[3] = {q->sb, q->sh, q->ss}, ks[3] = {k->sb, k->sh, k->ss};
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = bsa::launch_pool(q->dtype == BSA_F32, shape->D, q->ptr, qs, k->ptr, ks, shape->B, shape->H, nb,
-                                  qbar, kbarT, hs);
+                                  qbar, kbarT, f8, hs);
   if (e != hipSuccess) return hip_status(e, "pool launch");
   const uint64_t T_fixed = (uint64_t)std::ldexp(1.0 - thr, 60);
   e = bsa::launch_select(qbar, kbarT, shape->B, shape->H, nb, shape->D, scale, T_fixed, or_mask, or_sb, or_sh,
                          mask_out, hs);
   return hip_status(e, "select launch");
+}
+
+bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                            double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh, uint8_t* mask_out,
+                            void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, nullptr, ws, ws_bytes, stream);
+}
+
+static bsa_status check_fp8_out(const char* name, const bsa_tensor* c, const float* sc, const bsa_shape* shape) {
+  bsa_status st;
+  if ((st = check_tensor(name, c, shape)) != BSA_OK) return st;
+  if (c->dtype != BSA_FP8_E4M3FN) return fail(BSA_EINVAL, "%s must have dtype fp8 e4m3fn", name);
+  if (!sc || ((uintptr_t)sc & 3)) return fail(BSA_EINVAL, "%s scales are NULL or not 4-byte aligned", name);
+  return BSA_OK;
+}
+
+static bsa::Fp8Out fp8_out(const bsa_tensor* c0, float* s0, const bsa_tensor* c1, float* s1) {
+  bsa::Fp8Out f = {};
+  const bsa_tensor* c[2] = {c0, c1};
+  float* sc[2] = {s0, s1};
+  for (int x = 0; x < 2; ++x) {
+    if (!c[x]) continue;
+    f.codes[x] = (uint8_t*)c[x]->ptr;
+    f.sb[x] = c[x]->sb; f.sh[x] = c[x]->sh; f.ss[x] = c[x]->ss;
+    f.scale[x] = sc[x];
+  }
+  return f;
+}
+
+bsa_status nabla_build_mask_fp8(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                                double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                                uint8_t* mask_out, const bsa_tensor* q8, float* q_scale, const bsa_tensor* k8,
+                                float* k_scale, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  if ((st = check_fp8_out("q8", q8, q_scale, shape)) != BSA_OK) return st;
+  if ((st = check_fp8_out("k8", k8, k_scale, shape)) != BSA_OK) return st;
+  const bsa::Fp8Out f8 = fp8_out(q8, q_scale, k8, k_scale);
+  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, &f8, ws, ws_bytes, stream);
+}
+
+bsa_status quantize_fp8_blocks(const bsa_tensor* x, const bsa_shape* shape, const bsa_tensor* codes, float* scales,
+                               bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  if ((st = check_tensor("x", x, shape)) != BSA_OK) return st;
+  if (x->dtype != BSA_BF16 && x->dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "x must be bf16 or f32");
+  if ((st = check_fp8_out("codes", codes, scales, shape)) != BSA_OK) return st;
+  const bsa::Fp8Out f8 = fp8_out(codes, scales, nullptr, nullptr);
+  const int64_t xs[3] = {x->sb, x->sh, x->ss};
+  return hip_status(bsa::launch_pool(x->dtype == BSA_F32, shape->D, x->ptr, xs, x->ptr, xs, shape->B, shape->H,
+                                     shape->S / 64, nullptr, nullptr, &f8, (hipStream_t)stream),
+                    "quantize launch");
 }
 
 // ---------------------------------------------------------------------------

@@ -8,9 +8,18 @@
 namespace bsa {
 
 // nabla.hip
+// fp8 outputs of the pool kernel: codes [B,H,S,D] (byte strides) and one fp32 scale
+// per (b, h, block), [B,H,nb] contiguous; index 0 for Q, 1 for K.
+struct Fp8Out {
+  uint8_t* codes[2];
+  int64_t sb[2], sh[2], ss[2];
+  float* scale[2];
+};
+// Block means of q and k into qbar / kbarT; with f8, also their fp8 block quantisation
+// from the same read. qbar == NULL: quantisation of q alone (f8 index 0).
 hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* q_strides, const void* k,
                        const int64_t* k_strides, int B, int H, int nb, double* qbar, double* kbarT,
-                       hipStream_t st);
+                       const Fp8Out* f8, hipStream_t st);
 hipError_t launch_select(const double* qbar, const double* kbarT, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                          uint8_t* mask_out, hipStream_t st);

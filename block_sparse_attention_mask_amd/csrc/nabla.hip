@@ -37,17 +37,46 @@ __device__ __forceinline__ int64_t mf_index(int bh, int nb, int D, int blk, int 
 }
 
 // ----------------------------------------------------------------------------
+// fp8 e4m3fn encoding of an fp32 value, round to nearest even, saturating at +-448
+// (OCP 8-bit floating point: bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, no
+// infinities; FlashAttention-3 abstract, Daily Papers listing: block quantisation).
+// Normal range: round the 23-bit fp32 mantissa to 3 bits on the bit pattern (a carry
+// into the exponent is the correct next binade), then rebias 127 -> 7. Below 2^-6 the
+// codes are multiples of 2^-9, so the code is rint(|x| 512) (8 is the smallest normal).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ unsigned encode_e4m3(float x) {
+  const unsigned u = __float_as_uint(x);
+  const unsigned sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7Fu;
+  unsigned c;
+  if (a >= 448.f) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {
+    c = (unsigned)__builtin_rintf(a * 512.f);
+  } else {
+    const unsigned v = __float_as_uint(a), base = v >> 20, rem = v & 0xFFFFFu;
+    c = base + (rem > 0x80000u || (rem == 0x80000u && (base & 1u))) - (120u << 3);
+  }
+  return c | sign;
+}
+
+// ----------------------------------------------------------------------------
 // Pooling: Qbar[bh][i][d] = (1/64) sum_r Q[bh][64 i + r][d], and Kbar likewise.
 // One workgroup per two consecutive blocks of one (bh, tensor); each thread issues
 // all of its 16-byte loads (8 rows x 2 blocks) before converting any. NT: streaming
 // (non-temporal) loads, for inputs much larger than the last-level cache.
+// Q8: from the same registers, the block's fp8 quantisation (scale = amax / 448 in
+// fp32, codes = e4m3(x / scale)), so a run with fp8 Q/K reads Q and K once.
+// POOL = false skips the means (quantisation alone, of the tensor in q).
 // ----------------------------------------------------------------------------
 constexpr int POOL_BPW = 2;   // blocks per workgroup
-template <typename T, int D, bool NT>
+template <typename T, int D, bool NT, bool POOL, bool Q8>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
                                                    int64_t q_ss, const T* __restrict__ k, int64_t k_sb,
                                                    int64_t k_sh, int64_t k_ss, int H, int nb,
-                                                   double* __restrict__ qbar, double* __restrict__ kbarT) {
+                                                   double* __restrict__ qbar, double* __restrict__ kbarT,
+                                                   Fp8Out f8) {
   constexpr int E = 16 / sizeof(T);        // elements per 16-byte load
   constexpr int TPR = D / E;               // threads per row
   constexpr int RPP = 256 / TPR;           // rows per pass
@@ -72,6 +101,54 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
       else raw[bb][ps] = *ptr;
     }
   }
+  // element e of 16-byte word w as fp32
+  auto elem = [&](const i32x4_t& wv, int e) -> float {
+    if constexpr (sizeof(T) == 2) {
+      const unsigned u = (unsigned)wv[e / 2];
+      return __uint_as_float(e & 1 ? (u & 0xFFFF0000u) : (u << 16));
+    } else {
+      return __int_as_float(wv[e]);
+    }
+  };
+  if constexpr (Q8) {
+    __shared__ float wmax[POOL_BPW][4];
+    const int lane = t & 63, wave = t >> 6;
+#pragma unroll
+    for (int bb = 0; bb < POOL_BPW; ++bb) {
+      float m = 0.f;
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps)
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(elem(raw[bb][ps], e)));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) wmax[bb][wave] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bb = 0; bb < POOL_BPW; ++bb) {
+      const int i = i0 + bb;
+      if (i >= nb) continue;
+      const float amax = fmaxf(fmaxf(wmax[bb][0], wmax[bb][1]), fmaxf(wmax[bb][2], wmax[bb][3]));
+      const float sc = amax > 0.f ? amax / 448.f : 1.f;
+      uint8_t* cbase = f8.codes[which] + b * f8.sb[which] + h * f8.sh[which];
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        unsigned w[E / 4];
+#pragma unroll
+        for (int x = 0; x < E / 4; ++x) {
+          w[x] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[x] |= encode_e4m3(elem(raw[bb][ps], 4 * x + e) / sc) << (8 * e);
+        }
+        uint8_t* dst = cbase + ((int64_t)i * BSA_N + r0 + ps * RPP) * f8.ss[which] + cg * E;
+        if constexpr (E == 8) *(uint2*)dst = make_uint2(w[0], w[1]);
+        else *(unsigned*)dst = w[0];
+      }
+      if (t == 0) f8.scale[which][(int64_t)bh * nb + i] = sc;
+    }
+  }
+  if constexpr (!POOL) return;
 #pragma unroll
   for (int bb = 0; bb < POOL_BPW; ++bb) {
     double acc[E];
@@ -418,27 +495,39 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
+template <typename T, int D, bool NT>
+static void launch_pool_v(dim3 grid, hipStream_t st, const void* q, const int64_t* qs, const void* k,
+                          const int64_t* ks, int H, int nb, double* qbar, double* kbarT, const Fp8Out* f8) {
+  const Fp8Out none = {};
+  if (!f8)
+    hipLaunchKernelGGL((pool_kernel<T, D, NT, true, false>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1],
+                       qs[2], (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT, none);
+  else if (qbar)
+    hipLaunchKernelGGL((pool_kernel<T, D, NT, true, true>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1],
+                       qs[2], (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT, *f8);
+  else
+    hipLaunchKernelGGL((pool_kernel<T, D, NT, false, true>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1],
+                       qs[2], (const T*)q, qs[0], qs[1], qs[2], H, nb, nullptr, nullptr, *f8);
+}
+
 template <typename T, int D>
 static hipError_t launch_pool_t(const void* q, const int64_t* qs, const void* k, const int64_t* ks, int B,
-                                int H, int nb, double* qbar, double* kbarT, hipStream_t st) {
-  dim3 grid((nb + POOL_BPW - 1) / POOL_BPW, B * H, 2);
+                                int H, int nb, double* qbar, double* kbarT, const Fp8Out* f8, hipStream_t st) {
+  const int tensors = qbar ? 2 : 1;
+  dim3 grid((nb + POOL_BPW - 1) / POOL_BPW, B * H, tensors);
   // inputs far larger than the 256 MB last-level cache are streamed past it
-  const bool nt = 2.0 * B * H * nb * BSA_N * D * sizeof(T) > 512.0 * (1 << 20);
-  if (nt)
-    hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1], qs[2],
-                       (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT);
-  else
-    hipLaunchKernelGGL((pool_kernel<T, D, false>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1], qs[2],
-                       (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT);
+  const bool nt = (double)tensors * B * H * nb * BSA_N * D * sizeof(T) > 512.0 * (1 << 20);
+  if (nt) launch_pool_v<T, D, true>(grid, st, q, qs, k, ks, H, nb, qbar, kbarT, f8);
+  else launch_pool_v<T, D, false>(grid, st, q, qs, k, ks, H, nb, qbar, kbarT, f8);
   return hipGetLastError();
 }
 
 hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* qs, const void* k, const int64_t* ks,
-                       int B, int H, int nb, double* qbar, double* kbarT, hipStream_t st) {
-  if (f32) return D == 64 ? launch_pool_t<float, 64>(q, qs, k, ks, B, H, nb, qbar, kbarT, st)
-                          : launch_pool_t<float, 128>(q, qs, k, ks, B, H, nb, qbar, kbarT, st);
-  return D == 64 ? launch_pool_t<u16, 64>(q, qs, k, ks, B, H, nb, qbar, kbarT, st)
-                 : launch_pool_t<u16, 128>(q, qs, k, ks, B, H, nb, qbar, kbarT, st);
+                       int B, int H, int nb, double* qbar, double* kbarT, const Fp8Out* f8, hipStream_t st) {
+  if (f32) return D == 64 ? launch_pool_t<float, 64>(q, qs, k, ks, B, H, nb, qbar, kbarT, f8, st)
+                          : launch_pool_t<float, 128>(q, qs, k, ks, B, H, nb, qbar, kbarT, f8, st);
+  return D == 64 ? launch_pool_t<u16, 64>(q, qs, k, ks, B, H, nb, qbar, kbarT, f8, st)
+                 : launch_pool_t<u16, 128>(q, qs, k, ks, B, H, nb, qbar, kbarT, f8, st);
 }
 
 template <int NCT>

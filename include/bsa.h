@@ -102,6 +102,31 @@ bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_
                             uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * fp8 e4m3fn block quantisation of Q and K [FA3: block quantisation for FP8
+ * attention; the combined-sweep workload: fp8 e4m3 Q/K with one scale per block].
+ * Per (b, h, 64-token block): scale = amax / 448 over its 64 x D values, computed in
+ * fp32 (1 for an all-zero block); code = e4m3fn(x / scale) with the quotient in fp32,
+ * round to nearest even, saturating at +-448 (OCP e4m3fn: bias 7, 3 mantissa bits,
+ * no infinities). The value of code c of block j is fp8(c) * scale[b,h,j], which is
+ * what block_sparse_attn_fwd takes as q_scale / k_scale.
+ *
+ * quantize_fp8_blocks: x bf16 or f32 [B,H,S,D] -> codes (dtype BSA_FP8_E4M3FN,
+ *   [B,H,S,D], own strides) and scales float [B,H,nb] contiguous. All S rows are
+ *   quantised (zero padding gives code 0).
+ * nabla_build_mask_fp8: nabla_build_mask plus the quantisation of q and k from the
+ *   same read (q8, q_scale, k8, k_scale as codes, scales above); same workspace.
+ * Errors as for nabla_build_mask; BSA_EINVAL for a codes tensor of another dtype or
+ * misaligned scales.
+ * ------------------------------------------------------------------------- */
+bsa_status quantize_fp8_blocks(const bsa_tensor* x, const bsa_shape* shape, const bsa_tensor* codes,
+                               float* scales, bsa_stream_t stream);
+bsa_status nabla_build_mask_fp8(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
+                                double thr, double scale,
+                                const uint8_t* or_mask, int64_t or_sb, int64_t or_sh, uint8_t* mask_out,
+                                const bsa_tensor* q8, float* q_scale, const bsa_tensor* k8, float* k_scale,
+                                void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Static sliding-tile block mask [STA, "Observation & Proposed Method"].
  *
  * The T x H x W latent grid (T*H*W == shape->S_valid) is cut into tiles of

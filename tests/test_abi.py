@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 4
+    assert lib.bsa_abi_version() == 5
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
@@ -132,3 +132,15 @@ def test_backward_rejects_bad_arguments(lib):
     assert _bwd(lib, shape, ws_bytes=16) == 3
     assert _bwd(lib, bsa.Shape(1, 2, 256, 256, 96, 64)) == 2
     assert lib.attn_bwd_workspace_size(ctypes.byref(shape)) > 0
+
+
+def test_fp8_entry_points_reject_bad_arguments(lib):
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    x, codes = _t(), _t(dtype=bsa.BSA_FP8_E4M3FN)
+    assert lib.quantize_fp8_blocks(ctypes.byref(x), ctypes.byref(shape), ctypes.byref(_t()), 4096, None) == 1
+    assert "fp8" in lib.bsa_last_error().decode()
+    assert lib.quantize_fp8_blocks(ctypes.byref(x), ctypes.byref(shape), ctypes.byref(codes), 4098, None) == 1
+    assert lib.quantize_fp8_blocks(ctypes.byref(codes), ctypes.byref(shape), ctypes.byref(codes), 4096, None) == 2
+    st = lib.nabla_build_mask_fp8(ctypes.byref(x), ctypes.byref(x), ctypes.byref(shape), 0.2, 0.0, None, 0, 0, 4096,
+                                  ctypes.byref(codes), None, ctypes.byref(codes), 4096, 8192, 1 << 40, None)
+    assert st == 1 and "scales" in lib.bsa_last_error().decode()
