@@ -49,7 +49,7 @@ def _measured_traffic(workload, fp8=False, dense=False):
 def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     import torch
     import block_sparse_attention_mask_amd as bsa
-    from synth import make_inputs, quantize_fp8_blocks
+    from synth import make_inputs
 
     bsa.load()
     dev = torch.device("cuda:0")
@@ -57,8 +57,11 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     q, k, v = make_inputs(cfg, seed=0, device=dev)
     qa, ka, qs, ks = q, k, None, None
     if fp8:
-        qa, qs = quantize_fp8_blocks(q)
-        ka, ks = quantize_fp8_blocks(k)
+        # fp8 e4m3 Q/K with per-block scales, produced inside each step by the library
+        # (from the mask build's own read of Q and K when there is an adaptive mask)
+        qa, ka = torch.empty(q.shape, dtype=torch.uint8, device=dev), torch.empty(k.shape, dtype=torch.uint8, device=dev)
+        qs = torch.empty(cfg.B, cfg.H, cfg.nb, dtype=torch.float32, device=dev)
+        ks = torch.empty(cfg.B, cfg.H, cfg.nb, dtype=torch.float32, device=dev)
     nb, S = cfg.nb, cfg.S
     use_nabla = (thr is not None) and not dense
     plane = torch.empty(nb, nb, dtype=torch.uint8, device=dev)
@@ -84,12 +87,16 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
             bsa.sta_build_mask(S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
                                order_tile=cfg.order_tile, device=dev, out=plane)
         m = mask
-        if use_nabla:
+        if use_nabla and fp8:
+            bsa.nabla_build_mask_fp8(q, k, thr, or_mask=plane if cfg.sta is not None else None, out=mask,
+                                     q8_out=(qa, qs), k8_out=(ka, ks))
+        elif use_nabla:
             bsa.nabla_build_mask(q, k, thr, or_mask=plane if cfg.sta is not None else None, out=mask)
-        elif dense:
-            m = ones
         else:
-            m = plane
+            m = ones if dense else plane
+            if fp8:
+                bsa.quantize_fp8_blocks(q, out=(qa, qs))
+                bsa.quantize_fp8_blocks(k, out=(ka, ks))
         if ev is not None:
             ev[1].record()
         rp, ci = bsa.mask_to_csr(m, B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
@@ -129,7 +136,7 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     kept = int(rp[-1].item())
     return dict(ms_per_step=ms_total / steps, wall_s=wall, mask_ms=mask_ms, csr_ms=csr_ms, attn_ms=attn_ms,
                 kept_tiles=kept, kept_fraction=kept / (cfg.B * cfg.H * nb * nb), mask=m.cpu() if use_nabla else None,
-                q=q, k=k, v=v)
+                q=q, k=k, v=v, qa=qa, ka=ka, qs=qs, ks=ks)
 
 
 def run_cpu_baseline(cfg, thr, budget_s=15.0):
@@ -282,7 +289,7 @@ def run_sweep(cfg_id, steps, warmup):
     import torch
     import oracle
     import block_sparse_attention_mask_amd as bsa
-    from synth import get_config, make_inputs, quantize_fp8_blocks
+    from synth import get_config, make_inputs
 
     cfg = get_config(cfg_id)
     fpt = _flops_per_tile(cfg.D)
@@ -291,10 +298,6 @@ def run_sweep(cfg_id, steps, warmup):
     blocks = [0, cfg.nb // 2, cfg.nb - 1]                  # includes the partly padded last block
     rows = []
     for fp8 in (False, True):
-        qa, ka, qs, ks = q, k, None, None
-        if fp8:
-            qa, qs = quantize_fp8_blocks(q)
-            ka, ks = quantize_fp8_blocks(k)
         peak = BF16_PEAK_TFLOPS if not fp8 else 4.0 / (2.0 / FP8_PEAK_TFLOPS + 2.0 / BF16_PEAK_TFLOPS)
         dense = run_gpu(cfg, steps, warmup, None, dense=True, fp8=fp8)
         dense_tf = dense["kept_tiles"] * fpt / (dense["attn_ms"] * 1e-3) / 1e12
@@ -305,6 +308,7 @@ def run_sweep(cfg_id, steps, warmup):
                      "sampled_kept_blocks": None, "max_sparsify_err": None})
         for thr in cfg.thrs:
             r = run_gpu(cfg, steps, warmup, thr, fp8=fp8)
+            qa, ka, qs, ks = r["qa"], r["ka"], r["qs"], r["ks"]      # the step's own fp8 codes (or bf16 q, k)
             tf = r["kept_tiles"] * fpt / (r["attn_ms"] * 1e-3) / 1e12
             # error of sampled query blocks against the fp64 oracle, with the GPU's mask
             mask = r["mask"].to("cuda:0")
