@@ -46,7 +46,7 @@ def _measured_traffic(workload, fp8=False, dense=False):
     return rec["traffic_bytes_per_launch"].get(workload)
 
 
-def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
+def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
     import torch
     import block_sparse_attention_mask_amd as bsa
     from synth import make_inputs
@@ -112,6 +112,24 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if graph:
+        # one step captured as a HIP graph (the library allocates nothing, never syncs
+        # and records no memset), replayed once per timed step: the kernels and their
+        # order are the eager step's, without the host's per-launch overhead
+        ref = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            m_g, rp_g = step()
+
+        def run():
+            g.replay()
+            return m_g, rp_g
     # timed region: whole steps back to back, events only at its two ends
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
@@ -119,11 +137,13 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False):
     t0 = time.perf_counter()
     t_all0.record()
     for s in range(steps):
-        m, rp = step()
+        m, rp = run()
     t_all1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = t_all0.elapsed_time(t_all1)
+    if graph and not torch.equal(out, ref):
+        raise RuntimeError("graph replay output differs from the eager step")
     # phase breakdown in a second pass of the same steps, with events between the phases
     # (each event adds a few microseconds of its own, so it is kept out of the timed region)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -363,6 +383,8 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
     ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replaying the step as a HIP graph")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv) of the config instead of the forward step")
     ap.add_argument("--sweep", action="store_true",
@@ -397,7 +419,7 @@ def main():
     from synth import get_config
     cfg = get_config(args.config)
     thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
-    r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8)
+    r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=not args.no_graph)
     fpt = _flops_per_tile(cfg.D)
     kept_flops = r["kept_tiles"] * fpt
     attn_tflops = kept_flops / (r["attn_ms"] * 1e-3) / 1e12
@@ -418,7 +440,8 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S, "S_valid": cfg.S_valid, "D": cfg.D,
                    "grid": list(cfg.grid), "token_order": cfg.order, "thr": thr,
                    "sta": None if cfg.sta is None else {"tile": list(cfg.sta.tile), "window": list(cfg.sta.window)},
-                   "dense": args.dense, "fp8_qk": args.fp8},
+                   "dense": args.dense, "fp8_qk": args.fp8,
+                   "launch": "eager" if args.no_graph else "hip_graph"},
         "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
         "attn_tflops": round(attn_tflops, 2), "attn_frac_bf16_peak": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
         "mask_build_gbps": round(mask_bytes / (r["mask_ms"] * 1e-3) / 1e9, 1) if thr is not None else None,
