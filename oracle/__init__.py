@@ -13,6 +13,7 @@ pages by eye:
   attention_bwd.py  its gradients dQ, dK, dV (plain derivative of the same definition)
   csr.py        union of masks and the per-query-block kv index lists
   fp8.py        e4m3fn encoding and per-block fp8 quantisation of Q and K
+  reorder.py    token orders (tile-major / fractal flattening, spatial-major) and reordering
 
 Pins: every function is checked by `tests/test_oracle_*.py` against closed forms,
 brute force, textbook identities or library routines (see those files).
@@ -23,9 +24,10 @@ from .attention import block_sparse_attention
 from .attention_bwd import block_sparse_attention_bwd
 from .csr import mask_or, mask_to_csr, longest_first_order
 from .fp8 import decode_e4m3fn, encode_e4m3fn, quantize_blocks
+from .reorder import order_coords, reorder_tokens
 
 __all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask",
            "nabla_masks", "sta_block_mask", "sta_token_mask", "block_sparse_attention",
            "block_sparse_attention_bwd",
            "mask_or", "mask_to_csr", "longest_first_order", "decode_e4m3fn", "encode_e4m3fn",
-           "quantize_blocks"]
+           "quantize_blocks", "order_coords", "reorder_tokens"]
