@@ -298,6 +298,48 @@ def run_cpu_baseline_bwd(cfg, keep0, budget_s=15.0):
                       f"4 products per kept tile)"}
 
 
+def run_reorder(cfg, steps, warmup):
+    """Token reordering of Q at the config's shape: row-major -> tile-major (the config's
+    sliding tile, else 4 x 8 x 8) and back; HBM roofline (every row read and written once)."""
+    import torch
+    import block_sparse_attention_mask_amd as bsa
+    from synth import make_inputs
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    q, _, _ = make_inputs(cfg, seed=0, device=dev)
+    tile = cfg.sta.tile if cfg.sta is not None else (4, 8, 8)
+    y = torch.empty_like(q)
+    z = torch.empty_like(q)
+    res = {}
+    for name, fn in (("forward", lambda: bsa.token_reorder(q, cfg.grid, "tile", tile, out=y)),
+                     ("inverse", lambda: bsa.token_reorder(y, cfg.grid, "tile", tile, inverse=True, out=z))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    if not torch.equal(z[:, :, :cfg.S_valid], q[:, :, :cfg.S_valid]):
+        raise RuntimeError("reorder round trip failed")
+    nbytes = 2 * q.numel() * q.element_size()
+    gbps = nbytes / (res["forward"] * 1e-3) / 1e9
+    print(json.dumps({"metric": "token reorder GB/s (read + write of every row)", "value": round(gbps, 1),
+                      "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+                      "ms_per_step": round(res["forward"], 4), "higher_is_better": True, "scaling": "weak",
+                      "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": cfg.name, "grid": list(cfg.grid), "tile": list(tile), "B": cfg.B,
+                                 "H": cfg.H, "S": cfg.S, "D": cfg.D},
+                      "inverse_ms": round(res["inverse"], 4),
+                      "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                                   "kernel": "token_reorder_kernel", "per_launch_bytes": nbytes}}), flush=True)
+
+
 def run_sweep(cfg_id, steps, warmup):
     """Threshold sweep (the combined-sweep workload): for each thr, with bf16 and with fp8
     Q/K, the kept fraction, step and attention time, effective TFLOP/s over kept tiles,
@@ -385,6 +427,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replaying the step as a HIP graph")
+    ap.add_argument("--reorder", action="store_true",
+                    help="time the token reordering (row-major -> tile-major and back) at the config's shape")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv) of the config instead of the forward step")
     ap.add_argument("--sweep", action="store_true",
@@ -409,6 +453,10 @@ def main():
 
     if args.sweep:
         run_sweep(args.config if args.config != 2 else 5, min(args.steps, 5), min(args.warmup, 2))
+        return
+    if args.reorder:
+        from synth import get_config
+        run_reorder(get_config(args.config), args.steps, args.warmup)
         return
     if args.backward:
         from synth import get_config

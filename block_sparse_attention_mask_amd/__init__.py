@@ -25,7 +25,8 @@ EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "quantize_fp8_blocks", "n
            "sta_workspace_size", "sta_build_mask", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "attn_workspace_size", "block_sparse_attn_fwd",
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
-           "attn_bwd_workspace_size", "block_sparse_attn_bwd", "bsa_last_error", "bsa_abi_version"]
+           "attn_bwd_workspace_size", "block_sparse_attn_bwd", "token_reorder", "bsa_last_error",
+           "bsa_abi_version"]
 
 
 class BsaError(RuntimeError):
@@ -77,6 +78,7 @@ def load(path: Optional[str] = None):
         "attn_work_order_slots": (i32, [PS]),
         "attn_work_order": (i32, [PS, vp, vp, vp]),
         "attn_bwd_workspace_size": (sz, [PS]),
+        "token_reorder": (i32, [PT, PS, i3, i32, i3, i32, PT, vp]),
         "block_sparse_attn_bwd": (i32, [PT, PT, PT, PT, PT, vp, PS, vp, i64, i64, dbl, PT, PT, PT, vp, sz, vp]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_abi_version": (i32, []),
@@ -366,4 +368,24 @@ def block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
                                      ptr, sb, sh, float(scale) if scale else 0.0,
                                      *(ctypes.byref(x) for x in t[5:]), ws.data_ptr(), ws.numel(),
                                      _stream(q.device)))
+    return out
+
+
+ORDER_CODES = {"row": 0, "tile": 1, "spatial": 2}
+
+
+def token_reorder(x: torch.Tensor, grid: Sequence[int], order: str, tile: Optional[Sequence[int]] = None,
+                  inverse: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Permute the T*H*W token rows of x [B,H,S,D] from row-major (t, h, w) to `order`
+    ("tile" with `tile`, e.g. (1, P, P) for fractal flattening; "spatial"; "row"), or
+    back with inverse=True. Rows >= T*H*W of the result are zero."""
+    lib = load()
+    if out is None:
+        out = torch.empty_like(x)
+    shp = _shape(x, int(grid[0]) * int(grid[1]) * int(grid[2]))
+    a3 = ctypes.c_int * 3
+    t = a3(*tile) if tile is not None else None
+    tx, to = _tensor(x), _tensor(out)
+    _check(lib.token_reorder(ctypes.byref(tx), ctypes.byref(shp), a3(*grid), ORDER_CODES[order], t, int(inverse),
+                             ctypes.byref(to), _stream(x.device)))
     return out

@@ -10,7 +10,7 @@ import time
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["nabla.hip", "sta.hip", "mask_ops.hip", "attn.hip", "attn_bwd.hip", "api.cpp"]
+SOURCES = ["nabla.hip", "sta.hip", "mask_ops.hip", "attn.hip", "attn_bwd.hip", "reorder.hip", "api.cpp"]
 LIB = os.path.join(PKG, "libbsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 5; }
+int bsa_abi_version(void) { return 6; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -220,6 +220,39 @@ bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const i
   g.S_valid = shape->S_valid;
   g.nb = shape->S / 64;
   return hip_status(bsa::launch_sta(g, (int32_t*)ws, mask_out, (hipStream_t)stream), "sta launch");
+}
+
+// ---------------------------------------------------------------------------
+bsa_status token_reorder(const bsa_tensor* x, const bsa_shape* shape, const int grid_thw[3], int order,
+                         const int tile_thw[3], int inverse, const bsa_tensor* out, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  if ((st = check_tensor("x", x, shape)) != BSA_OK) return st;
+  if ((st = check_tensor("out", out, shape)) != BSA_OK) return st;
+  if (x->dtype != out->dtype) return fail(BSA_EINVAL, "x and out must have the same dtype");
+  if (x->ptr == out->ptr) return fail(BSA_EINVAL, "token_reorder does not work in place");
+  if (!grid_thw) return fail(BSA_EINVAL, "grid_thw is NULL");
+  if (order != BSA_ORDER_ROW && order != BSA_ORDER_TILE && order != BSA_ORDER_SPATIAL)
+    return fail(BSA_EINVAL, "order=%d (0 row-major, 1 tile-major, 2 spatial-major)", order);
+  if (order == BSA_ORDER_TILE && !tile_thw) return fail(BSA_EINVAL, "tile_thw is NULL for the tile-major order");
+  for (int d = 0; d < 3; ++d) {
+    if (grid_thw[d] < 1) return fail(BSA_EINVAL, "grid sizes must be >= 1");
+    if (order == BSA_ORDER_TILE && tile_thw[d] < 1) return fail(BSA_EINVAL, "tile sizes must be >= 1");
+  }
+  if ((int64_t)grid_thw[0] * grid_thw[1] * grid_thw[2] != shape->S_valid)
+    return fail(BSA_EINVAL, "T*H*W must equal S_valid=%d", shape->S_valid);
+  bsa::ReorderGeom g;
+  g.T = grid_thw[0]; g.H = grid_thw[1]; g.W = grid_thw[2];
+  g.tt = order == BSA_ORDER_TILE ? tile_thw[0] : 1;
+  g.th = order == BSA_ORDER_TILE ? tile_thw[1] : 1;
+  g.tw = order == BSA_ORDER_TILE ? tile_thw[2] : 1;
+  g.order = order;
+  const int64_t es = (int64_t)dtype_size(x->dtype);
+  const int64_t xs[3] = {x->sb * es, x->sh * es, x->ss * es}, os[3] = {out->sb * es, out->sh * es, out->ss * es};
+  return hip_status(bsa::launch_token_reorder(x->ptr, xs, (void*)out->ptr, os, shape->B, shape->H, shape->S,
+                                              (int)(shape->D * es), g, inverse != 0, (hipStream_t)stream),
+                    "reorder launch");
 }
 
 // ---------------------------------------------------------------------------

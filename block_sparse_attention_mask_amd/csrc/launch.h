@@ -53,6 +53,18 @@ bool pair_schedule_fits(int BH, int nb);
 int pair_schedule_slots(int BH, int nb);   // entries of the order = workgroups to launch
 hipError_t launch_pair_schedule(const int32_t* row_ptr, int BH, int nb, int32_t* order, hipStream_t st);
 
+// reorder.hip
+constexpr int ORDER_ROW = 0, ORDER_TILE = 1, ORDER_SPATIAL = 2;
+struct ReorderGeom {
+  int T, H, W;       // latent grid
+  int tt, th, tw;    // tile of ORDER_TILE
+  int order;
+};
+// dst = src reordered (inverse: back to row-major); strides in bytes; row_bytes in {64, 128, 256, 512}
+hipError_t launch_token_reorder(const void* src, const int64_t* s_strides_bytes, void* dst,
+                                const int64_t* d_strides_bytes, int B, int H, int S, int row_bytes,
+                                const ReorderGeom& g, bool inverse, hipStream_t st);
+
 // attn.hip
 struct AttnArgs {
   const void* q; int64_t q_sb, q_sh, q_ss;

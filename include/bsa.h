@@ -263,6 +263,28 @@ bsa_status block_sparse_attn_bwd(const bsa_tensor* q, const bsa_tensor* k, const
                                  const bsa_tensor* dq, const bsa_tensor* dk, const bsa_tensor* dv,
                                  void* ws, size_t ws_bytes, bsa_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Token reordering [NABLA review, Figure 4 and "Assumptions & free parameters":
+ * fractal flattening into P x P spatial patches; STA: tokens grouped into 3D tiles;
+ * SVG: layout transformation grouping one spatial position across frames]. The
+ * T*H*W token rows of x [B,H,S,D] are permuted between the row-major (t, h, w) order
+ * and one of:
+ *   BSA_ORDER_TILE     tiles of tile_thw in row-major tile order, tokens row-major
+ *                      inside a tile, smaller tiles at the grid border (fractal
+ *                      flattening with patch P is tile_thw = {1, P, P});
+ *   BSA_ORDER_SPATIAL  (h, w, t): the frames of one spatial position together;
+ *   BSA_ORDER_ROW      the identity (a copy).
+ * inverse = 0: out = x (row-major) in the chosen order; inverse = 1: x is in the
+ * chosen order and out is row-major (the scatter back of the attention output).
+ * Rows >= S_valid of out are written as zeros. x and out: same dtype (bf16, f32 or
+ * fp8 codes), own strides, distinct buffers; S_valid = T*H*W. Errors: BSA_EINVAL.
+ * ------------------------------------------------------------------------- */
+#define BSA_ORDER_ROW 0
+#define BSA_ORDER_TILE 1
+#define BSA_ORDER_SPATIAL 2
+bsa_status token_reorder(const bsa_tensor* x, const bsa_shape* shape, const int grid_thw[3], int order,
+                         const int tile_thw[3], int inverse, const bsa_tensor* out, bsa_stream_t stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* bsa_last_error(void);
 
