@@ -7,7 +7,8 @@ reordered beyond the definitions it cites, so each step can be checked against t
 pages by eye:
 
   nabla.py      adaptive block mask: block pooling, reduced map, row softmax,
-                descending sort, exclusive cumulative mass, threshold at 1 - thr
+                descending sort, exclusive cumulative mass, threshold at 1 - thr;
+                the Top-k alternative (fixed count per row) on the same map
   sta.py        static sliding-tile block mask (tile window, clipped at borders)
   attention.py  softmax attention restricted to the kept N x N blocks
   attention_bwd.py  its gradients dQ, dK, dV (plain derivative of the same definition)
@@ -18,7 +19,7 @@ pages by eye:
 Pins: every function is checked by `tests/test_oracle_*.py` against closed forms,
 brute force, textbook identities or library routines (see those files).
 """
-from .nabla import block_pool, reduced_map, row_softmax, cdf_select, nabla_mask, nabla_masks
+from .nabla import block_pool, reduced_map, row_softmax, cdf_select, nabla_mask, nabla_masks, topk_select, topk_mask
 from .sta import sta_block_mask, sta_token_mask
 from .attention import block_sparse_attention
 from .attention_bwd import block_sparse_attention_bwd
@@ -26,7 +27,7 @@ from .csr import mask_or, mask_to_csr, longest_first_order
 from .fp8 import decode_e4m3fn, encode_e4m3fn, quantize_blocks
 from .reorder import order_coords, reorder_tokens
 
-__all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask",
+__all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask", "topk_select", "topk_mask",
            "nabla_masks", "sta_block_mask", "sta_token_mask", "block_sparse_attention",
            "block_sparse_attention_bwd",
            "mask_or", "mask_to_csr", "longest_first_order", "decode_e4m3fn", "encode_e4m3fn",

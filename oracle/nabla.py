@@ -62,6 +62,30 @@ def cdf_select(P: np.ndarray, thr: float):
     return keep, E
 
 
+def topk_select(P: np.ndarray, topk: int) -> np.ndarray:
+    """The fixed-count alternative the NABLA review compares CDF thresholding with
+    (Appendix C, Theorem 1: CDF vs Top-k at equal retained blocks): keep the topk
+    entries of each row in the same descending order (ties by ascending index)."""
+    rows, nb = P.shape
+    col = np.broadcast_to(np.arange(nb), P.shape)
+    order = np.lexsort((col, -P), axis=1)
+    keep_sorted = np.zeros((rows, nb), dtype=bool)
+    keep_sorted[:, :min(int(topk), nb)] = True
+    keep = np.zeros((rows, nb), dtype=bool)
+    np.put_along_axis(keep, order, keep_sorted, axis=1)
+    return keep
+
+
+def topk_mask(q: np.ndarray, k: np.ndarray, n: int, topk: int, scale=None):
+    """One head: the reduced map of `nabla_mask`, rows cut to their topk largest entries."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[1])
+    P = row_softmax(reduced_map(block_pool(q, n), block_pool(k, n), scale))
+    return topk_select(P, topk), P
+
+
 def nabla_mask(q: np.ndarray, k: np.ndarray, n: int, thr: float, scale=None):
     """One head: q, k [S, D] -> (keep bool [nb, nb], E [nb, nb], P [nb, nb])."""
     q = np.asarray(q, dtype=np.float64)

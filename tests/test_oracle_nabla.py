@@ -181,3 +181,35 @@ def test_multi_head_matches_single_head():
         for h in range(3):
             kk, ee, _ = oracle.nabla_mask(q[b, h], k[b, h], 64, 0.2)
             assert np.array_equal(kk, keep[b, h]) and np.array_equal(ee, E[b, h])
+
+
+# ----------------------------------------------------------------------------- Top-k
+def test_topk_brute_force_and_count():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        nb = int(rng.integers(1, 10))
+        P = rng.dirichlet(np.ones(nb), size=3)
+        P[0, : nb // 2] = P[0, 0]                     # a tie group
+        P /= P.sum(1, keepdims=True)
+        for kk in range(0, nb + 2):
+            keep = oracle.topk_select(P, kk)
+            assert np.all(keep.sum(1) == min(kk, nb))
+            for r in range(3):
+                if keep[r].any() and (~keep[r]).any():
+                    assert P[r][keep[r]].min() >= P[r][~keep[r]].max()
+                # among equal values the lower indices are kept first
+                for j in range(nb):
+                    for j2 in range(j + 1, nb):
+                        if P[r, j] == P[r, j2]:
+                            assert not (keep[r, j2] and not keep[r, j])
+
+
+def test_topk_equals_cdf_mask_at_the_cdf_count():
+    # CDF keeps a prefix of the same descending order, so each row equals Top-k with k = its kept count
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((512, 32))
+    k = q + 0.5 * rng.standard_normal((512, 32))
+    for thr in (0.05, 0.2, 0.6):
+        keep, _, P = oracle.nabla_mask(q, k, 64, thr)
+        for i in range(P.shape[0]):
+            assert np.array_equal(oracle.topk_select(P[i:i + 1], int(keep[i].sum()))[0], keep[i])
