@@ -21,7 +21,8 @@ BSA_F32, BSA_BF16, BSA_FP8_E4M3FN = 0, 1, 2
 _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPACE", 4: "BSA_EHIP"}
 
 # every function the C header declares, in declaration order
-EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "quantize_fp8_blocks", "nabla_build_mask_fp8",
+EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_topk", "quantize_fp8_blocks",
+           "nabla_build_mask_fp8",
            "sta_workspace_size", "sta_build_mask", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "attn_workspace_size", "block_sparse_attn_fwd",
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
@@ -64,6 +65,7 @@ def load(path: Optional[str] = None):
     sig = {
         "nabla_workspace_size": (sz, [PS]),
         "nabla_build_mask": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, sz, vp]),
+        "nabla_build_mask_topk": (i32, [PT, PT, PS, i32, dbl, vp, i64, i64, vp, vp, sz, vp]),
         "quantize_fp8_blocks": (i32, [PT, PS, PT, vp, vp]),
         "nabla_build_mask_fp8": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, PT, vp, PT, vp, vp, sz, vp]),
         "sta_workspace_size": (sz, [PS]),
@@ -154,6 +156,26 @@ def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Option
     _check(lib.nabla_build_mask(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
                                 float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(), ws.data_ptr(),
                                 ws.numel(), _stream(q.device)))
+    return out
+
+
+def nabla_build_mask_topk(q: torch.Tensor, k: torch.Tensor, topk: int, scale: Optional[float] = None,
+                          or_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k block mask on NABLA's reduced map: each row keeps its topk most probable blocks."""
+    lib = load()
+    B, H, S, D = q.shape
+    nb = S // 64
+    shp = _shape(q, None)
+    if out is None:
+        out = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device)
+    ws = _ws(lib.nabla_workspace_size(ctypes.byref(shp)), q.device)
+    om, osb, osh = None, 0, 0
+    if or_mask is not None:
+        om, osb, osh, _keep = _mask_strides(or_mask)
+    tq, tk = _tensor(q), _tensor(k)
+    _check(lib.nabla_build_mask_topk(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), int(topk),
+                                     float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(), ws.data_ptr(),
+                                     ws.numel(), _stream(q.device)))
     return out
 
 

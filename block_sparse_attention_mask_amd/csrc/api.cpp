@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 6; }
+int bsa_abi_version(void) { return 7; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -92,7 +92,7 @@ size_t nabla_workspace_size(const bsa_shape* s) {
 static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                                uint8_t* mask_out, const bsa::Fp8Out* f8, void* ws, size_t ws_bytes,
-                               bsa_stream_t stream) {
+                               bsa_stream_t stream, int topk = 0) {
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
   if ((st = check_tensor("q", q, shape)) != BSA_OK) return st;
@@ -119,8 +119,8 @@ static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const b
                                   qbar, kbarT, f8, hs);
   if (e != hipSuccess) return hip_status(e, "pool launch");
   const uint64_t T_fixed = (uint64_t)std::ldexp(1.0 - thr, 60);
-  e = bsa::launch_select(qbar, kbarT, shape->B, shape->H, nb, shape->D, scale, T_fixed, or_mask, or_sb, or_sh,
-                         mask_out, hs);
+  e = bsa::launch_select(qbar, kbarT, shape->B, shape->H, nb, shape->D, scale, T_fixed, topk, or_mask, or_sb,
+                         or_sh, mask_out, hs);
   return hip_status(e, "select launch");
 }
 
@@ -150,6 +150,14 @@ static bsa::Fp8Out fp8_out(const bsa_tensor* c0, float* s0, const bsa_tensor* c1
     f.scale[x] = sc[x];
   }
   return f;
+}
+
+bsa_status nabla_build_mask_topk(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, int topk,
+                                 double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                                 uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  if (topk < 1) return fail(BSA_EINVAL, "topk=%d must be >= 1", topk);
+  return nabla_common(q, k, shape, 0.0, scale, or_mask, or_sb, or_sh, mask_out, nullptr, ws, ws_bytes, stream, topk);
 }
 
 bsa_status nabla_build_mask_fp8(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,

@@ -20,8 +20,10 @@ struct Fp8Out {
 hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* q_strides, const void* k,
                        const int64_t* k_strides, int B, int H, int nb, double* qbar, double* kbarT,
                        const Fp8Out* f8, hipStream_t st);
+// T_fixed = floor((1 - thr) 2^60) for the cumulative-mass rule; topk > 0 keeps the
+// topk largest entries of each row instead (T_fixed unused)
 hipError_t launch_select(const double* qbar, const double* kbarT, int B, int H, int nb, int D, double scale,
-                         uint64_t T_fixed, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                         uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                          uint8_t* mask_out, hipStream_t st);
 
 // sta.hip

@@ -194,7 +194,7 @@ enum : int { ROW_ACTIVE = 0, ROW_PIVOT = 1, ROW_ALL = 2, ROW_TIE = 3, ROW_SKIP =
 
 struct SelRowState {
   uint64_t lo;         // current key range [lo, lo + 2^span)
-  uint64_t mass_above; // fixed-point mass of all keys above the range
+  uint64_t mass_above; // fixed-point mass (Top-k: number) of all keys above the range
   int span;            // bits of the range (-1 before the exponent pass)
   int status;
   int cnt;             // candidates in the range
@@ -236,12 +236,17 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 // tiles); wave w owns column tiles w, w + SEL_WAVES, ... (NCT of them). In the
 // result layout lane l holds rows {4v + l/16 : v = 0..3} of column 16*tile + l%16,
 // so a row lives in one 16-lane group of every wave.
+// topk > 0 selects the Top-k alternative (NABLA review, Appendix C: a fixed number of
+// blocks per row): the same descending order, the radix passes search the key at which
+// the COUNT of entries reaches topk instead of the mass reaching 1 - thr.
 template <int NCT, int KS>   // KS = D / 4 k-steps of the f64 MFMA
 __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __restrict__ qmf,
                                                                const double* __restrict__ kmf, int nb, int D,
-                                                               double scale, uint64_t T_fixed,
+                                                               double scale, uint64_t T_fixed, int topk,
                                                                const uint8_t* __restrict__ or_mask, int64_t or_sb,
                                                                int64_t or_sh, int H, uint8_t* __restrict__ mask_out) {
+  const bool by_count = topk > 0;
+  const uint64_t target = by_count ? (uint64_t)topk : T_fixed;
   __shared__ uint64_t hmass[SEL_ROWS][256];
   __shared__ uint32_t hcnt[SEL_ROWS][256];
   __shared__ uint32_t tiebits[SEL_ROWS][64];
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
     n.cnt = 0;
     n.tie_keep = 0;
     if (row0 + r >= nb) n.status = ROW_SKIP;
-    else if (total < T_fixed) n.status = ROW_ALL;   // every entry is reached before the mass 1 - thr
+    else if (by_count ? nb <= topk : total < T_fixed) n.status = ROW_ALL;   // every entry is kept
     else n.status = ROW_ACTIVE;
     st[r] = n;
   }
@@ -391,20 +396,20 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
       uint64_t lt = 0;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        mb[x] = hmass[r][255 - 4 * l - x];
         cb[x] = hcnt[r][255 - 4 * l - x];
+        mb[x] = by_count ? (uint64_t)cb[x] : hmass[r][255 - 4 * l - x];   // what the target counts
         lt += mb[x];
       }
       const uint64_t incl = wave_incl_scan_u64(lt);
       const uint64_t before = sr.mass_above + (incl - lt);
-      const uint64_t ball = __ballot(before + lt >= T_fixed);
+      const uint64_t ball = __ballot(before + lt >= target);
       const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
       if (l == L) {
         uint64_t cum = before;
         int xs = 3;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          if (cum + mb[x] >= T_fixed) { xs = x; break; }
+          if (cum + mb[x] >= target) { xs = x; break; }
           cum += mb[x];
         }
         const int dg = 255 - 4 * l - xs;
@@ -420,9 +425,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
         }
         if (n.cnt <= 1) n.status = ROW_PIVOT;
         else if (n.span == 0) {
-          // identical keys: visited by ascending index, each adds the same mass
-          const uint64_t wq = n.lo;
-          const uint64_t need = T_fixed - n.mass_above;          // > 0
+          // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
+          const uint64_t wq = by_count ? 1 : n.lo;
+          const uint64_t need = target - n.mass_above;           // > 0
           const uint64_t t = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
           n.tie_keep = (int)(t < (uint64_t)n.cnt ? t : (uint64_t)n.cnt);
           n.status = ROW_TIE;
@@ -532,25 +537,25 @@ hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* qs, const 
 
 template <int NCT>
 static hipError_t launch_select_c(const double* qmf, const double* kmf, int B, int H, int nb, int D,
-                                  double scale, uint64_t T_fixed, const uint8_t* or_mask, int64_t or_sb,
+                                  double scale, uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb,
                                   int64_t or_sh, uint8_t* mask_out, hipStream_t st) {
   dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS, B * H);
   if (D == 64)
     hipLaunchKernelGGL((select_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
-                       or_mask, or_sb, or_sh, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, H, mask_out);
   else
     hipLaunchKernelGGL((select_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
-                       or_mask, or_sb, or_sh, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, H, mask_out);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
-                         uint64_t T_fixed, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                         uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                          uint8_t* mask_out, hipStream_t st) {
   const int ntile = (nb + 15) / 16;
   const int nct = (ntile + SEL_WAVES - 1) / SEL_WAVES;
 #define BSA_SEL_CASE(n) \
-  case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, or_mask, or_sb, or_sh, mask_out, st);
+  case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, mask_out, st);
   switch (nct) {
     BSA_SEL_CASE(1) BSA_SEL_CASE(2) BSA_SEL_CASE(3) BSA_SEL_CASE(4) BSA_SEL_CASE(5) BSA_SEL_CASE(6)
     BSA_SEL_CASE(7) BSA_SEL_CASE(8) BSA_SEL_CASE(9) BSA_SEL_CASE(10) BSA_SEL_CASE(11) BSA_SEL_CASE(12)

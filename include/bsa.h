@@ -102,6 +102,20 @@ bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_
                             uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Top-k block selection [NABLA review, Appendix C / Theorem 1: the fixed-count
+ * alternative that CDF thresholding is compared with at equal retained blocks].
+ * The same reduced map and row softmax as nabla_build_mask; each row keeps its topk
+ * largest entries in the same descending order (equal probabilities by ascending
+ * block index, entries closer than 2^-60 counting as equal), then the optional OR.
+ * Rows with nb <= topk keep every block. topk >= 1 (else BSA_EINVAL); other
+ * arguments, workspace and errors as for nabla_build_mask.
+ * ------------------------------------------------------------------------- */
+bsa_status nabla_build_mask_topk(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
+                                 int topk, double scale,
+                                 const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                                 uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * fp8 e4m3fn block quantisation of Q and K [FA3: block quantisation for FP8
  * attention; the combined-sweep workload: fp8 e4m3 Q/K with one scale per block].
  * Per (b, h, 64-token block): scale = amax / 448 over its 64 x D values, computed in

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 6
+    assert lib.bsa_abi_version() == 7
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
@@ -144,3 +144,11 @@ def test_fp8_entry_points_reject_bad_arguments(lib):
     st = lib.nabla_build_mask_fp8(ctypes.byref(x), ctypes.byref(x), ctypes.byref(shape), 0.2, 0.0, None, 0, 0, 4096,
                                   ctypes.byref(codes), None, ctypes.byref(codes), 4096, 8192, 1 << 40, None)
     assert st == 1 and "scales" in lib.bsa_last_error().decode()
+
+
+def test_topk_rejects_bad_arguments(lib):
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    q = _t()
+    st = lib.nabla_build_mask_topk(ctypes.byref(q), ctypes.byref(q), ctypes.byref(shape), 0, 0.0, None, 0, 0, 4096,
+                                   8192, 1 << 40, None)
+    assert st == 1 and "topk" in lib.bsa_last_error().decode()
