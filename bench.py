@@ -340,6 +340,59 @@ def run_reorder(cfg, steps, warmup):
                                    "kernel": "token_reorder_kernel", "per_launch_bytes": nbytes}}), flush=True)
 
 
+def run_topk_compare(cfg, steps, warmup, thr):
+    """CDF thresholding vs Top-k at equal average retained blocks (the comparison of the
+    NABLA review's Appendix C): k = the CDF mask's mean kept count per row. For each
+    scorer: mask-build time, kept fraction, attention time, and the L1 distance of
+    sampled query blocks' attention output from dense attention (fp64 oracle)."""
+    import numpy as np
+    import torch
+    import oracle
+    import block_sparse_attention_mask_amd as bsa
+    from synth import make_inputs
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    q, k, v = make_inputs(cfg, seed=0, device=dev)
+    cdf = bsa.nabla_build_mask(q, k, thr)
+    kk = int(round(cdf.float().sum(-1).mean().item()))
+    builders = {"cdf": lambda: bsa.nabla_build_mask(q, k, thr, out=cdf),
+                "topk": lambda: bsa.nabla_build_mask_topk(q, k, kk)}
+    heads, blocks = [0, cfg.H - 1], [0, cfg.nb // 3, 2 * cfg.nb // 3]
+    dense = {}
+    for h in heads:
+        qd, kd, vd = (x[0, h].double().cpu().numpy() for x in (q, k, v))
+        dense[h] = oracle.block_sparse_attention(qd, kd, vd, np.ones((cfg.nb, cfg.nb), bool), 64, cfg.S_valid,
+                                                 q_blocks=blocks)[0]
+    for name, build in builders.items():
+        for _ in range(warmup):
+            m = build()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        for _ in range(steps):
+            m = build()
+        e[1].record()
+        for _ in range(steps):
+            bsa.block_sparse_attn_fwd(q, k, v, m, s_valid=cfg.S_valid)
+        e[2].record()
+        torch.cuda.synchronize()
+        mask_ms, attn_ms = e[0].elapsed_time(e[1]) / steps, e[1].elapsed_time(e[2]) / steps
+        mk = m.cpu().numpy().astype(bool)
+        l1 = []
+        for h in heads:
+            qd, kd, vd = (x[0, h].double().cpu().numpy() for x in (q, k, v))
+            O = oracle.block_sparse_attention(qd, kd, vd, mk[0, h], 64, cfg.S_valid, q_blocks=blocks)[0]
+            rows = np.concatenate([np.arange(i * 64, min((i + 1) * 64, cfg.S_valid)) for i in blocks])
+            l1.append(np.abs(O[rows] - dense[h][rows]).sum(axis=1).mean())
+        kept = int(mk.sum())
+        print(json.dumps({"compare": "cdf_vs_topk", "workload": cfg.name, "scorer": name, "thr": thr, "topk": kk,
+                          "kept_fraction": round(kept / mk.size, 5), "mask_ms": round(mask_ms, 4),
+                          "attn_ms": round(attn_ms, 4),
+                          "attn_tflops": round(kept * _flops_per_tile(cfg.D) / (attn_ms * 1e-3) / 1e12, 1),
+                          "mean_row_l1_vs_dense": float(np.mean(l1))}), flush=True)
+
+
 def run_sweep(cfg_id, steps, warmup):
     """Threshold sweep (the combined-sweep workload): for each thr, with bf16 and with fp8
     Q/K, the kept fraction, step and attention time, effective TFLOP/s over kept tiles,
@@ -427,6 +480,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replaying the step as a HIP graph")
+    ap.add_argument("--topk-compare", action="store_true",
+                    help="CDF vs Top-k masks at equal average kept blocks (default config 3)")
     ap.add_argument("--reorder", action="store_true",
                     help="time the token reordering (row-major -> tile-major and back) at the config's shape")
     ap.add_argument("--backward", action="store_true",
@@ -453,6 +508,11 @@ def main():
 
     if args.sweep:
         run_sweep(args.config if args.config != 2 else 5, min(args.steps, 5), min(args.warmup, 2))
+        return
+    if args.topk_compare:
+        from synth import get_config
+        cfg = get_config(args.config if args.config != 2 else 3)
+        run_topk_compare(cfg, min(args.steps, 5), min(args.warmup, 2), args.thr or cfg.thrs[0])
         return
     if args.reorder:
         from synth import get_config
