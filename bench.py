@@ -150,11 +150,13 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
     for s in range(steps):
         step(evs[s])
     torch.cuda.synchronize()
+    per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
     mask_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     csr_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
     kept = int(rp[-1].item())
     return dict(ms_per_step=ms_total / steps, wall_s=wall, mask_ms=mask_ms, csr_ms=csr_ms, attn_ms=attn_ms,
+                step_ms_median=per_step[len(per_step) // 2], step_ms_min=per_step[0],
                 kept_tiles=kept, kept_fraction=kept / (cfg.B * cfg.H * nb * nb), mask=m.cpu() if use_nabla else None,
                 q=q, k=k, v=v, qa=qa, ka=ka, qs=qs, ks=ks)
 
@@ -175,19 +177,24 @@ def run_cpu_baseline(cfg, thr, budget_s=15.0):
     if cfg.sta is not None:
         plane = oracle.sta_block_mask(cfg.grid, cfg.order, cfg.order_tile, cfg.sta.tile, cfg.sta.window, 64, cfg.S)
     flops, heads, blocks_done = 0.0, 0, 0
+    t_mask = t_attn = 0.0
     t0 = time.perf_counter()
     for h in range(c1.H):
         qh, kh, vh = (x[0, h].double().numpy() for x in (q, k, v))
+        tm = time.perf_counter()
         if thr is not None:
             keep, _, _ = oracle.nabla_mask(qh, kh, 64, thr)
             if plane is not None:
                 keep = keep | plane
         else:
             keep = plane
+        t_mask += time.perf_counter() - tm
         # attention on as many query blocks as the budget allows (whole head when possible)
         for i0 in range(0, cfg.nb, 32):
             blocks = list(range(i0, min(cfg.nb, i0 + 32)))
+            ta = time.perf_counter()
             oracle.block_sparse_attention(qh, kh, vh, keep, 64, cfg.S_valid, q_blocks=blocks)
+            t_attn += time.perf_counter() - ta
             flops += keep[blocks].sum() * _flops_per_tile(cfg.D)
             blocks_done += len(blocks)
             if time.perf_counter() - t0 > budget_s:
@@ -196,7 +203,11 @@ def run_cpu_baseline(cfg, thr, budget_s=15.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    per_block = t_attn / max(blocks_done, 1)
+    full = t_mask / heads * cfg.B * cfg.H + per_block * cfg.B * cfg.H * cfg.nb
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "oracle_s_per_head_mask": round(t_mask / heads, 4), "oracle_s_per_query_block": round(per_block, 6),
+            "extrapolated_full_oracle_s": round(full, 1),
             "sample": f"{cfg.name}: NABLA/STA mask of {heads} head(s) + attention of {blocks_done} query blocks "
                       f"in fp64 numpy ({dt:.1f} s)"}
 
@@ -551,6 +562,8 @@ def main():
                    "dense": args.dense, "fp8_qk": args.fp8,
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
+        # per-step spread from the phase pass (eager launches with events between the phases)
+        "step_ms_median_eager": round(r["step_ms_median"], 4), "step_ms_min_eager": round(r["step_ms_min"], 4),
         "attn_tflops": round(attn_tflops, 2), "attn_frac_bf16_peak": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
         "mask_build_gbps": round(mask_bytes / (r["mask_ms"] * 1e-3) / 1e9, 1) if thr is not None else None,
         "mask_build_frac_hbm": round(mask_bytes / (r["mask_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)

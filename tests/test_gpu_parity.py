@@ -369,3 +369,28 @@ def test_longest_first_order_large(gpu_lib):
     rp, ci, order = gpu_lib.mask_to_csr(plane, B=1, H=1, return_order=True)
     ref = np.concatenate([np.arange(0, nb2, 3), np.setdiff1d(np.arange(nb2), np.arange(0, nb2, 3))])
     assert np.array_equal(order.cpu().numpy(), ref)
+
+
+def test_maximum_nb_mask_topk_and_attention(gpu_lib):
+    # nb = 2048 (the largest sequence the mask build accepts): the widest select instantiation
+    from dataclasses import replace
+    cfg = replace(get_config(3, heads=2), cid=9, name="max-32x64x64", grid=(32, 64, 64))
+    assert cfg.nb == 2048 and cfg.S_valid == cfg.S
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    print(f"[max] nb {cfg.nb}, {cfg.H} heads", flush=True)
+    m = gpu_lib.nabla_build_mask(q, k, 0.2)
+    mt = gpu_lib.nabla_build_mask_topk(q, k, 300)
+    torch.cuda.synchronize()
+    keep, E = oracle_masks(q, k, 0.2)
+    bad, near = compare_masks(m, keep, E, 0.2)
+    print(f"  cdf mismatches {bad}, near {near}, kept {keep.mean():.4f}", flush=True)
+    assert bad == 0
+    for h in range(cfg.H):
+        ref, _ = oracle.topk_mask(f64(q[0, h]), f64(k[0, h]), 64, 300)
+        assert np.array_equal(mt[0, h].cpu().numpy().astype(bool), ref)
+    out = gpu_lib.block_sparse_attn_fwd(q, k, v, m)
+    torch.cuda.synchronize()
+    blocks = [(0, h, i) for h in range(cfg.H) for i in (0, 1023, 2047)]
+    mx, mean = attention_errors(out, oracle_attention_blocks(q, k, v, m.cpu().numpy().astype(bool), blocks, cfg.S))
+    print(f"  attention max {mx:.3e} mean {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
