@@ -394,3 +394,32 @@ def test_maximum_nb_mask_topk_and_attention(gpu_lib):
     mx, mean = attention_errors(out, oracle_attention_blocks(q, k, v, m.cpu().numpy().astype(bool), blocks, cfg.S))
     print(f"  attention max {mx:.3e} mean {mean:.3e}", flush=True)
     assert mx <= MAX_ERR and mean <= MEAN_ERR
+
+
+def test_batched_model_layout_views(gpu_lib):
+    """B = 2 with Q, K, V as [B, S, H, D] views of one packed QKV tensor (head and row strides of the
+    model's layout, not contiguous [B, H, S, D]); the output written into a strided view too."""
+    B, S, H, D, Sv = 2, 64 * 7, 3, 128, 64 * 6 + 20
+    g = torch.Generator(device="cpu").manual_seed(21)
+    qkv = torch.randn(B, S, 3, H, D, generator=g)
+    pos = torch.sin(torch.arange(S)[:, None] * 0.05 + torch.arange(D)[None, :] * 0.3)   # some structure
+    qkv[:, :, :2] += 2 * pos[None, :, None, None, :]
+    qkv[:, Sv:] = 0
+    qkv = qkv.to(torch.bfloat16).to(DEV)
+    q, k, v = (qkv[:, :, t].permute(0, 2, 1, 3) for t in range(3))          # [B, H, S, D] views
+    assert not q.is_contiguous() and q.stride(3) == 1
+    m = gpu_lib.nabla_build_mask(q, k, 0.3)
+    o2 = gpu_lib.block_sparse_attn_fwd(q, k, v, m, s_valid=Sv)
+    obuf = torch.full((B, S, H, D), 7.0, dtype=torch.bfloat16, device=DEV)
+    rp, ci = gpu_lib.mask_to_csr(m)
+    gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=Sv, out=obuf.permute(0, 2, 1, 3))
+    torch.cuda.synchronize()
+    assert torch.equal(obuf.permute(0, 2, 1, 3), o2)           # strided output, same values, every row written
+    keep, E = oracle_masks(q, k, 0.3)
+    bad, near = compare_masks(m, keep, E, 0.3)
+    assert bad == 0
+    for b in range(B):
+        for h in range(H):
+            O, _ = oracle.block_sparse_attention(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), keep[b, h], 64, Sv)
+            err = np.abs(f64(o2[b, h]) - O)
+            assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR, (b, h, err.max())
