@@ -69,27 +69,38 @@ __global__ __launch_bounds__(256) void sta_tiles_kernel(StaGeom g, int32_t* __re
   if (l == 0) out[0] = __popcll(ball);
 }
 
-// One workgroup per query block i; threads sweep the key blocks j.
+// One workgroup per query block i; threads sweep the key blocks j. Block i's tiles are
+// decoded once into shared memory; block j's list is read 8 entries at a time with
+// independent loads, so a pair costs about 1 + n_j / 8 memory round trips.
 __global__ __launch_bounds__(256) void sta_pairs_kernel(StaGeom g, const int32_t* __restrict__ tiles,
                                                         uint8_t* __restrict__ mask) {
-  __shared__ int32_t ti[STA_MAX_TILES];
+  __shared__ int16_t ta[3][STA_MAX_TILES];
   __shared__ int nti;
   const int i = blockIdx.x;
   const int32_t* src = tiles + (int64_t)i * (STA_MAX_TILES + 1);
   if (threadIdx.x == 0) nti = src[0];
-  if (threadIdx.x < STA_MAX_TILES) ti[threadIdx.x] = src[1 + threadIdx.x];
+  if (threadIdx.x < STA_MAX_TILES) {
+    const int32_t t = src[1 + threadIdx.x];
+    ta[0][threadIdx.x] = (int16_t)(t >> 20);
+    ta[1][threadIdx.x] = (int16_t)((t >> 10) & 1023);
+    ta[2][threadIdx.x] = (int16_t)(t & 1023);
+  }
   __syncthreads();
   const int n_i = nti;
   for (int j = threadIdx.x; j < g.nb; j += 256) {
     const int32_t* tj = tiles + (int64_t)j * (STA_MAX_TILES + 1);
     const int n_j = tj[0];
     bool keep = false;
-    for (int x = 0; x < n_i && !keep; ++x) {
-      const int a0 = ti[x] >> 20, a1 = (ti[x] >> 10) & 1023, a2 = ti[x] & 1023;
-      for (int y = 0; y < n_j; ++y) {
-        const int32_t c = tj[1 + y];
-        const int c0 = c >> 20, c1 = (c >> 10) & 1023, c2 = c & 1023;
-        if (abs(a0 - c0) <= g.rt && abs(a1 - c1) <= g.rh && abs(a2 - c2) <= g.rw) { keep = true; break; }
+    for (int y0 = 0; y0 < n_j && !keep; y0 += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int y = 0; y < 8; ++y) c[y] = y0 + y < n_j ? tj[1 + y0 + y] : -1;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        if (c[y] < 0) continue;
+        const int c0 = c[y] >> 20, c1 = (c[y] >> 10) & 1023, c2 = c[y] & 1023;
+        for (int x = 0; x < n_i; ++x)
+          keep |= abs(ta[0][x] - c0) <= g.rt && abs(ta[1][x] - c1) <= g.rh && abs(ta[2][x] - c2) <= g.rw;
       }
     }
     mask[(int64_t)i * g.nb + j] = keep ? 1 : 0;
