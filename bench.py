@@ -80,9 +80,9 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
     n_slots = lib.attn_work_order_slots(ctypes.byref(shp))
     work_order = torch.empty(n_slots, dtype=torch.int32, device=dev) if n_slots > 0 else None
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    st = {}
+
+    def phase_mask():
         if cfg.sta is not None and not dense:
             bsa.sta_build_mask(S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
                                order_tile=cfg.order_tile, device=dev, out=plane)
@@ -97,17 +97,25 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
             if fp8:
                 bsa.quantize_fp8_blocks(q, out=(qa, qs))
                 bsa.quantize_fp8_blocks(k, out=(ka, ks))
-        if ev is not None:
-            ev[1].record()
-        rp, ci = bsa.mask_to_csr(m, B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
-        wo = bsa.attn_work_order(qa, rp, s_valid=cfg.S_valid, out=work_order) if work_order is not None else None
-        if ev is not None:
-            ev[2].record()
-        bsa.block_sparse_attn_fwd_csr(qa, ka, v, rp, ci, s_valid=cfg.S_valid, q_scale=qs, k_scale=ks, out=out,
-                                      ws=attn_ws, work_order=wo)
+        st["m"] = m
+
+    def phase_csr():
+        st["rp"], st["ci"] = bsa.mask_to_csr(st["m"], B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
+        st["wo"] = (bsa.attn_work_order(qa, st["rp"], s_valid=cfg.S_valid, out=work_order)
+                    if work_order is not None else None)
+
+    def phase_attn():
+        bsa.block_sparse_attn_fwd_csr(qa, ka, v, st["rp"], st["ci"], s_valid=cfg.S_valid, q_scale=qs, k_scale=ks,
+                                      out=out, ws=attn_ws, work_order=st["wo"])
+
+    def step(ev=None):
+        for x, fn in enumerate((phase_mask, phase_csr, phase_attn)):
+            if ev is not None:
+                ev[x].record()
+            fn()
         if ev is not None:
             ev[3].record()
-        return m, rp
+        return st["m"], st["rp"]
 
     for _ in range(warmup):
         step()
@@ -151,11 +159,29 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
         step(evs[s])
     torch.cuda.synchronize()
     per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
-    mask_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    csr_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    eager_ms = {name: sum(e[x].elapsed_time(e[x + 1]) for e in evs) / steps
+                for x, name in enumerate(("mask", "csr", "attn"))}
+    # Device time of each phase: in the eager pass the host's marshalling of a call can
+    # leave the GPU idle after a phase event, and the event pair counts that. Here the
+    # phase runs `steps` times back to back after one call queued ahead, one event pair
+    # around them: the host stays ahead of the GPU, so the pair sees the kernels and the
+    # gaps between them only. (A HIP graph of the repeated calls reads higher at the
+    # 2B-DiT shape: 238 us per attention launch against 222-224 us in the kernel trace.)
+    def phase_ms(fn):
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        fn()
+        p0.record()
+        for _ in range(steps):
+            fn()
+        p1.record()
+        torch.cuda.synchronize()
+        return p0.elapsed_time(p1) / steps
+
+    mask_ms, csr_ms, attn_ms = phase_ms(phase_mask), phase_ms(phase_csr), phase_ms(phase_attn)
     kept = int(rp[-1].item())
     return dict(ms_per_step=ms_total / steps, wall_s=wall, mask_ms=mask_ms, csr_ms=csr_ms, attn_ms=attn_ms,
+                eager_phase_ms=eager_ms,
                 step_ms_median=per_step[len(per_step) // 2], step_ms_min=per_step[0],
                 kept_tiles=kept, kept_fraction=kept / (cfg.B * cfg.H * nb * nb), mask=m.cpu() if use_nabla else None,
                 q=q, k=k, v=v, qa=qa, ka=ka, qs=qs, ks=ks)
@@ -562,8 +588,9 @@ def main():
                    "dense": args.dense, "fp8_qk": args.fp8,
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
-        # per-step spread from the phase pass (eager launches with events between the phases)
+        # per-step spread and phase times from the eager pass with events between the phases
         "step_ms_median_eager": round(r["step_ms_median"], 4), "step_ms_min_eager": round(r["step_ms_min"], 4),
+        "eager_phase_ms": {k: round(x, 4) for k, x in r["eager_phase_ms"].items()},
         "attn_tflops": round(attn_tflops, 2), "attn_frac_bf16_peak": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
         "mask_build_gbps": round(mask_bytes / (r["mask_ms"] * 1e-3) / 1e9, 1) if thr is not None else None,
         "mask_build_frac_hbm": round(mask_bytes / (r["mask_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)

@@ -196,6 +196,10 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const int g16 = l & 15, mbase = 16 * ((l >> 4) & 1);
+  // lane bases of the operand reads (bf16 K rows 32 kt + l32, chunk 2 s + hi: base ^ 32 s;
+  // V^T rows 32 (sp >> 1) + 16 (sp & 1) + {0, 8} + 4 hi + g16 / 4, d tile dt: base ^ 64 dt)
+  const int k_lane = koff_lane<RBK>(l32, hi);
+  const int v_lane = voff<RBV>(4 * hi + (g16 >> 2), (mbase + 4 * (g16 & 3)) * 2);
 
   // two-entry look-ahead ring: (j, flags, scale) of steps u and u+1
   int f0 = 0, f1 = 0;
@@ -217,6 +221,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     bf16x8_t pop[4];
     if (use) {
       char BSA_LDS* kt0 = k_lds(st, 0);
+      const int ka = opaque(k_lane + st * NSPLIT * KT_BYTES);   // offset of this step's K slot
       // ---- S^T = K Q^T for this wave's 32 queries: sacc[kt], kv = kt*32 + 8(v/4) + 4 hi + v%4
       const f32x16_t zero16 = {};
       KOp kk[2][KS];
@@ -231,7 +236,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
             i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb + 16));
             kk[kt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           } else {
-            kk[kt][s] = *(const bf16x8_t BSA_LDS*)(kt0 + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+            kk[kt][s] = *(const bf16x8_t BSA_LDS*)(lds + (ka ^ (32 * s)) + kt * 32 * RBK);
           }
         }
 #pragma unroll
@@ -243,13 +248,13 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
           } else {
             sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[kt][s], qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0);
             if constexpr (MODE == ATTN_SPLIT_F32) {
-              const int r = kt * 32 + l32;
-              const bf16x8_t k1 = *(const bf16x8_t BSA_LDS*)(k_lds(st, 1) + koff<RBK>(r, (16 * s + 8 * hi) * 2));
+              const bf16x8_t k1 = *(const bf16x8_t BSA_LDS*)(lds + KT_BYTES + (ka ^ (32 * s)) + kt * 32 * RBK);
               sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[kt][s], qop[1][s], sacc[kt], 0, 0, 0);
               sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[0][s], sacc[kt], 0, 0, 0);
             }
           }
         }
+      if constexpr (MODE == ATTN_BF16) pipeline_reads<2 * KS, 1, 4>();
       // ---- mask padded keys of the last block
       if (kv0 + 64 > a.S_valid) {
 #pragma unroll
@@ -299,21 +304,22 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     wg_barrier();                                        // everybody's share
     if (use) {
       // ---- O^T += V^T P^T, V^T read from the row-major V tile with transposing reads
+      const int va = opaque(v_lane);
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
-        const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
+        const int rofs = (32 * (sp >> 1) + 16 * (sp & 1)) * RBV;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int cb = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
 #pragma unroll
           for (int x = 0; x < NSPLIT; ++x) {
-            char BSA_LDS* vt = v_lds(st, x);
-            s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt + voff<RBV>(ra, cb)));
-            s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt + voff<RBV>(ra + 8, cb)));
+            char BSA_LDS* vt = v_lds(st, x) + (va ^ (64 * dt)) + rofs;
+            s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)vt);
+            s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(vt + 8 * RBV));
             oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(v0, v1), pop[sp], oacc[dt], 0, 0, 0);
           }
         }
       }
+      if constexpr (MODE == ATTN_BF16) pipeline_reads<4 * DT, 2, 4>();
     }
     wait_lgkm0();                                        // reads of this step's slots done before the next barrier
     int f2 = 0;

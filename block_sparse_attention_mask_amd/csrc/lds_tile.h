@@ -44,20 +44,23 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Wave w of a P-wave workgroup issues instructions [w*NI/P, (w+1)*NI/P) of a tile copy.
+// A tile copy is 64 / RPI instructions of 1 KB, instruction t filling rows
+// [t RPI, (t + 1) RPI). Wave w of a P-wave workgroup issues t = u P + w, u = 0 .. NH-1:
+// the rows of one wave's instructions are P RPI apart, a multiple of both swizzle
+// periods (16 and 4 rows), so all of them use the same per-lane offset and only the
+// scalar base moves (one address register per tile instead of NH).
 template <int RB, bool VSWZ, int P>
 __device__ __forceinline__ void load_tile_part(const char* gtile, unsigned rs, unsigned lds, int lane, int w) {
   using G = TileGeom<RB>;
   constexpr int RPI = 1024 / RB;
   constexpr int NH = 64 / RPI / P;
   static_assert(NH * RPI * P == 64, "tile copy must split evenly");
+  static_assert(NH == 1 || (P * RPI) % 16 == 0, "the instructions of a wave must share the swizzle phase");
+  const int r0 = w * RPI + lane / G::NCH;
+  const int c = (lane % G::NCH) ^ (VSWZ ? G::swz_v(r0) : G::swz_k(r0));
+  const unsigned voff = (unsigned)r0 * rs + (unsigned)c * 16u;
 #pragma unroll
-  for (int u = 0; u < NH; ++u) {
-    const int t = w * NH + u;
-    const int r = t * RPI + lane / G::NCH;
-    const int c = (lane % G::NCH) ^ (VSWZ ? G::swz_v(r) : G::swz_k(r));
-    dma16(gtile, (unsigned)r * rs + (unsigned)c * 16u, lds + t * 1024);
-  }
+  for (int u = 0; u < NH; ++u) dma16(gtile + (int64_t)(u * P * RPI) * rs, voff, lds + (u * P + w) * 1024);
 }
 
 // byte offset of (row r, byte column cb) in a K-swizzled / V-swizzled tile
@@ -70,6 +73,25 @@ template <int RB>
 __device__ __forceinline__ int voff(int r, int cb) {
   using G = TileGeom<RB>;
   return r * RB + (((cb >> 4) ^ G::swz_v(r)) << 4) + (cb & 15);
+}
+
+// Operand reads of bf16 tiles as lane base ^ step. K-swizzled rows, 16-byte chunk 2s + hi:
+// koff(r, 32 s + 16 hi) = koff_lane(r, hi) ^ (32 s) (the swizzle moves bits 4 .. log2(RB)-1
+// of the offset only, and bit 4 separately from the others). V-swizzled rows, byte column
+// 64 dt + c with c < 64: voff(r, 64 dt + c) = voff(r, c) ^ (64 dt) (the swizzle is a
+// multiple of 4 chunks). Rows 4 apart (V) or 16 apart (K) share the swizzle, so other
+// rows are these offsets plus a multiple of RB.
+template <int RB>
+__device__ __forceinline__ int koff_lane(int r, int hi) {
+  using G = TileGeom<RB>;
+  const int w = G::swz_k(r);
+  return r * RB + 16 * (hi ^ (w & 1)) + 32 * (w >> 1);
+}
+// keeps a value in a register as computed, so that offsets derived from it are formed
+// where they are used instead of being hoisted into registers of their own
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 __device__ __forceinline__ float partner(float x) {
@@ -89,6 +111,22 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // building a bf16 vector element by element is mis-compiled by the current toolchain.
 __device__ __forceinline__ unsigned pk_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// Scheduling order for a run of NM MFMAs that each consume NR LDS reads: the reads of
+// the first P MFMAs, then each MFMA followed by the reads of the MFMA P places later.
+// Without it the compiler, short of registers, issues each operand read right before
+// its MFMA and waits for it there; with it P operand sets are in flight.
+template <int NM, int NR, int P>
+__device__ __forceinline__ void pipeline_reads() {
+  constexpr int D = P < NM ? P : NM;
+  __builtin_amdgcn_sched_group_barrier(0x100, NR * D, 0);    // DS reads
+#pragma unroll
+  for (int x = 0; x < NM - D; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
 }
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
