@@ -220,41 +220,61 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     f32x16_t sacc[2];
     bf16x8_t pop[4];
     if (use) {
-      char BSA_LDS* kt0 = k_lds(st, 0);
       const int ka = opaque(k_lane + st * NSPLIT * KT_BYTES);   // offset of this step's K slot
       // ---- S^T = K Q^T for this wave's 32 queries: sacc[kt], kv = kt*32 + 8(v/4) + 4 hi + v%4
       const f32x16_t zero16 = {};
-      KOp kk[2][KS];
+      if constexpr (MODE == ATTN_BF16) {
+        // MFMA m = (s, kt) = (m / 2, m % 2): the two accumulator chains alternate and the
+        // operand reads run PD MFMAs ahead. Scheduling fences keep this order; left alone,
+        // the compiler runs the chains one after the other and reads each operand right
+        // before its MFMA.
+        constexpr int NM = 2 * KS, PD = 6;
+        auto kread = [&](int m) {
+          return *(const bf16x8_t BSA_LDS*)(lds + (ka ^ (32 * (m >> 1))) + (m & 1) * 32 * RBK);
+        };
+        bf16x8_t kq[NM];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int m = 0; m < PD; ++m) kq[m] = kread(m);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int r = kt * 32 + l32;
-          if constexpr (MODE == ATTN_FP8) {
-            const int cb = 64 * s + 32 * hi;
-            i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb));
-            i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb + 16));
-            kk[kt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          } else {
-            kk[kt][s] = *(const bf16x8_t BSA_LDS*)(lds + (ka ^ (32 * s)) + kt * 32 * RBK);
-          }
+        for (int m = 0; m < NM; ++m) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int sm = m >> 1, kt = m & 1;
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[m], qop[0][sm], sm ? sacc[kt] : zero16, 0, 0, 0);
+          if (m + PD < NM) kq[m + PD] = kread(m + PD);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // fp8 and the f32 split: all K operands of the tile, then the MFMAs
+        char BSA_LDS* kt0 = k_lds(st, 0);
+        KOp kk[2][KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          if constexpr (MODE == ATTN_FP8) {
-            sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kk[kt][s], qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0, 127, 0, 127);
-          } else {
-            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[kt][s], qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0);
-            if constexpr (MODE == ATTN_SPLIT_F32) {
+          for (int s = 0; s < KS; ++s) {
+            if constexpr (MODE == ATTN_FP8) {
+              const int r = kt * 32 + l32, cb = 64 * s + 32 * hi;
+              i32x4_t x0 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb));
+              i32x4_t x1 = *(const i32x4_t BSA_LDS*)(kt0 + koff<RBK>(r, cb + 16));
+              kk[kt][s] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            } else {
+              kk[kt][s] = *(const bf16x8_t BSA_LDS*)(lds + (ka ^ (32 * s)) + kt * 32 * RBK);
+            }
+          }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if constexpr (MODE == ATTN_FP8) {
+              sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kk[kt][s], qop[0][s], s ? sacc[kt] : zero16, 0,
+                                                                         0, 0, 127, 0, 127);
+            } else {
               const bf16x8_t k1 = *(const bf16x8_t BSA_LDS*)(lds + KT_BYTES + (ka ^ (32 * s)) + kt * 32 * RBK);
+              sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[kt][s], qop[0][s], s ? sacc[kt] : zero16, 0, 0, 0);
               sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[kt][s], qop[1][s], sacc[kt], 0, 0, 0);
               sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[0][s], sacc[kt], 0, 0, 0);
             }
           }
-        }
-      if constexpr (MODE == ATTN_BF16) pipeline_reads<2 * KS, 1, 4>();
+      }
       // ---- mask padded keys of the last block
       if (kv0 + 64 > a.S_valid) {
 #pragma unroll

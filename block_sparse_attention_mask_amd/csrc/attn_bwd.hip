@@ -171,8 +171,14 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
                                    (unsigned)(uintptr_t)(lds + KV0 + (2 * x + 1) * KT), l, wave);
     }
   }
-  const char BSA_LDS* kt = lds + KV0 + 2 * kb * KT;
-  const char BSA_LDS* vt = kt + KT;
+  // lane bases of the operand reads (an XOR swizzle moves only offset bits below log2 RB,
+  // so the offset of byte column cb in a row is the row's offset ^ cb; slot offsets are
+  // multiples of 1024 and leave those bits alone): Q / dO rows 32 qh + l32, K / V rows
+  // 32 kh + l32 of this wave's key block, transposed dO / Q reads at rows
+  // 32 qh + 16 sp + {0, 8} + 4 hi + g16 / 4 and d tile dt
+  const int q_row = voff<RB>(qh * 32 + l32, 16 * hi);
+  const int kv_row = KV0 + 2 * kb * KT + koff<RB>(kh * 32 + l32, 16 * hi);
+  const int q_tr = voff<RB>(32 * qh + 4 * hi + (g16 >> 2), (mbase + 4 * (g16 & 3)) * 2);
   const int key = j * 64 + kh * 32 + l32;
   const bool kvalid = key < a.S_valid;
   const float c2 = a.scale_log2;
@@ -222,16 +228,15 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
     if (i1 >= 0) dma(st ^ 1, i1);
     if (((f0 >> kb) & 1) && i0 * 64 < a.S_valid) {
       const char BSA_LDS* sq = lds + st * SLOT;
-      const char BSA_LDS* sdo = sq + KT;
       const float BSA_LDS* sld = (const float BSA_LDS*)(sq + 2 * KT);
       const f32x16_t zero16 = {};
-      const int qr = qh * 32 + l32;
+      const int qr = opaque(q_row + st * SLOT), qt = opaque(q_tr + st * SLOT), kvr = opaque(kv_row);
       // S = Q K^T: rows q = 32 qh + 8 (v/4) + 4 hi + v%4, column = key
       f32x16_t acc = zero16;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8_t aq = *(const bf16x8_t BSA_LDS*)(sq + voff<RB>(qr, (16 * s + 8 * hi) * 2));
-        const bf16x8_t bk = *(const bf16x8_t BSA_LDS*)(kt + koff<RB>(kh * 32 + l32, (16 * s + 8 * hi) * 2));
+        const bf16x8_t aq = *(const bf16x8_t BSA_LDS*)(lds + (qr ^ (32 * s)));
+        const bf16x8_t bk = *(const bf16x8_t BSA_LDS*)(lds + (kvr ^ (32 * s)));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, acc, 0, 0, 0);
       }
       // P; (lse2, delta) of the 4 consecutive rows of group v/4 in two 16-byte reads
@@ -250,12 +255,11 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
         const bf16x8_t pb = pack8(p + 8 * sp);
-        const int ra = 32 * qh + 16 * sp + 4 * hi + (g16 >> 2);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int cbt = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
-          const s16x4_t o0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(sdo + voff<RB>(ra, cbt)));
-          const s16x4_t o1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(sdo + voff<RB>(ra + 8, cbt)));
+          const char BSA_LDS* o = lds + KT + (qt ^ (64 * dt)) + 16 * sp * RB;
+          const s16x4_t o0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)o);
+          const s16x4_t o1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(o + 8 * RB));
           dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(o0, o1), pb, dvT[dt], 0, 0, 0);
         }
       }
@@ -263,8 +267,8 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
       acc = zero16;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8_t ad = *(const bf16x8_t BSA_LDS*)(sdo + voff<RB>(qr, (16 * s + 8 * hi) * 2));
-        const bf16x8_t bv = *(const bf16x8_t BSA_LDS*)(vt + koff<RB>(kh * 32 + l32, (16 * s + 8 * hi) * 2));
+        const bf16x8_t ad = *(const bf16x8_t BSA_LDS*)(lds + KT + (qr ^ (32 * s)));
+        const bf16x8_t bv = *(const bf16x8_t BSA_LDS*)(lds + KT + (kvr ^ (32 * s)));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, acc, 0, 0, 0);
       }
 #pragma unroll
@@ -280,12 +284,11 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
 #pragma unroll
       for (int sp = 0; sp < 2; ++sp) {
         const bf16x8_t db = pack8(p + 8 * sp);
-        const int ra = 32 * qh + 16 * sp + 4 * hi + (g16 >> 2);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int cbt = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
-          const s16x4_t q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(sq + voff<RB>(ra, cbt)));
-          const s16x4_t q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(sq + voff<RB>(ra + 8, cbt)));
+          const char BSA_LDS* o = lds + (qt ^ (64 * dt)) + 16 * sp * RB;
+          const s16x4_t q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)o);
+          const s16x4_t q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(o + 8 * RB));
           dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(q0, q1), db, dkT[dt], 0, 0, 0);
         }
       }
@@ -416,6 +419,10 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dqT[dt][v] = 0.f;
+  // lane bases of the operand reads (offset of byte column cb = row offset ^ cb): K rows
+  // (V-swizzled) and V rows (K-swizzled) t*32 + l32, transposed K reads as in the forward
+  const int k_row = voff<RB>(l32, 16 * hi), v_row = KT + koff<RB>(l32, 16 * hi);
+  const int k_tr = voff<RB>(4 * hi + (g16 >> 2), (mbase + 4 * (g16 & 3)) * 2);
 
   int f0 = 0, f1 = 0;
   int j0 = next_entry(f0);
@@ -428,8 +435,8 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     if (j1 >= 0) dma(st ^ 1, j1);
     const int kv0 = j0 * 64;
     if (((f0 >> pr) & 1) && kv0 < a.S_valid) {
-      char BSA_LDS* kt = k_lds(st);
-      char BSA_LDS* vt = v_lds(st);
+      const int so = st * 2 * KT;
+      const int kr = opaque(k_row + so), vr = opaque(v_row + so), ktr = opaque(k_tr + so);
       const f32x16_t zero16 = {};
       f32x16_t sacc[2], dpacc[2];
 #pragma unroll
@@ -441,9 +448,8 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
       for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int r = t * 32 + l32;
-          const bf16x8_t ak = *(const bf16x8_t BSA_LDS*)(kt + voff<RB>(r, (16 * s + 8 * hi) * 2));
-          const bf16x8_t av = *(const bf16x8_t BSA_LDS*)(vt + koff<RB>(r, (16 * s + 8 * hi) * 2));
+          const bf16x8_t ak = *(const bf16x8_t BSA_LDS*)(lds + (kr ^ (32 * s)) + t * 32 * RB);
+          const bf16x8_t av = *(const bf16x8_t BSA_LDS*)(lds + (vr ^ (32 * s)) + t * 32 * RB);
           sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[s], sacc[t], 0, 0, 0);
           dpacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dop[s], dpacc[t], 0, 0, 0);
         }
@@ -461,12 +467,11 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         const bf16x8_t db = pack8(&ds[sp >> 1][8 * (sp & 1)]);
-        const int ra = 32 * (sp >> 1) + 16 * (sp & 1) + 4 * hi + (g16 >> 2);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int cbt = (32 * dt + mbase + 4 * (g16 & 3)) * 2;
-          const s16x4_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(kt + voff<RB>(ra, cbt)));
-          const s16x4_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(kt + voff<RB>(ra + 8, cbt)));
+          const char BSA_LDS* o = lds + (ktr ^ (64 * dt)) + (32 * (sp >> 1) + 16 * (sp & 1)) * RB;
+          const s16x4_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)o);
+          const s16x4_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(o + 8 * RB));
           dqT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(k0, k1), db, dqT[dt], 0, 0, 0);
         }
       }
