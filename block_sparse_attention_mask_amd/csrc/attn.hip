@@ -339,7 +339,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
           }
         }
       }
-      if constexpr (MODE == ATTN_BF16) pipeline_reads<4 * DT, 2, 4>();
+      if constexpr (MODE != ATTN_SPLIT_F32) pipeline_reads<4 * DT, 2, 4>();
     }
     wait_lgkm0();                                        // reads of this step's slots done before the next barrier
     int f2 = 0;
