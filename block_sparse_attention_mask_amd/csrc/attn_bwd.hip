@@ -438,22 +438,39 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
       const int so = st * 2 * KT;
       const int kr = opaque(k_row + so), vr = opaque(v_row + so), ktr = opaque(k_tr + so);
       const f32x16_t zero16 = {};
+      // MFMA list: n < 4 KS: S^T = K Q^T and dP^T = V dO^T for (s, t) = (n / 4, (n / 2) % 2),
+      // n even S, n odd dP (four independent accumulator chains, one row read each); then
+      // 4 DT MFMAs dQ^T += K^T dS^T (the forward's P V step with K in place of V), sp = m / DT,
+      // dt = m % DT, one pair of transposing reads each. Operand reads run PD MFMAs ahead
+      // (across the switch to dQ, while dS is formed); scheduling fences keep the order.
+      constexpr int NSD = 4 * KS, NM = NSD + 4 * DT, PD = 4;
+      auto rd = [&](int n) -> bf16x8_t {
+        if (n < NSD) {
+          const int sm = n >> 2, t = (n >> 1) & 1;
+          return *(const bf16x8_t BSA_LDS*)(lds + (((n & 1) ? vr : kr) ^ (32 * sm)) + t * 32 * RB);
+        }
+        const int m = n - NSD, sp = m / DT, dt = m % DT;
+        const char BSA_LDS* o = lds + (ktr ^ (64 * dt)) + (32 * (sp >> 1) + 16 * (sp & 1)) * RB;
+        const s16x4_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)o);
+        const s16x4_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(o + 8 * RB));
+        return join_bf16x8(k0, k1);
+      };
+      bf16x8_t op[NM];
+#pragma unroll
+      for (int n = 0; n < PD; ++n) op[n] = rd(n);
       f32x16_t sacc[2], dpacc[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sacc[t] = zero16;
-        dpacc[t] = zero16;
+      for (int n = 0; n < NSD; ++n) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int sm = n >> 2, t = (n >> 1) & 1;
+        if (n & 1)
+          dpacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n], dop[sm], sm ? dpacc[t] : zero16, 0, 0, 0);
+        else
+          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n], qop[sm], sm ? sacc[t] : zero16, 0, 0, 0);
+        op[n + PD] = rd(n + PD);
       }
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8_t ak = *(const bf16x8_t BSA_LDS*)(lds + (kr ^ (32 * s)) + t * 32 * RB);
-          const bf16x8_t av = *(const bf16x8_t BSA_LDS*)(lds + (vr ^ (32 * s)) + t * 32 * RB);
-          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[s], sacc[t], 0, 0, 0);
-          dpacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dop[s], dpacc[t], 0, 0, 0);
-        }
       // P^T and dS^T: rows kv = 32 t + 8 (v/4) + 4 hi + v%4, column = this lane's query
+      __builtin_amdgcn_sched_barrier(0);
       float ds[2][16];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -463,18 +480,17 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
           const float pv = kv0 + kv < a.S_valid ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, -lse2)) : 0.f;
           ds[t][v] = pv * (dpacc[t][v] - delta);
         }
-      // dQ^T += K^T dS^T (the forward's P V step with K in place of V)
+      bf16x8_t db[4];
 #pragma unroll
-      for (int sp = 0; sp < 4; ++sp) {
-        const bf16x8_t db = pack8(&ds[sp >> 1][8 * (sp & 1)]);
+      for (int sp = 0; sp < 4; ++sp) db[sp] = pack8(&ds[sp >> 1][8 * (sp & 1)]);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const char BSA_LDS* o = lds + (ktr ^ (64 * dt)) + (32 * (sp >> 1) + 16 * (sp & 1)) * RB;
-          const s16x4_t k0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)o);
-          const s16x4_t k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t BSA_LDS*)(o + 8 * RB));
-          dqT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_bf16x8(k0, k1), db, dqT[dt], 0, 0, 0);
-        }
+      for (int n = NSD; n < NM; ++n) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int m = n - NSD;
+        dqT[m % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n], db[m / DT], dqT[m % DT], 0, 0, 0);
+        if (n + PD < NM) op[n + PD] = rd(n + PD);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     wait_lgkm0();
     int f2 = 0;
