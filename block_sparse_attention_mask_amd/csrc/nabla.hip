@@ -20,6 +20,8 @@
 //     closer than 2^-60 to each other are ordered by index), with per-bucket
 //     histograms of count and mass. The sums are exact integers, so the result does
 //     not depend on the order of the atomic additions (run-to-run deterministic).
+//     For short rows (nb <= 256) select_rows_kernel does the same per row with one
+//     wave per row after the map is formed, without workgroup barriers.
 #include "common.h"
 #include "launch.h"
 
@@ -229,6 +231,37 @@ __device__ __forceinline__ int sel_digit(uint64_t key, const SelRowState& st) {
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
+// The reduced map of 16 query-block rows row0 = 16 rt ..: acc[c] = Qbar(16 rows) .
+// Kbar^T(column tile w + SEL_WAVES c) on v_mfma_f64_16x16x4f64. In the result layout
+// lane l holds rows {4v + l/16 : v = 0..3} of column 16*tile + l%16. All KS operands of
+// a column tile are loaded before its MFMAs (one latency per tile); columns past nb
+// hold unspecified values. Ends with the rows' operands staged in qa_lds (after a
+// workgroup barrier).
+template <int NCT, int KS>
+__device__ __forceinline__ void reduced_map_strip(const double* __restrict__ qmf, const double* __restrict__ kmf,
+                                                  int bh, int rt, int ntile, int nb, double BSA_LDS* qa_lds,
+                                                  f64x4_t (&acc)[NCT]) {
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, row0 = rt * SEL_ROWS;
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  const double* qa = qmf + ((int64_t)bh * ntile + rt) * KS * 64;
+  for (int x = tid; x < KS * 64; x += SEL_WAVES * 64) qa_lds[x] = row0 + (x & 15) < nb ? qa[x] : 0.0;
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int ct = w + SEL_WAVES * c;
+    if (ct >= ntile) break;
+    const double* kb = kmf + ((int64_t)bh * ntile + ct) * KS * 64 + l;
+    double bv[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bv[s] = kb[s * 64];
+    f64x4_t a4 = acc[c];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a4 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa_lds[s * 64 + l], bv[s], a4, 0, 0, 0);
+    acc[c] = a4;
+  }
+}
+
 // One workgroup of SEL_WAVES waves per tile of 16 query-block rows of one head.
 // The reduced map of the 16 rows is an MFMA f64 product (16 rows) x (16-column
 // tiles); wave w owns column tiles w, w + SEL_WAVES, ... (NCT of them). In the
@@ -258,30 +291,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lc = l & 15;
   const int ntile = (nb + 15) / 16;
 
-  // ---- reduced map: acc[c] = Qbar(16 rows) . Kbar^T(column tile w + SEL_WAVES c).
-  // All KS operands of a column tile are loaded before its MFMAs (one latency per
-  // tile); columns past nb hold unspecified values and are masked below.
+  // ---- reduced map (columns past nb are masked below)
   f64x4_t acc[NCT];
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) acc[c] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  {
-    const double* qa = qmf + ((int64_t)bh * ntile + rt) * KS * 64;
-    for (int x = tid; x < KS * 64; x += SEL_WAVES * 64) qa_lds[x] = row0 + (x & 15) < nb ? qa[x] : 0.0;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      const int ct = w + SEL_WAVES * c;
-      if (ct >= ntile) break;
-      const double* kb = kmf + ((int64_t)bh * ntile + ct) * KS * 64 + l;
-      double bv[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) bv[s] = kb[s * 64];
-      f64x4_t a4 = acc[c];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) a4 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa_lds[s * 64 + l], bv[s], a4, 0, 0, 0);
-      acc[c] = a4;
-    }
-  }
+  reduced_map_strip<NCT, KS>(qmf, kmf, bh, rt, ntile, nb, (double BSA_LDS*)qa_lds, acc);
 
   // column of value (c) in this lane, its validity; rows of value slot v: 4v + g
   auto colof = [&](int c) { return (w + SEL_WAVES * c) * 16 + lc; };
@@ -496,6 +508,186 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
 }
 
 // ----------------------------------------------------------------------------
+// Row selection for short rows (nb <= 256). The same reduced map, fixed-point keys,
+// radix digits and tie rule as select_kernel; once the map is formed it is written to
+// shared memory, and each wave then owns two whole rows: softmax, radix select, tie
+// ranking and the row's write use wave reductions, ballots and wave-uniform state only,
+// with no workgroup barrier. Column j of a row is entry e = j / 64 of lane j % 64. A
+// wave's histogram lives in its own part of shared memory; the shared-memory
+// operations of one wave are processed in program order, so a clear, the atomic
+// updates and the reads that follow need no wait between them.
+// ----------------------------------------------------------------------------
+constexpr int SELR_MAX_NB = 256;
+
+// value of x in lane L (L wave-uniform)
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int L) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, L);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), L);
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+template <int NCT, int KS>   // NCT = column tiles per wave (nb <= 128 NCT)
+__global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const double* __restrict__ qmf,
+                                                                    const double* __restrict__ kmf, int nb,
+                                                                    double scale, uint64_t T_fixed, int topk,
+                                                                    const uint8_t* __restrict__ or_mask,
+                                                                    int64_t or_sb, int64_t or_sh, int H,
+                                                                    uint8_t* __restrict__ mask_out) {
+  constexpr int E = 2 * NCT;                        // entries per lane per row
+  constexpr int NBP = SEL_WAVES * 16 * NCT;         // map row length
+  const bool by_count = topk > 0;
+  const uint64_t target = by_count ? (uint64_t)topk : T_fixed;
+  __shared__ double qa_lds[32 * 64];
+  __shared__ double map[SEL_ROWS][NBP];
+  __shared__ uint64_t hmass[SEL_WAVES][256];
+  __shared__ uint32_t hcnt[SEL_WAVES][256];
+
+  const int bh = blockIdx.y, rt = blockIdx.x, row0 = rt * SEL_ROWS;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lc = l & 15;
+  const int ntile = (nb + 15) / 16;
+
+  f64x4_t acc[NCT];
+  reduced_map_strip<NCT, KS>(qmf, kmf, bh, rt, ntile, nb, (double BSA_LDS*)qa_lds, acc);
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int ct = w + SEL_WAVES * c;
+    if (ct >= ntile) break;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) map[4 * v + g][ct * 16 + lc] = acc[c][v] * scale;
+  }
+  __syncthreads();
+
+  const int b = bh / H, h = bh % H;
+  for (int rr = 0; rr < SEL_ROWS / SEL_WAVES; ++rr) {
+    const int r = (SEL_ROWS / SEL_WAVES) * w + rr, row = row0 + r;
+    if (row >= nb) break;                            // wave-uniform
+    // ---- softmax of the row in fp64, then the fixed-point mass w = floor(p 2^60) (the key)
+    bool valid[E];
+    double x[E];
+    double m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = 64 * e + l;
+      valid[e] = j < nb;
+      x[e] = valid[e] ? map[r][j] : -INFINITY;
+      m = fmax(m, x[e]);
+    }
+    m = wave_max_f64(m);
+    double sum = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      x[e] = valid[e] ? exp(x[e] - m) : 0.0;
+      sum += x[e];
+    }
+    const double inv = 1.0 / wave_sum_f64(sum);
+    uint64_t key[E];
+    uint64_t ms = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      key[e] = valid[e] ? fixed_mass(x[e] * inv) : 0;
+      ms += key[e];
+    }
+    const uint64_t total = wave_sum_u64(ms);
+
+    // ---- radix select of the pivot; the row state is wave-uniform
+    SelRowState sr;
+    sr.lo = 0;
+    sr.mass_above = 0;
+    sr.span = -1;
+    sr.cnt = 0;
+    sr.tie_keep = 0;
+    sr.status = (by_count ? nb <= topk : total < T_fixed) ? ROW_ALL : ROW_ACTIVE;
+    for (int pass = 0; pass < 9 && sr.status == ROW_ACTIVE; ++pass) {
+#pragma unroll
+      for (int x4 = 0; x4 < 4; ++x4) {
+        hmass[w][4 * l + x4] = 0;
+        hcnt[w][4 * l + x4] = 0;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (!valid[e]) continue;
+        const int dg = sel_digit(key[e], sr);
+        if (dg >= 0) {
+          atomicAdd((unsigned long long*)&hmass[w][dg], (unsigned long long)key[e]);
+          atomicAdd(&hcnt[w][dg], 1u);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // lane l owns buckets 255-4l .. 252-4l (descending keys)
+      uint64_t mb[4];
+      uint32_t cb[4];
+      uint64_t lt = 0;
+#pragma unroll
+      for (int x4 = 0; x4 < 4; ++x4) {
+        cb[x4] = hcnt[w][255 - 4 * l - x4];
+        mb[x4] = by_count ? (uint64_t)cb[x4] : hmass[w][255 - 4 * l - x4];   // what the target counts
+        lt += mb[x4];
+      }
+      const uint64_t incl = wave_incl_scan_u64(lt);
+      const uint64_t before = sr.mass_above + (incl - lt);
+      const uint64_t ball = __ballot(before + lt >= target);
+      const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
+      // the crossing bucket of lane L, found by every lane from lane L's values
+      uint64_t cum = readlane_u64(before, L);
+      int xs = 3, cnt = 0;
+#pragma unroll
+      for (int x4 = 0; x4 < 4; ++x4) {
+        const uint64_t mbl = readlane_u64(mb[x4], L);
+        const int cbl = __builtin_amdgcn_readlane((int)cb[x4], L);
+        if (xs == 3 && x4 < 3) {
+          if (cum + mbl >= target) { xs = x4; cnt = cbl; }
+          else cum += mbl;
+        } else if (x4 == 3 && xs == 3) {
+          cnt = cbl;
+        }
+      }
+      const int dg = 255 - 4 * L - xs;
+      SelRowState n = sr;
+      n.mass_above = cum;
+      n.cnt = cnt;
+      if (sr.span < 0) {
+        first_range(dg, n.lo, n.span);
+      } else {
+        const int db = sr.span < 8 ? sr.span : 8;
+        n.span = sr.span - db;
+        n.lo = sr.lo + ((uint64_t)dg << n.span);
+      }
+      if (n.cnt <= 1) n.status = ROW_PIVOT;
+      else if (n.span == 0) {
+        // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
+        const uint64_t wq = by_count ? 1 : n.lo;
+        const uint64_t need = target - n.mass_above;           // > 0
+        const uint64_t t = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
+        n.tie_keep = (int)(t < (uint64_t)n.cnt ? t : (uint64_t)n.cnt);
+        n.status = ROW_TIE;
+      }
+      sr = n;
+    }
+
+    // ---- write the row (OR'd with the optional mask); tied keys ranked by ascending index
+    uint8_t* dst = mask_out + ((int64_t)bh * nb + row) * nb;
+    const uint8_t* om = or_mask ? or_mask + b * or_sb + h * or_sh + (int64_t)row * nb : nullptr;
+    int tie_base = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = 64 * e + l;
+      const bool tied = sr.status == ROW_TIE && valid[e] && key[e] == sr.lo;
+      const uint64_t tb = __ballot(tied);
+      const int rank = tie_base + __popcll(tb & ((1ull << l) - 1ull));
+      tie_base += __popcll(tb);
+      if (!valid[e]) continue;
+      bool keep;
+      if (sr.status == ROW_ALL) keep = true;
+      else if (sr.status == ROW_PIVOT) keep = key[e] >= sr.lo;
+      else keep = tied ? rank < sr.tie_keep : key[e] > sr.lo;
+      if (om && om[j]) keep = true;
+      dst[j] = keep ? 1 : 0;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
 template <typename T, int D, bool NT>
@@ -547,11 +739,30 @@ static hipError_t launch_select_c(const double* qmf, const double* kmf, int B, i
   return hipGetLastError();
 }
 
+template <int NCT>
+static hipError_t launch_select_rows(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
+                                     uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                                     uint8_t* mask_out, hipStream_t st) {
+  dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS, B * H);
+  if (D == 64)
+    hipLaunchKernelGGL((select_rows_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
+                       topk, or_mask, or_sb, or_sh, H, mask_out);
+  else
+    hipLaunchKernelGGL((select_rows_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
+                       topk, or_mask, or_sb, or_sh, H, mask_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                          uint8_t* mask_out, hipStream_t st) {
   const int ntile = (nb + 15) / 16;
   const int nct = (ntile + SEL_WAVES - 1) / SEL_WAVES;
+  if (nb <= SELR_MAX_NB) {
+    if (nct == 1)
+      return launch_select_rows<1>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, mask_out, st);
+    return launch_select_rows<2>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, mask_out, st);
+  }
 #define BSA_SEL_CASE(n) \
   case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, mask_out, st);
   switch (nct) {

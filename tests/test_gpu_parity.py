@@ -396,6 +396,39 @@ def test_maximum_nb_mask_topk_and_attention(gpu_lib):
     assert mx <= MAX_ERR and mean <= MEAN_ERR
 
 
+@pytest.mark.parametrize("grid", [(3, 43, 64), (8, 40, 40), (16, 32, 32)])
+def test_short_row_select_two_tiles(gpu_lib, grid):
+    # nb = 129, 200, 256: the mask build for short rows (one wave per row once the map is
+    # formed) with two column tiles per wave; thresholds, Top-k and an OR'd mask
+    from dataclasses import replace
+    cfg = replace(get_config(3, heads=3), cid=9, name="short-%dx%dx%d" % grid, grid=grid)
+    assert cfg.S_valid == cfg.S and 128 < cfg.nb <= 256
+    q, k, _ = make_inputs(cfg, seed=1, device=DEV)
+    rng = np.random.default_rng(7)
+    plane = rng.random((cfg.nb, cfg.nb)) < 0.05
+    plane_t = torch.from_numpy(plane.astype(np.uint8)).to(DEV)
+    for thr in (0.0, 0.1, 0.2, 0.6):
+        print(f"[short] nb {cfg.nb} thr {thr}", flush=True)
+        m = gpu_lib.nabla_build_mask(q, k, thr)
+        mo = gpu_lib.nabla_build_mask(q, k, thr, or_mask=plane_t)
+        torch.cuda.synchronize()
+        keep, E = oracle_masks(q, k, thr)
+        bad, near = compare_masks(m, keep, E, thr)
+        assert bad == 0, (thr, bad, near)
+        keep_or, _ = oracle_masks(q, k, thr, or_plane=plane)
+        bad, near = compare_masks(mo, keep_or, E, thr)
+        assert bad == 0, (thr, "or", bad, near)
+    for topk in (1, 37, cfg.nb - 1):
+        print(f"[short] nb {cfg.nb} topk {topk}", flush=True)
+        mt = gpu_lib.nabla_build_mask_topk(q, k, topk)
+        torch.cuda.synchronize()
+        for h in range(cfg.H):
+            ref, P = oracle.topk_mask(f64(q[0, h]), f64(k[0, h]), 64, topk)
+            diff = mt[0, h].cpu().numpy().astype(bool) != ref
+            kth = -np.sort(-P, axis=1)[:, topk - 1]
+            assert not (diff & ~(np.abs(P - kth[:, None]) <= 2.0 ** -59)).any(), (topk, h)
+
+
 def test_batched_model_layout_views(gpu_lib):
     """B = 2 with Q, K, V as [B, S, H, D] views of one packed QKV tensor (head and row strides of the
     model's layout, not contiguous [B, H, S, D]); the output written into a strided view too."""
