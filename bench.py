@@ -100,9 +100,10 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
         st["m"] = m
 
     def phase_csr():
-        st["rp"], st["ci"] = bsa.mask_to_csr(st["m"], B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
-        st["wo"] = (bsa.attn_work_order(qa, st["rp"], s_valid=cfg.S_valid, out=work_order)
-                    if work_order is not None else None)
+        # kv lists, and the attention work order where the shape has one (one call)
+        st["rp"], st["ci"] = bsa.mask_to_csr(st["m"], B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws,
+                                             work_order=work_order)
+        st["wo"] = work_order
 
     def phase_attn():
         bsa.block_sparse_attn_fwd_csr(qa, ka, v, st["rp"], st["ci"], s_valid=cfg.S_valid, q_scale=qs, k_scale=ks,

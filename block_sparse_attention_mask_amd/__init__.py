@@ -24,7 +24,8 @@ _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPA
 EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_topk", "quantize_fp8_blocks",
            "nabla_build_mask_fp8",
            "sta_workspace_size", "sta_build_mask", "mask_or",
-           "csr_workspace_size", "bsa_mask_to_csr", "attn_workspace_size", "block_sparse_attn_fwd",
+           "csr_workspace_size", "bsa_mask_to_csr", "bsa_mask_to_csr_ordered", "attn_workspace_size",
+           "block_sparse_attn_fwd",
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
            "attn_bwd_workspace_size", "block_sparse_attn_bwd", "token_reorder", "bsa_last_error",
            "bsa_abi_version"]
@@ -73,6 +74,7 @@ def load(path: Optional[str] = None):
         "mask_or": (i32, [vp, vp, i64, vp, i64, vp]),
         "csr_workspace_size": (sz, [i32, i32, i32]),
         "bsa_mask_to_csr": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "bsa_mask_to_csr_ordered": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "attn_workspace_size": (sz, [PS, i32]),
         "block_sparse_attn_fwd": (i32, [PT, PT, PT, PS, vp, i64, i64, vp, vp, dbl, PT, vp, vp, sz, vp]),
         "attn_csr_workspace_size": (sz, [PS, i32]),
@@ -259,11 +261,13 @@ def mask_or(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None
 def mask_to_csr(mask: torch.Tensor, B: Optional[int] = None, H: Optional[int] = None,
                 row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None,
                 ws: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
-                return_order: bool = False):
+                return_order: bool = False, work_order: Optional[torch.Tensor] = None):
     """Per-query-block kv lists of a [B,H,nb,nb] mask (or one [nb,nb] plane broadcast
     over B, H) -> (row_ptr int32 [B*H*nb+1], col_idx int32 [B*H*nb*nb]); with
     return_order (or an `order` buffer) also the rows sorted by kept count,
-    descending, ties by row index (int32 [B*H*nb])."""
+    descending, ties by row index (int32 [B*H*nb]). With `work_order` (int32
+    [attn_work_order_slots]) the attention work order of the lists is written into it
+    in the same call (bsa_mask_to_csr_ordered); it cannot be combined with `order`."""
     lib = load()
     ptr, sb, sh, m = _mask_strides(mask)
     B = B or m.shape[0]
@@ -276,6 +280,12 @@ def mask_to_csr(mask: torch.Tensor, B: Optional[int] = None, H: Optional[int] = 
         col_idx = torch.empty(rows * nb, dtype=torch.int32, device=m.device)
     if ws is None:
         ws = _ws(lib.csr_workspace_size(B, H, nb), m.device)
+    if work_order is not None:
+        if order is not None or return_order:
+            raise ValueError("work_order cannot be combined with order")
+        _check(lib.bsa_mask_to_csr_ordered(ptr, sb, sh, B, H, nb, row_ptr.data_ptr(), col_idx.data_ptr(),
+                                           work_order.data_ptr(), ws.data_ptr(), ws.numel(), _stream(m.device)))
+        return row_ptr, col_idx
     if return_order and order is None:
         order = torch.empty(rows, dtype=torch.int32, device=m.device)
     _check(lib.bsa_mask_to_csr(ptr, sb, sh, B, H, nb, row_ptr.data_ptr(), col_idx.data_ptr(),

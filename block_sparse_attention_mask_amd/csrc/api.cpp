@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 7; }
+int bsa_abi_version(void) { return 8; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -305,6 +305,24 @@ bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh
   if (e != hipSuccess || !order) return hip_status(e, "csr launch");
   int32_t* sort_ws = (int32_t*)((char*)ws + align256(((size_t)rows + rows / 1024 + 1) * sizeof(int32_t)));
   return hip_status(bsa::launch_lpt_rows(row_ptr, rows, nb, sort_ws, order, (hipStream_t)stream), "order launch");
+}
+
+static int work_order_slots(const bsa_shape* s);
+
+bsa_status bsa_mask_to_csr_ordered(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H, int nb,
+                                   int32_t* row_ptr, int32_t* col_idx, int32_t* work_order, void* ws,
+                                   size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_mask_args(mask, mask_sb, mask_sh, B, H, nb)) != BSA_OK) return st;
+  if (!row_ptr || !col_idx || !work_order) return fail(BSA_EINVAL, "row_ptr / col_idx / work_order is NULL");
+  const bsa_shape shape = {B, H, nb * 64, nb * 64, 128, 64};
+  if (!work_order_slots(&shape)) return fail(BSA_EUNSUPPORTED, "this shape runs in the default order (0 slots)");
+  const size_t need = csr_workspace_size(B, H, nb);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  return hip_status(bsa::launch_csr(mask, mask_sb, mask_sh, B, H, nb, row_ptr, col_idx, (int32_t*)ws,
+                                    (hipStream_t)stream, work_order),
+                    "csr launch");
 }
 
 // ---------------------------------------------------------------------------

@@ -41,8 +41,11 @@ hipError_t launch_sta(const StaGeom& g, int32_t* tiles_ws, uint8_t* mask_out, hi
 // mask_ops.hip
 hipError_t launch_mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, int64_t b_n,
                           hipStream_t st);
+// with pair_order: also the attention work order of these lists (pair_schedule_fits must
+// hold); masks on the single-launch path get it from one extra workgroup of that launch
 hipError_t launch_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H, int nb,
-                      int32_t* row_ptr, int32_t* col_idx, int32_t* counts_ws, hipStream_t st);
+                      int32_t* row_ptr, int32_t* col_idx, int32_t* counts_ws, hipStream_t st,
+                      int32_t* pair_order = nullptr);
 // rows sorted by kept count (descending, ties by row index); workspace in int32s,
 // 0 when nb is too large for the sort
 size_t lpt_rows_ws_ints(int rows, int nk);

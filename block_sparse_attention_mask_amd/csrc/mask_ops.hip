@@ -120,12 +120,17 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(const uint8_t* __restrict
 // thread, 1024 threads; the mask is small, so the repeated reads stay in L2), stages its own rows
 // in shared memory, counts them with wave ballots, scans the counts, and writes
 // row_ptr and the ascending kept indices.
+constexpr int SCHED_RANGES = 8;   // XCD ranges of the attention work order (below)
+template <typename Cost>
+__device__ __forceinline__ void pair_schedule_block(Cost cost, int BH, int nb, int32_t* __restrict__ order, int* sm);
+
 constexpr int CSR_SMALL_ROWS = 4096;
 constexpr int CSR_SMALL_NB = 512;
 constexpr int CSR_SMALL_RPW = 64;                     // rows per workgroup
 __global__ __launch_bounds__(1024) void csr_small_kernel(const uint8_t* __restrict__ mask, int64_t sb, int64_t sh,
                                                         int H, int nb, int rows, int32_t* __restrict__ row_ptr,
-                                                        int32_t* __restrict__ col_idx) {
+                                                        int32_t* __restrict__ col_idx,
+                                                        int32_t* __restrict__ pair_order) {
   __shared__ __attribute__((aligned(16))) uint8_t own[CSR_SMALL_RPW * CSR_SMALL_NB];
   __shared__ int rc[CSR_SMALL_RPW];
   __shared__ int red[16];
@@ -148,10 +153,41 @@ __global__ __launch_bounds__(1024) void csr_small_kernel(const uint8_t* __restri
     }
     return n;
   };
+  constexpr int NL = 16;
+  if (pair_order && blockIdx.x == gridDim.x - 1) {
+    // the extra last workgroup: kept count of every row straight from the mask (in the
+    // row buffer), then the attention work order from them, beside the compaction
+    int* cnt = (int*)own;
+    for (int r = t; r < rows; r += 1024) cnt[r] = 0;
+    __syncthreads();
+    const int nall = rows * cpr;
+    for (int c0 = 0; c0 < nall; c0 += 1024 * NL) {
+      i32x4_t v[NL];
+#pragma unroll
+      for (int k = 0; k < NL; ++k) {
+        const int c = c0 + t + k * 1024;
+        v[k] = c < nall ? chunk(c) : i32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int k = 0; k < NL; ++k) {
+        const int c = c0 + t + k * 1024, n = nz16(v[k]);
+        if (c < nall && n) atomicAdd(&cnt[c / cpr], n);
+      }
+    }
+    __syncthreads();
+    extern __shared__ int sched_sm[];
+    const int npair = (nb + 1) / 2;
+    pair_schedule_block(
+        [&](int it) {
+          const int rA = (it / npair) * nb + 2 * (it % npair);
+          return max(cnt[rA], 2 * (it % npair) + 1 < nb ? cnt[rA + 1] : 0);
+        },
+        rows / nb, nb, pair_order, sched_sm);
+    return;
+  }
   // ---- stage the own rows
   for (int c = t; c < nown * cpr; c += 1024) *(i32x4_t*)(own + c * 16) = chunk(row0 * cpr + c);
   // ---- kept entries before row0
-  constexpr int NL = 16;
   int part = 0;
   const int nchunk = row0 * cpr;
   for (int c0 = 0; c0 < nchunk; c0 += 1024 * NL) {
@@ -198,15 +234,18 @@ __global__ __launch_bounds__(1024) void csr_small_kernel(const uint8_t* __restri
 }
 
 hipError_t launch_csr(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H, int nb, int32_t* row_ptr,
-                      int32_t* col_idx, int32_t* counts, hipStream_t st) {
+                      int32_t* col_idx, int32_t* counts, hipStream_t st, int32_t* pair_order) {
   const int rows = B * H * nb;
   const bool dense = (H == 1 || sh == (int64_t)nb * nb) && (B == 1 || sb == (int64_t)H * nb * nb) && (sb || sh);
   const bool plane = sb == 0 && sh == 0;
   if (nb % 16 == 0 && ((uintptr_t)mask & 15) == 0 && (dense || plane) && rows <= CSR_SMALL_ROWS &&
       nb <= CSR_SMALL_NB) {
     if (dense) sb = 1;                                 // kernel: sb == 0 means one repeated plane
-    hipLaunchKernelGGL(csr_small_kernel, dim3((rows + CSR_SMALL_RPW - 1) / CSR_SMALL_RPW), dim3(1024), 0, st, mask, sb,
-                       sh, H, nb, rows, row_ptr, col_idx);
+    // with a pair order: one more workgroup, which builds it from the mask's row counts
+    const unsigned g = (rows + CSR_SMALL_RPW - 1) / CSR_SMALL_RPW + (pair_order ? 1 : 0);
+    const size_t dyn = pair_order ? (size_t)2 * SCHED_RANGES * (nb + 1) * 4 : 0;
+    hipLaunchKernelGGL(csr_small_kernel, dim3(g), dim3(1024), dyn, st, mask, sb, sh, H, nb, rows, row_ptr, col_idx,
+                       pair_order);
     return hipGetLastError();
   }
   const unsigned g = (unsigned)((rows + 3) / 4);
@@ -224,7 +263,9 @@ hipError_t launch_csr(const uint8_t* mask, int64_t sb, int64_t sh, int B, int H,
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(csr_fill_kernel, dim3(g), dim3(256), 0, st, mask, sb, sh, H, nb, rows,
                      (const int32_t*)row_ptr, col_idx);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !pair_order) return e;
+  return launch_pair_schedule(row_ptr, B * H, nb, pair_order, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -366,10 +407,8 @@ hipError_t launch_lpt_rows(const int32_t* row_ptr, int rows, int nb, int32_t* ws
 // the item of position x / 8 in range x % 8, or -1.
 // One workgroup of 1024 threads does it all in shared memory: per-range key
 // histograms, a descending scan per range, and a scatter with shared-memory atomics.
-constexpr int SCHED_RANGES = 8;
-__global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __restrict__ row_ptr, int BH, int nb,
-                                                             int32_t* __restrict__ order) {
-  extern __shared__ int sm[];
+template <typename Cost>
+__device__ __forceinline__ void pair_schedule_block(Cost cost, int BH, int nb, int32_t* __restrict__ order, int* sm) {
   const int nk = nb + 1, npair = (nb + 1) / 2, items = BH * npair;
   const int maxg = (items + SCHED_RANGES - 1) / SCHED_RANGES;
   int* hist = sm;                                    // [ranges][nk]
@@ -386,11 +425,7 @@ __global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __re
     const int it = t + r * 1024;
     key[r] = -1;
     if (it < items) {
-      const int bh = it / npair, i = 2 * (it % npair);
-      const int rA = bh * nb + i;
-      const int cA = row_ptr[rA + 1] - row_ptr[rA];
-      const int cB = i + 1 < nb ? row_ptr[rA + 2] - row_ptr[rA + 1] : 0;
-      key[r] = max(cA, cB);
+      key[r] = cost(it);
       grp[r] = (int)(((int64_t)it * SCHED_RANGES) / items);
       atomicAdd(&hist[grp[r] * nk + key[r]], 1);
     }
@@ -426,6 +461,21 @@ __global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __re
   // slots past the end of a range
   for (int x = t; x < maxg * SCHED_RANGES; x += 1024)
     if (x / SCHED_RANGES >= gsize[x % SCHED_RANGES]) order[x] = -1;
+}
+
+__global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __restrict__ row_ptr, int BH, int nb,
+                                                             int32_t* __restrict__ order) {
+  extern __shared__ int sm[];
+  const int npair = (nb + 1) / 2;
+  pair_schedule_block(
+      [&](int it) {
+        const int bh = it / npair, i = 2 * (it % npair);
+        const int rA = bh * nb + i;
+        const int cA = row_ptr[rA + 1] - row_ptr[rA];
+        const int cB = i + 1 < nb ? row_ptr[rA + 2] - row_ptr[rA + 1] : 0;
+        return max(cA, cB);
+      },
+      BH, nb, order, sm);
 }
 
 bool pair_schedule_fits(int BH, int nb) {

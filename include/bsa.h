@@ -187,6 +187,20 @@ bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh
                            int nb, int32_t* row_ptr, int32_t* col_idx, int32_t* order, void* ws,
                            size_t ws_bytes, bsa_stream_t stream);
 
+/* The same kv lists plus the attention kernel's work order for them (the order
+ * attn_work_order writes; see block_sparse_attn_fwd below) in one call. For small masks
+ * (B*H*nb <= 4096 rows, nb a multiple of 16 and <= 512, contiguous or one plane) both come
+ * from a single launch, the order built by one extra workgroup from the mask's row
+ * counts beside the compaction; otherwise the order is a second launch.
+ *   work_order int32 [attn_work_order_slots(shape)] for a shape with these B, H and
+ *              S = 64 nb; BSA_EUNSUPPORTED when that is 0 (the shape runs in the
+ *              default order)
+ * Other arguments, workspace and errors as bsa_mask_to_csr. Equal keys may be ordered
+ * differently from attn_work_order's; the attention results never depend on the order. */
+bsa_status bsa_mask_to_csr_ordered(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H,
+                                   int nb, int32_t* row_ptr, int32_t* col_idx, int32_t* work_order,
+                                   void* ws, size_t ws_bytes, bsa_stream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Block-sparse attention forward [FA: exact tiled attention with online softmax,
  * extended to block-sparse attention; NABLA: the mask tells the operator which

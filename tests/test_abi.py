@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 7
+    assert lib.bsa_abi_version() == 8
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
@@ -90,6 +90,14 @@ def test_mask_or_and_csr_reject(lib):
     assert lib.mask_or(None, 4096, 10, 8192, 10, None) == 1
     assert lib.bsa_mask_to_csr(4096, -1, 0, 1, 1, 4, 8192, 8192, None, 8192, 1 << 20, None) == 1
     assert lib.bsa_mask_to_csr(4096, 0, 0, 1, 1, 4, 8192, 8192, None, 8192, 0, None) == 3
+    # kv lists with the attention work order: NULL order, bad stride, a shape that runs in
+    # the default order (64 heads x 64 pairs = 4096 items > 4 rounds), too small a workspace
+    f = lib.bsa_mask_to_csr_ordered
+    assert f(4096, 0, 0, 1, 16, 128, 8192, 8192, None, 8192, 1 << 20, None) == 1
+    assert f(4096, -1, 0, 1, 16, 128, 8192, 8192, 8192, 8192, 1 << 20, None) == 1
+    assert f(4096, 0, 0, 1, 64, 128, 8192, 8192, 8192, 8192, 1 << 20, None) == 2
+    assert "default order" in lib.bsa_last_error().decode()
+    assert f(4096, 0, 0, 1, 16, 128, 8192, 8192, 8192, 8192, 0, None) == 3
 
 
 def test_attention_rejects(lib):

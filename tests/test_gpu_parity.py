@@ -347,6 +347,43 @@ def test_attention_work_order(gpu_lib):
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
+@pytest.mark.parametrize("heads", [16, 48])
+def test_csr_with_work_order_one_call(gpu_lib, heads):
+    """bsa_mask_to_csr_ordered: the same kv lists as bsa_mask_to_csr and the work order
+    attn_work_order gives for them (per XCD range the same pairs with the same decreasing
+    keys; equal keys may come in another order), identical attention results. 16 heads
+    (2048 rows) take the single-launch path, 48 heads (6144 rows) the two-launch one."""
+    cfg = get_config(2, heads=heads)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    plane = _gpu_sta(gpu_lib, cfg)
+    mask = gpu_lib.nabla_build_mask(q, k, cfg.thrs[0], or_mask=plane)
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    ref = gpu_lib.attn_work_order(q, rp)
+    assert ref is not None
+    wo = torch.full_like(ref, -7)
+    rp2, ci2 = gpu_lib.mask_to_csr(mask, work_order=wo)
+    torch.cuda.synchronize()
+    assert torch.equal(rp, rp2)
+    n = int(rp[-1].item())
+    assert torch.equal(ci[:n], ci2[:n])
+    counts = np.diff(rp.cpu().numpy())
+    npair = cfg.nb // 2
+    o, r = wo.cpu().numpy(), ref.cpu().numpy()
+    assert not (o == -7).any()
+    for x in range(8):
+        a, b = o[x::8], r[x::8]
+        assert np.array_equal(a < 0, b < 0)
+        a, b = a[a >= 0], b[b >= 0]
+        assert sorted(a.tolist()) == sorted(b.tolist())
+        ka = np.maximum(counts[(a // npair) * cfg.nb + 2 * (a % npair)], counts[(a // npair) * cfg.nb + 2 * (a % npair) + 1])
+        kb = np.maximum(counts[(b // npair) * cfg.nb + 2 * (b % npair)], counts[(b // npair) * cfg.nb + 2 * (b % npair) + 1])
+        assert np.array_equal(ka, kb)
+    out_a = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp2, ci2, work_order=wo)
+    out_b = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, work_order=ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+
+
 def test_longest_first_order_large(gpu_lib):
     """Several sort blocks and many equal counts (rows of a 40-head, nb=1182 mask with
     counts from a narrow band), and the largest nb the order supports in one head."""
