@@ -83,10 +83,17 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
     st = {}
 
     def phase_mask():
+        m = mask
+        if use_nabla and not fp8 and cfg.sta is not None:
+            # NABLA OR sliding tiles in one call (the rule inside the selection where the
+            # layout allows it)
+            bsa.nabla_build_mask_sta(q, k, thr, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                                     order_tile=cfg.order_tile, s_valid=cfg.S_valid, out=mask)
+            st["m"] = m
+            return
         if cfg.sta is not None and not dense:
             bsa.sta_build_mask(S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
                                order_tile=cfg.order_tile, device=dev, out=plane)
-        m = mask
         if use_nabla and fp8:
             bsa.nabla_build_mask_fp8(q, k, thr, or_mask=plane if cfg.sta is not None else None, out=mask,
                                      q8_out=(qa, qs), k8_out=(ka, ks))

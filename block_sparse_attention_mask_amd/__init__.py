@@ -23,7 +23,7 @@ _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPA
 # every function the C header declares, in declaration order
 EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_topk", "quantize_fp8_blocks",
            "nabla_build_mask_fp8",
-           "sta_workspace_size", "sta_build_mask", "mask_or",
+           "sta_workspace_size", "sta_build_mask", "nabla_sta_workspace_size", "nabla_build_mask_sta", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "bsa_mask_to_csr_ordered", "attn_workspace_size",
            "block_sparse_attn_fwd",
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
@@ -71,6 +71,8 @@ def load(path: Optional[str] = None):
         "nabla_build_mask_fp8": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, PT, vp, PT, vp, vp, sz, vp]),
         "sta_workspace_size": (sz, [PS]),
         "sta_build_mask": (i32, [PS, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
+        "nabla_sta_workspace_size": (sz, [PS]),
+        "nabla_build_mask_sta": (i32, [PT, PT, PS, dbl, dbl, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
         "mask_or": (i32, [vp, vp, i64, vp, i64, vp]),
         "csr_workspace_size": (sz, [i32, i32, i32]),
         "bsa_mask_to_csr": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
@@ -244,6 +246,29 @@ def sta_build_mask(S: int, S_valid: int, grid: Sequence[int], tile: Sequence[int
     _check(lib.sta_build_mask(ctypes.byref(shp), arr(*grid), arr(*tile), arr(*window),
                               0 if order == "row" else 1, ot, out.data_ptr(), ws.data_ptr(), ws.numel(),
                               _stream(dev)))
+    return out
+
+
+def nabla_build_mask_sta(q: torch.Tensor, k: torch.Tensor, thr: float, grid: Sequence[int], tile: Sequence[int],
+                         window: Sequence[int], order: str = "row", order_tile: Optional[Sequence[int]] = None,
+                         s_valid: Optional[int] = None, scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """NABLA mask of q, k OR'd with the sliding-tile mask of the grid in one call
+    -> uint8 [B,H,S/64,S/64] (equal to nabla_build_mask(..., or_mask=sta_build_mask(...)))."""
+    lib = load()
+    B, H, S, D = q.shape
+    nb = S // 64
+    shp = _shape(q, s_valid)
+    if out is None:
+        out = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device)
+    ws = _ws(lib.nabla_sta_workspace_size(ctypes.byref(shp)), q.device)
+    arr = ctypes.c_int * 3
+    ot = arr(*order_tile) if order_tile is not None else None
+    tq, tk = _tensor(q), _tensor(k)
+    _check(lib.nabla_build_mask_sta(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
+                                    float(scale) if scale else 0.0, arr(*grid), arr(*tile), arr(*window),
+                                    0 if order == "row" else 1, ot, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                    _stream(q.device)))
     return out
 
 

@@ -92,7 +92,9 @@ size_t nabla_workspace_size(const bsa_shape* s) {
 static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                                uint8_t* mask_out, const bsa::Fp8Out* f8, void* ws, size_t ws_bytes,
-                               bsa_stream_t stream, int topk = 0) {
+                               bsa_stream_t stream, int topk = 0, bsa::StaRule sta = {0, 0, 0, 0, 0, 0},
+                               const bsa::StaGeom* plane_geom = nullptr, uint8_t* plane = nullptr,
+                               void* sta_ws = nullptr) {
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
   if ((st = check_tensor("q", q, shape)) != BSA_OK) return st;
@@ -115,12 +117,18 @@ static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const b
   double* kbarT = (double*)((char*)ws + align256(bh * nbp * (size_t)shape->D * sizeof(double)));
   const int64_t qs[3] = {q->sb, q->sh, q->ss}, ks[3] = {k->sb, k->sh, k->ss};
   hipStream_t hs = (hipStream_t)stream;
+  if (plane_geom) {   // a sliding-tile plane to build (after validation) and OR in
+    hipError_t e = bsa::launch_sta(*plane_geom, (int32_t*)sta_ws, plane, hs);
+    if (e != hipSuccess) return hip_status(e, "sta launch");
+    or_mask = plane;
+    or_sb = or_sh = 0;
+  }
   hipError_t e = bsa::launch_pool(q->dtype == BSA_F32, shape->D, q->ptr, qs, k->ptr, ks, shape->B, shape->H, nb,
                                   qbar, kbarT, f8, hs);
   if (e != hipSuccess) return hip_status(e, "pool launch");
   const uint64_t T_fixed = (uint64_t)std::ldexp(1.0 - thr, 60);
   e = bsa::launch_select(qbar, kbarT, shape->B, shape->H, nb, shape->D, scale, T_fixed, topk, or_mask, or_sb,
-                         or_sh, mask_out, hs);
+                         or_sh, sta, mask_out, hs);
   return hip_status(e, "select launch");
 }
 
@@ -194,12 +202,9 @@ size_t sta_workspace_size(const bsa_shape* s) {
   return align256((size_t)(s->S / 64) * (bsa::STA_MAX_TILES + 1) * sizeof(int32_t));
 }
 
-bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
-                          int token_order, const int order_tile_thw[3], uint8_t* mask_out, void* ws, size_t ws_bytes,
-                          bsa_stream_t stream) {
-  g_err.clear();
-  bsa_status st;
-  if ((st = check_shape(shape, false)) != BSA_OK) return st;
+// sliding-tile arguments -> geometry (shape already checked)
+static bsa_status sta_geom_from(const bsa_shape* shape, const int grid_thw[3], const int tile_thw[3],
+                                const int win_thw[3], int token_order, const int order_tile_thw[3], bsa::StaGeom* g) {
   if (!grid_thw || !tile_thw || !win_thw) return fail(BSA_EINVAL, "grid/tile/window arrays must not be NULL");
   if (token_order != 0 && token_order != 1) return fail(BSA_EINVAL, "token_order=%d (0 row-major, 1 tile-major)", token_order);
   if (token_order == 1 && !order_tile_thw) return fail(BSA_EINVAL, "order_tile_thw is NULL for tile-major order");
@@ -214,20 +219,58 @@ bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const i
   const int64_t cells = (int64_t)grid_thw[0] * grid_thw[1] * grid_thw[2];
   if (cells != shape->S_valid)
     return fail(BSA_EINVAL, "T*H*W=%lld must equal S_valid=%d", (long long)cells, shape->S_valid);
+  g->T = grid_thw[0]; g->H = grid_thw[1]; g->W = grid_thw[2];
+  g->tt = tile_thw[0]; g->th = tile_thw[1]; g->tw = tile_thw[2];
+  g->rt = win_thw[0] / 2; g->rh = win_thw[1] / 2; g->rw = win_thw[2] / 2;
+  g->order = token_order;
+  g->ot = token_order ? order_tile_thw[0] : 1;
+  g->oh = token_order ? order_tile_thw[1] : 1;
+  g->ow = token_order ? order_tile_thw[2] : 1;
+  g->S_valid = shape->S_valid;
+  g->nb = shape->S / 64;
+  return BSA_OK;
+}
+
+bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
+                          int token_order, const int order_tile_thw[3], uint8_t* mask_out, void* ws, size_t ws_bytes,
+                          bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape, false)) != BSA_OK) return st;
+  bsa::StaGeom g;
+  if ((st = sta_geom_from(shape, grid_thw, tile_thw, win_thw, token_order, order_tile_thw, &g)) != BSA_OK) return st;
   if (!mask_out) return fail(BSA_EINVAL, "mask_out is NULL");
   const size_t need = sta_workspace_size(shape);
   if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
-  bsa::StaGeom g;
-  g.T = grid_thw[0]; g.H = grid_thw[1]; g.W = grid_thw[2];
-  g.tt = tile_thw[0]; g.th = tile_thw[1]; g.tw = tile_thw[2];
-  g.rt = win_thw[0] / 2; g.rh = win_thw[1] / 2; g.rw = win_thw[2] / 2;
-  g.order = token_order;
-  g.ot = token_order ? order_tile_thw[0] : 1;
-  g.oh = token_order ? order_tile_thw[1] : 1;
-  g.ow = token_order ? order_tile_thw[2] : 1;
-  g.S_valid = shape->S_valid;
-  g.nb = shape->S / 64;
   return hip_status(bsa::launch_sta(g, (int32_t*)ws, mask_out, (hipStream_t)stream), "sta launch");
+}
+
+size_t nabla_sta_workspace_size(const bsa_shape* s) {
+  if (!s || s->S <= 0 || s->D <= 0) return 0;
+  const size_t nb = (size_t)s->S / 64;
+  return nabla_workspace_size(s) + align256(nb * nb) + sta_workspace_size(s);
+}
+
+bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                                double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
+                                int token_order, const int order_tile_thw[3], uint8_t* mask_out, void* ws,
+                                size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  bsa::StaGeom g;
+  if ((st = sta_geom_from(shape, grid_thw, tile_thw, win_thw, token_order, order_tile_thw, &g)) != BSA_OK) return st;
+  const size_t need = nabla_sta_workspace_size(shape);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+  const bsa::StaRule rule = bsa::sta_rule_of(g);
+  const size_t nws = nabla_workspace_size(shape);
+  if (rule.bpt)   // aligned layout: the rule is applied inside the select
+    return nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule);
+  // otherwise the sliding-tile plane is built in the workspace and OR'd like any mask
+  const size_t nb = (size_t)shape->S / 64;
+  return nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule, &g,
+                      (uint8_t*)ws + nws, (char*)ws + nws + align256(nb * nb));
 }
 
 // ---------------------------------------------------------------------------

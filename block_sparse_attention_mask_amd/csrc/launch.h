@@ -20,11 +20,24 @@ struct Fp8Out {
 hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* q_strides, const void* k,
                        const int64_t* k_strides, int B, int H, int nb, double* qbar, double* kbarT,
                        const Fp8Out* f8, hipStream_t st);
+// The sliding-tile rule of tile-major layouts made of whole tiles of whole blocks: block
+// i lies in tile i / bpt of a row-major tile grid with GH x GW tiles per frame of tiles;
+// blocks i and j are kept together when their tiles are within (rt, rh, rw) of each
+// other on every axis. bpt == 0: no rule.
+struct StaRule {
+  int bpt, GH, GW, rt, rh, rw;
+};
+__device__ __forceinline__ bool sta_rule_keep(const StaRule& s, int i, int j) {
+  const int ti = i / s.bpt, tj = j / s.bpt, per = s.GH * s.GW;
+  return abs(ti / per - tj / per) <= s.rt && abs((ti / s.GW) % s.GH - (tj / s.GW) % s.GH) <= s.rh &&
+         abs(ti % s.GW - tj % s.GW) <= s.rw;
+}
 // T_fixed = floor((1 - thr) 2^60) for the cumulative-mass rule; topk > 0 keeps the
-// topk largest entries of each row instead (T_fixed unused)
+// topk largest entries of each row instead (T_fixed unused). The result is OR'd with
+// or_mask (if any) and with the sliding-tile rule sta (if sta.bpt > 0).
 hipError_t launch_select(const double* qbar, const double* kbarT, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                         uint8_t* mask_out, hipStream_t st);
+                         StaRule sta, uint8_t* mask_out, hipStream_t st);
 
 // sta.hip
 struct StaGeom {
@@ -37,6 +50,9 @@ struct StaGeom {
 };
 constexpr int STA_MAX_TILES = 64;   // distinct window tiles touched by one 64-token block
 hipError_t launch_sta(const StaGeom& g, int32_t* tiles_ws, uint8_t* mask_out, hipStream_t st);
+// the rule of g when its layout is aligned (tile-major, whole tiles, tiles of whole
+// blocks, no padding), else {0}
+StaRule sta_rule_of(const StaGeom& g);
 
 // mask_ops.hip
 hipError_t launch_mask_or(uint8_t* dst, const uint8_t* a, int64_t n, const uint8_t* b, int64_t b_n,

@@ -275,7 +275,8 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
                                                                const double* __restrict__ kmf, int nb, int D,
                                                                double scale, uint64_t T_fixed, int topk,
                                                                const uint8_t* __restrict__ or_mask, int64_t or_sb,
-                                                               int64_t or_sh, int H, uint8_t* __restrict__ mask_out) {
+                                                               int64_t or_sh, StaRule sta, int H,
+                                                               uint8_t* __restrict__ mask_out) {
   const bool by_count = topk > 0;
   const uint64_t target = by_count ? (uint64_t)topk : T_fixed;
   __shared__ uint64_t hmass[SEL_ROWS][256];
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
           keep = rank < sr.tie_keep;
         }
       }
-      if (om && om[j]) keep = true;
+      if ((om && om[j]) || (sta.bpt && sta_rule_keep(sta, row, j))) keep = true;
       dst[j] = keep ? 1 : 0;
     }
   }
@@ -531,8 +532,8 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
                                                                     const double* __restrict__ kmf, int nb,
                                                                     double scale, uint64_t T_fixed, int topk,
                                                                     const uint8_t* __restrict__ or_mask,
-                                                                    int64_t or_sb, int64_t or_sh, int H,
-                                                                    uint8_t* __restrict__ mask_out) {
+                                                                    int64_t or_sb, int64_t or_sh, StaRule sta,
+                                                                    int H, uint8_t* __restrict__ mask_out) {
   constexpr int E = 2 * NCT;                        // entries per lane per row
   constexpr int NBP = SEL_WAVES * 16 * NCT;         // map row length
   const bool by_count = topk > 0;
@@ -681,7 +682,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
       if (sr.status == ROW_ALL) keep = true;
       else if (sr.status == ROW_PIVOT) keep = key[e] >= sr.lo;
       else keep = tied ? rank < sr.tie_keep : key[e] > sr.lo;
-      if (om && om[j]) keep = true;
+      if ((om && om[j]) || (sta.bpt && sta_rule_keep(sta, row, j))) keep = true;
       dst[j] = keep ? 1 : 0;
     }
   }
@@ -728,43 +729,44 @@ hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* qs, const 
 template <int NCT>
 static hipError_t launch_select_c(const double* qmf, const double* kmf, int B, int H, int nb, int D,
                                   double scale, uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb,
-                                  int64_t or_sh, uint8_t* mask_out, hipStream_t st) {
+                                  int64_t or_sh, StaRule sta, uint8_t* mask_out, hipStream_t st) {
   dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS, B * H);
   if (D == 64)
     hipLaunchKernelGGL((select_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
   else
     hipLaunchKernelGGL((select_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
   return hipGetLastError();
 }
 
 template <int NCT>
 static hipError_t launch_select_rows(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
                                      uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                                     uint8_t* mask_out, hipStream_t st) {
+                                     StaRule sta, uint8_t* mask_out, hipStream_t st) {
   dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS, B * H);
   if (D == 64)
     hipLaunchKernelGGL((select_rows_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
   else
     hipLaunchKernelGGL((select_rows_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                         uint8_t* mask_out, hipStream_t st) {
+                         StaRule sta, uint8_t* mask_out, hipStream_t st) {
   const int ntile = (nb + 15) / 16;
   const int nct = (ntile + SEL_WAVES - 1) / SEL_WAVES;
   if (nb <= SELR_MAX_NB) {
     if (nct == 1)
-      return launch_select_rows<1>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, mask_out, st);
-    return launch_select_rows<2>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, mask_out, st);
+      return launch_select_rows<1>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out,
+                                   st);
+    return launch_select_rows<2>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st);
   }
 #define BSA_SEL_CASE(n) \
-  case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, mask_out, st);
+  case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st);
   switch (nct) {
     BSA_SEL_CASE(1) BSA_SEL_CASE(2) BSA_SEL_CASE(3) BSA_SEL_CASE(4) BSA_SEL_CASE(5) BSA_SEL_CASE(6)
     BSA_SEL_CASE(7) BSA_SEL_CASE(8) BSA_SEL_CASE(9) BSA_SEL_CASE(10) BSA_SEL_CASE(11) BSA_SEL_CASE(12)

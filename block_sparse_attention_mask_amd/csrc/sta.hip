@@ -111,26 +111,25 @@ __global__ __launch_bounds__(256) void sta_pairs_kernel(StaGeom g, const int32_t
 // (every grid extent a multiple of the tile), a tile a whole number of 64-token
 // blocks, no padding. Then every block lies inside one tile, block i's tile is i / bpt,
 // and the any-pair rule reduces to the tile-distance test; one kernel, O(1) per pair.
-__global__ __launch_bounds__(256) void sta_aligned_kernel(StaGeom g, int bpt, uint8_t* __restrict__ mask) {
-  const int GH = g.H / g.th, GW = g.W / g.tw;
+__global__ __launch_bounds__(256) void sta_aligned_kernel(StaRule r, int nb, uint8_t* __restrict__ mask) {
   const int i = blockIdx.x;
-  const int ti = i / bpt;
-  const int a0 = ti / (GH * GW), a1 = (ti / GW) % GH, a2 = ti % GW;
-  for (int j = threadIdx.x; j < g.nb; j += 256) {
-    const int tj = j / bpt;
-    const int c0 = tj / (GH * GW), c1 = (tj / GW) % GH, c2 = tj % GW;
-    const bool keep = abs(a0 - c0) <= g.rt && abs(a1 - c1) <= g.rh && abs(a2 - c2) <= g.rw;
-    mask[(int64_t)i * g.nb + j] = keep ? 1 : 0;
-  }
+  for (int j = threadIdx.x; j < nb; j += 256) mask[(int64_t)i * nb + j] = sta_rule_keep(r, i, j) ? 1 : 0;
 }
 
-hipError_t launch_sta(const StaGeom& g, int32_t* tiles_ws, uint8_t* mask_out, hipStream_t st) {
+StaRule sta_rule_of(const StaGeom& g) {
   const int tile_tokens = g.tt * g.th * g.tw;
   const bool aligned = g.order == 1 && g.ot == g.tt && g.oh == g.th && g.ow == g.tw && g.T % g.tt == 0 &&
                        g.H % g.th == 0 && g.W % g.tw == 0 && tile_tokens % BSA_N == 0 &&
                        g.S_valid == g.T * g.H * g.W && g.S_valid == g.nb * BSA_N;
-  if (aligned) {
-    hipLaunchKernelGGL(sta_aligned_kernel, dim3(g.nb), dim3(256), 0, st, g, tile_tokens / BSA_N, mask_out);
+  StaRule r = {0, 0, 0, 0, 0, 0};
+  if (aligned) r = {tile_tokens / BSA_N, g.H / g.th, g.W / g.tw, g.rt, g.rh, g.rw};
+  return r;
+}
+
+hipError_t launch_sta(const StaGeom& g, int32_t* tiles_ws, uint8_t* mask_out, hipStream_t st) {
+  const StaRule r = sta_rule_of(g);
+  if (r.bpt) {
+    hipLaunchKernelGGL(sta_aligned_kernel, dim3(g.nb), dim3(256), 0, st, r, g.nb, mask_out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(sta_tiles_kernel, dim3((g.nb + 3) / 4), dim3(256), 0, st, g, tiles_ws);

@@ -163,6 +163,24 @@ bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const i
                           uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * NABLA mask OR'd with the sliding-tile mask in one call [NABLA: the adaptive mask
+ * combined with STA]. The result equals nabla_build_mask with or_mask = the
+ * sta_build_mask plane of (grid_thw, tile_thw, win_thw, token_order, order_tile_thw) for
+ * every head. For tile-major layouts of whole tiles made of whole blocks (no padding)
+ * the sliding-tile rule is evaluated inside the selection and no plane is built;
+ * otherwise the plane is built in the workspace first.
+ *   q, k, shape, thr, scale, mask_out   as nabla_build_mask
+ *   grid_thw .. order_tile_thw          as sta_build_mask (T*H*W must equal S_valid)
+ *   ws         at least nabla_sta_workspace_size(shape) bytes, 256-byte aligned
+ * Errors as the two calls; every check precedes any launch.
+ * ------------------------------------------------------------------------- */
+size_t nabla_sta_workspace_size(const bsa_shape* shape);
+bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                                double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
+                                int token_order, const int order_tile_thw[3], uint8_t* mask_out, void* ws,
+                                size_t ws_bytes, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Union of block masks [NABLA: adaptive mask OR sliding-tile mask].
  *   dst[i] = (a[i] | b[i % b_n]) != 0 for 0 <= i < n; b_n divides n (b_n == n is a
  *   plain elementwise OR; b_n == nb*nb broadcasts one plane over every head).

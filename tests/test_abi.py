@@ -85,6 +85,28 @@ def test_sta_rejects_bad_geometry(lib):
     assert st == 1
 
 
+def test_nabla_sta_rejects(lib):
+    # NABLA OR sliding tiles in one call: the checks of both calls, before any launch
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    a3 = ctypes.c_int * 3
+    q, k = _t(), _t(4096)
+    f = lib.nabla_build_mask_sta
+    need = lib.nabla_sta_workspace_size(ctypes.byref(shape))
+    assert need >= lib.nabla_workspace_size(ctypes.byref(shape)) + 16
+    st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 0.1, 0.0, a3(4, 8, 8), a3(4, 8, 8), a3(3, 2, 3), 0,
+           None, 8192, 1 << 16, need, None)
+    assert st == 1 and "odd" in lib.bsa_last_error().decode()
+    st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 0.1, 0.0, a3(4, 8, 9), a3(4, 8, 8), a3(3, 3, 3), 0,
+           None, 8192, 1 << 16, need, None)
+    assert st == 1 and "S_valid" in lib.bsa_last_error().decode()
+    st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 0.1, 0.0, a3(4, 8, 8), a3(4, 8, 8), a3(3, 3, 3), 0,
+           None, 8192, 1 << 16, need - 1, None)
+    assert st == 3
+    st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 1.5, 0.0, a3(4, 8, 8), a3(4, 8, 8), a3(3, 3, 3), 0,
+           None, 8192, 1 << 16, need, None)
+    assert st == 1 and "thr" in lib.bsa_last_error().decode()
+
+
 def test_mask_or_and_csr_reject(lib):
     assert lib.mask_or(4096, 4096, 10, 8192, 3, None) == 1
     assert lib.mask_or(None, 4096, 10, 8192, 10, None) == 1

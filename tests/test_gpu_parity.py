@@ -119,6 +119,22 @@ def test_sta_ragged_geometries(gpu_lib, grid, order, otile, tile, window):
     assert np.array_equal(g.cpu().numpy().astype(bool), ref)
 
 
+@pytest.mark.parametrize("cid,heads,thr", [(2, None, 0.1), (4, 2, 0.3), (5, 3, 0.2)])
+def test_nabla_sta_one_call(gpu_lib, cid, heads, thr):
+    """nabla_build_mask_sta equals nabla_build_mask OR'd with the sta_build_mask plane, bit
+    for bit: aligned tile-major layouts (configs 2 and 4: the rule inside the short-row and
+    the wide select) and a padded row-major one (config 5: the plane built first)."""
+    cfg = get_config(cid, heads)
+    q, k, _ = make_inputs(cfg, seed=0, device=DEV)
+    plane = _gpu_sta(gpu_lib, cfg)
+    ref = gpu_lib.nabla_build_mask(q, k, thr, or_mask=plane)
+    one = gpu_lib.nabla_build_mask_sta(q, k, thr, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                                       order_tile=cfg.order_tile, s_valid=cfg.S_valid)
+    torch.cuda.synchronize()
+    print(f"[nabla+sta] config {cid} nb {cfg.nb} kept {ref.float().mean().item():.4f}", flush=True)
+    assert torch.equal(ref, one)
+
+
 def test_mask_or_and_csr(gpu_lib):
     rng = np.random.default_rng(0)
     a = rng.random((2, 3, 37, 37)) < 0.2
