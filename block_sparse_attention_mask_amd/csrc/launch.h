@@ -27,10 +27,18 @@ hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* q_strides,
 struct StaRule {
   int bpt, GH, GW, rt, rh, rw;
 };
+struct StaCoord {
+  int t, h, w;   // tile coordinates of a block
+};
+__device__ __forceinline__ StaCoord sta_rule_coord(const StaRule& s, int i) {
+  const int ti = i / s.bpt;
+  return {ti / (s.GH * s.GW), (ti / s.GW) % s.GH, ti % s.GW};
+}
+__device__ __forceinline__ bool sta_rule_near(const StaRule& s, StaCoord a, StaCoord c) {
+  return abs(a.t - c.t) <= s.rt && abs(a.h - c.h) <= s.rh && abs(a.w - c.w) <= s.rw;
+}
 __device__ __forceinline__ bool sta_rule_keep(const StaRule& s, int i, int j) {
-  const int ti = i / s.bpt, tj = j / s.bpt, per = s.GH * s.GW;
-  return abs(ti / per - tj / per) <= s.rt && abs((ti / s.GW) % s.GH - (tj / s.GW) % s.GH) <= s.rh &&
-         abs(ti % s.GW - tj % s.GW) <= s.rw;
+  return sta_rule_near(s, sta_rule_coord(s, i), sta_rule_coord(s, j));
 }
 // T_fixed = floor((1 - thr) 2^60) for the cumulative-mass rule; topk > 0 keeps the
 // topk largest entries of each row instead (T_fixed unused). The result is OR'd with

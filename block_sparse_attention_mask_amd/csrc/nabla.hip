@@ -475,14 +475,19 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
     __syncthreads();
   }
 
-  // ---- write the mask rows (OR'd with the optional mask)
+  // ---- write the mask rows (OR'd with the optional mask and the sliding-tile rule;
+  // the rule's tile coordinates of this lane's columns are formed once)
   const int b = bh / H, h = bh % H;
+  StaCoord cc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) cc[c] = sta.bpt ? sta_rule_coord(sta, min(colof(c), nb - 1)) : StaCoord{0, 0, 0};
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int r = 4 * v + g;
     const SelRowState sr = st[r];
     if (sr.status == ROW_SKIP) continue;
     const int row = row0 + r;
+    const StaCoord rc = sta.bpt ? sta_rule_coord(sta, row) : StaCoord{0, 0, 0};
     uint8_t* dst = mask_out + ((int64_t)bh * nb + row) * nb;
     const uint8_t* om = or_mask ? or_mask + b * or_sb + h * or_sh + (int64_t)row * nb : nullptr;
 #pragma unroll
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
           keep = rank < sr.tie_keep;
         }
       }
-      if ((om && om[j]) || (sta.bpt && sta_rule_keep(sta, row, j))) keep = true;
+      if ((om && om[j]) || (sta.bpt && sta_rule_near(sta, rc, cc[c]))) keep = true;
       dst[j] = keep ? 1 : 0;
     }
   }
@@ -559,9 +564,13 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
   __syncthreads();
 
   const int b = bh / H, h = bh % H;
+  StaCoord cc[E];   // the sliding-tile rule's tile coordinates of this lane's columns
+#pragma unroll
+  for (int e = 0; e < E; ++e) cc[e] = sta.bpt ? sta_rule_coord(sta, min(64 * e + l, nb - 1)) : StaCoord{0, 0, 0};
   for (int rr = 0; rr < SEL_ROWS / SEL_WAVES; ++rr) {
     const int r = (SEL_ROWS / SEL_WAVES) * w + rr, row = row0 + r;
     if (row >= nb) break;                            // wave-uniform
+    const StaCoord rc = sta.bpt ? sta_rule_coord(sta, row) : StaCoord{0, 0, 0};
     // ---- softmax of the row in fp64, then the fixed-point mass w = floor(p 2^60) (the key)
     bool valid[E];
     double x[E];
@@ -682,7 +691,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
       if (sr.status == ROW_ALL) keep = true;
       else if (sr.status == ROW_PIVOT) keep = key[e] >= sr.lo;
       else keep = tied ? rank < sr.tie_keep : key[e] > sr.lo;
-      if ((om && om[j]) || (sta.bpt && sta_rule_keep(sta, row, j))) keep = true;
+      if ((om && om[j]) || (sta.bpt && sta_rule_near(sta, rc, cc[e]))) keep = true;
       dst[j] = keep ? 1 : 0;
     }
   }
