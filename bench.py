@@ -46,7 +46,7 @@ def _measured_traffic(workload, fp8=False, dense=False):
     return rec["traffic_bytes_per_launch"].get(workload)
 
 
-def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
+def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_step=False):
     import torch
     import block_sparse_attention_mask_amd as bsa
     from synth import make_inputs
@@ -79,11 +79,25 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
                           dtype=torch.uint8, device=dev)
     n_slots = lib.attn_work_order_slots(ctypes.byref(shp))
     work_order = torch.empty(n_slots, dtype=torch.int32, device=dev) if n_slots > 0 else None
+    # short rows: the kv lists (and the work order) come out of the mask build's own
+    # launch, and attention reads them there; no compaction pass over the mask
+    fused = use_nabla and not fp8 and nb <= 256 and not csr_step
+    if fused:
+        kv_len = torch.empty(rows, dtype=torch.int32, device=dev)
+        kv_idx = torch.empty(rows, nb, dtype=torch.int32, device=dev)
+        lists_ws = bsa.nabla_lists_workspace(q, cfg.S_valid)
+        sta_kw = {} if cfg.sta is None else dict(grid=cfg.grid, tile=cfg.sta.tile, window=cfg.sta.window,
+                                                  order=cfg.order, order_tile=cfg.order_tile)
 
     st = {}
 
     def phase_mask():
         m = mask
+        if fused:
+            bsa.nabla_build_mask_lists(q, k, thr, s_valid=cfg.S_valid, out=(mask, kv_len, kv_idx, work_order),
+                                       ws=lists_ws, **sta_kw)
+            st["m"], st["wo"] = m, work_order
+            return
         if use_nabla and not fp8 and cfg.sta is not None:
             # NABLA OR sliding tiles in one call (the rule inside the selection where the
             # layout allows it)
@@ -107,12 +121,18 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
         st["m"] = m
 
     def phase_csr():
+        if fused:
+            return      # built by the mask phase
         # kv lists, and the attention work order where the shape has one (one call)
         st["rp"], st["ci"] = bsa.mask_to_csr(st["m"], B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws,
                                              work_order=work_order)
         st["wo"] = work_order
 
     def phase_attn():
+        if fused:
+            bsa.block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, s_valid=cfg.S_valid, out=out, ws=attn_ws,
+                                            work_order=st["wo"])
+            return
         bsa.block_sparse_attn_fwd_csr(qa, ka, v, st["rp"], st["ci"], s_valid=cfg.S_valid, q_scale=qs, k_scale=ks,
                                       out=out, ws=attn_ws, work_order=st["wo"])
 
@@ -123,7 +143,7 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
             fn()
         if ev is not None:
             ev[3].record()
-        return st["m"], st["rp"]
+        return st["m"], (kv_len if fused else st["rp"])
 
     for _ in range(warmup):
         step()
@@ -187,9 +207,9 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True):
         return p0.elapsed_time(p1) / steps
 
     mask_ms, csr_ms, attn_ms = phase_ms(phase_mask), phase_ms(phase_csr), phase_ms(phase_attn)
-    kept = int(rp[-1].item())
+    kept = int(rp.sum().item()) if fused else int(rp[-1].item())
     return dict(ms_per_step=ms_total / steps, wall_s=wall, mask_ms=mask_ms, csr_ms=csr_ms, attn_ms=attn_ms,
-                eager_phase_ms=eager_ms,
+                eager_phase_ms=eager_ms, kv_lists="from the mask build" if fused else "compaction launch",
                 step_ms_median=per_step[len(per_step) // 2], step_ms_min=per_step[0],
                 kept_tiles=kept, kept_fraction=kept / (cfg.B * cfg.H * nb * nb), mask=m.cpu() if use_nabla else None,
                 q=q, k=k, v=v, qa=qa, ka=ka, qs=qs, ks=ks)
@@ -523,6 +543,8 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
     ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--csr-step", action="store_true",
+                    help="kv lists from a compaction launch over the mask instead of from the mask build")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replaying the step as a HIP graph")
     ap.add_argument("--topk-compare", action="store_true",
@@ -572,7 +594,8 @@ def main():
     from synth import get_config
     cfg = get_config(args.config)
     thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
-    r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=not args.no_graph)
+    r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=not args.no_graph,
+                csr_step=args.csr_step)
     fpt = _flops_per_tile(cfg.D)
     kept_flops = r["kept_tiles"] * fpt
     attn_tflops = kept_flops / (r["attn_ms"] * 1e-3) / 1e12
@@ -596,6 +619,7 @@ def main():
                    "dense": args.dense, "fp8_qk": args.fp8,
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
+        "kv_lists": r["kv_lists"],
         # per-step spread and phase times from the eager pass with events between the phases
         "step_ms_median_eager": round(r["step_ms_median"], 4), "step_ms_min_eager": round(r["step_ms_min"], 4),
         "eager_phase_ms": {k: round(x, 4) for k, x in r["eager_phase_ms"].items()},

@@ -23,10 +23,12 @@ _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPA
 # every function the C header declares, in declaration order
 EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_topk", "quantize_fp8_blocks",
            "nabla_build_mask_fp8",
-           "sta_workspace_size", "sta_build_mask", "nabla_sta_workspace_size", "nabla_build_mask_sta", "mask_or",
+           "sta_workspace_size", "sta_build_mask", "nabla_sta_workspace_size", "nabla_build_mask_sta",
+           "nabla_lists_workspace_size", "nabla_build_mask_lists", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "bsa_mask_to_csr_ordered", "attn_workspace_size",
            "block_sparse_attn_fwd",
-           "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "attn_work_order_slots", "attn_work_order",
+           "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "block_sparse_attn_fwd_lists",
+           "attn_work_order_slots", "attn_work_order",
            "attn_bwd_workspace_size", "block_sparse_attn_bwd", "token_reorder", "bsa_last_error",
            "bsa_abi_version"]
 
@@ -73,6 +75,8 @@ def load(path: Optional[str] = None):
         "sta_build_mask": (i32, [PS, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
         "nabla_sta_workspace_size": (sz, [PS]),
         "nabla_build_mask_sta": (i32, [PT, PT, PS, dbl, dbl, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
+        "nabla_lists_workspace_size": (sz, [PS]),
+        "nabla_build_mask_lists": (i32, [PT, PT, PS, dbl, dbl, i3, i3, i3, i32, i3, vp, vp, vp, vp, vp, sz, vp]),
         "mask_or": (i32, [vp, vp, i64, vp, i64, vp]),
         "csr_workspace_size": (sz, [i32, i32, i32]),
         "bsa_mask_to_csr": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
@@ -81,6 +85,7 @@ def load(path: Optional[str] = None):
         "block_sparse_attn_fwd": (i32, [PT, PT, PT, PS, vp, i64, i64, vp, vp, dbl, PT, vp, vp, sz, vp]),
         "attn_csr_workspace_size": (sz, [PS, i32]),
         "block_sparse_attn_fwd_csr": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
+        "block_sparse_attn_fwd_lists": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
         "attn_work_order_slots": (i32, [PS]),
         "attn_work_order": (i32, [PS, vp, vp, vp]),
         "attn_bwd_workspace_size": (sz, [PS]),
@@ -272,6 +277,51 @@ def nabla_build_mask_sta(q: torch.Tensor, k: torch.Tensor, thr: float, grid: Seq
     return out
 
 
+def nabla_lists_workspace(q: torch.Tensor, s_valid: Optional[int] = None) -> torch.Tensor:
+    """A workspace for nabla_build_mask_lists on tensors shaped like q (reusable by calls
+    that do not overlap in time)."""
+    lib = load()
+    shp = _shape(q, s_valid)
+    return _ws(lib.nabla_lists_workspace_size(ctypes.byref(shp)), q.device)
+
+
+def nabla_build_mask_lists(q: torch.Tensor, k: torch.Tensor, thr: float, grid: Optional[Sequence[int]] = None,
+                           tile: Optional[Sequence[int]] = None, window: Optional[Sequence[int]] = None,
+                           order: str = "row", order_tile: Optional[Sequence[int]] = None,
+                           s_valid: Optional[int] = None, scale: Optional[float] = None, work_order: bool = True,
+                           out=None, ws: Optional[torch.Tensor] = None):
+    """The mask of nabla_build_mask_sta (grid None: of nabla_build_mask) with, from the same
+    launch, the kv lists -> (mask uint8 [B,H,nb,nb], kv_len int32 [B*H*nb], kv_idx int32
+    [B*H*nb, nb] (row r's kept blocks, ascending, in kv_idx[r, :kv_len[r]]), work order
+    int32 [slots] or None when the shape runs in the default order). nb <= 256."""
+    lib = load()
+    B, H, S, D = q.shape
+    nb = S // 64
+    shp = _shape(q, s_valid)
+    if out is None:
+        out = (torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device),
+               torch.empty(B * H * nb, dtype=torch.int32, device=q.device),
+               torch.empty(B * H * nb, nb, dtype=torch.int32, device=q.device), None)
+        n = lib.attn_work_order_slots(ctypes.byref(shp))
+        if work_order and n > 0:
+            out = out[:3] + (torch.empty(n, dtype=torch.int32, device=q.device),)
+    mask, kv_len, kv_idx, wo = out
+    if ws is None:
+        ws = nabla_lists_workspace(q, s_valid)
+    arr = ctypes.c_int * 3
+    g3 = arr(*grid) if grid is not None else None
+    t3 = arr(*tile) if tile is not None else None
+    w3 = arr(*window) if window is not None else None
+    ot = arr(*order_tile) if order_tile is not None else None
+    tq, tk = _tensor(q), _tensor(k)
+    _check(lib.nabla_build_mask_lists(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
+                                      float(scale) if scale else 0.0, g3, t3, w3, 0 if order == "row" else 1, ot,
+                                      mask.data_ptr(), kv_len.data_ptr(), kv_idx.data_ptr(),
+                                      wo.data_ptr() if wo is not None else None, ws.data_ptr(), ws.numel(),
+                                      _stream(q.device)))
+    return mask, kv_len, kv_idx, wo
+
+
 def mask_or(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """a | b elementwise; b may be one [nb, nb] plane broadcast over a [B,H,nb,nb] mask."""
     lib = load()
@@ -394,6 +444,30 @@ def block_sparse_attn_fwd_csr(q, k, v, row_ptr, col_idx, scale=None, s_valid=Non
     _check(lib.block_sparse_attn_fwd_csr(
         ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(shp), row_ptr.data_ptr(),
         col_idx.data_ptr(), work_order.data_ptr() if work_order is not None else None,
+        q_scale.data_ptr() if q_scale is not None else None,
+        k_scale.data_ptr() if k_scale is not None else None, float(scale) if scale else 0.0, ctypes.byref(to),
+        lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, scale=None, s_valid=None, q_scale=None, k_scale=None,
+                                return_lse=False, out=None, lse=None, ws=None, work_order=None):
+    """Attention over the fixed-stride kv lists of nabla_build_mask_lists, optionally with
+    its work order (computed internally when None)."""
+    lib = load()
+    shp = _shape(q, s_valid)
+    code = _dtype_code(q)
+    if ws is None:
+        ws = _ws(lib.attn_csr_workspace_size(ctypes.byref(shp), code), q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if q.dtype == torch.float32 else torch.bfloat16,
+                          device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    tq, tk, tv, to = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    _check(lib.block_sparse_attn_fwd_lists(
+        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(shp), kv_len.data_ptr(),
+        kv_idx.data_ptr(), work_order.data_ptr() if work_order is not None else None,
         q_scale.data_ptr() if q_scale is not None else None,
         k_scale.data_ptr() if k_scale is not None else None, float(scale) if scale else 0.0, ctypes.byref(to),
         lse.data_ptr() if return_lse else None, ws.data_ptr(), ws.numel(), _stream(q.device)))

@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 8; }
+int bsa_abi_version(void) { return 9; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -94,7 +94,7 @@ static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const b
                                uint8_t* mask_out, const bsa::Fp8Out* f8, void* ws, size_t ws_bytes,
                                bsa_stream_t stream, int topk = 0, bsa::StaRule sta = {0, 0, 0, 0, 0, 0},
                                const bsa::StaGeom* plane_geom = nullptr, uint8_t* plane = nullptr,
-                               void* sta_ws = nullptr) {
+                               void* sta_ws = nullptr, const bsa::SelLists* lists = nullptr) {
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
   if ((st = check_tensor("q", q, shape)) != BSA_OK) return st;
@@ -123,12 +123,13 @@ static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const b
     or_mask = plane;
     or_sb = or_sh = 0;
   }
+  const bsa::SelLists sl = lists ? *lists : bsa::SelLists{};
   hipError_t e = bsa::launch_pool(q->dtype == BSA_F32, shape->D, q->ptr, qs, k->ptr, ks, shape->B, shape->H, nb,
                                   qbar, kbarT, f8, hs);
   if (e != hipSuccess) return hip_status(e, "pool launch");
   const uint64_t T_fixed = (uint64_t)std::ldexp(1.0 - thr, 60);
   e = bsa::launch_select(qbar, kbarT, shape->B, shape->H, nb, shape->D, scale, T_fixed, topk, or_mask, or_sb,
-                         or_sh, sta, mask_out, hs);
+                         or_sh, sta, mask_out, hs, sl);
   return hip_status(e, "select launch");
 }
 
@@ -273,6 +274,51 @@ bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const 
                       (uint8_t*)ws + nws, (char*)ws + nws + align256(nb * nb));
 }
 
+static int work_order_slots(const bsa_shape* s);
+
+size_t nabla_lists_workspace_size(const bsa_shape* s) { return nabla_sta_workspace_size(s); }
+
+bsa_status nabla_build_mask_lists(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                                  double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
+                                  int token_order, const int order_tile_thw[3], uint8_t* mask_out, int32_t* kv_len,
+                                  int32_t* kv_idx, int32_t* work_order, void* ws, size_t ws_bytes,
+                                  bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  const int nb = shape->S / 64;
+  if (nb > bsa::SELR_MAX_NB)
+    return fail(BSA_EUNSUPPORTED, "nb=%d: kv lists from the mask build need nb <= %d (use bsa_mask_to_csr)", nb,
+                bsa::SELR_MAX_NB);
+  if (!kv_len || !kv_idx) return fail(BSA_EINVAL, "kv_len / kv_idx is NULL");
+  if ((int64_t)shape->B * shape->H * nb * nb >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "too many list entries");
+  if (work_order && !work_order_slots(shape))
+    return fail(BSA_EUNSUPPORTED, "this shape runs in the default order (attn_work_order_slots is 0)");
+  const size_t need = nabla_lists_workspace_size(shape);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+  const size_t nws = nabla_workspace_size(shape);
+  const bsa::SelLists lists = {kv_len, kv_idx};
+  if (!grid_thw) {
+    st = nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0,
+                      bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr, nullptr, &lists);
+  } else {
+    bsa::StaGeom g;
+    if ((st = sta_geom_from(shape, grid_thw, tile_thw, win_thw, token_order, order_tile_thw, &g)) != BSA_OK) return st;
+    const bsa::StaRule rule = bsa::sta_rule_of(g);
+    if (rule.bpt)   // aligned layout: the rule inside the selection
+      st = nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule, nullptr,
+                        nullptr, nullptr, &lists);
+    else            // the sliding-tile plane built in the workspace first
+      st = nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule, &g,
+                        (uint8_t*)ws + nws, (char*)ws + nws + align256((size_t)nb * nb), &lists);
+  }
+  if (st != BSA_OK || !work_order) return st;
+  // the work order from the list lengths: one small launch (a single workgroup)
+  return hip_status(bsa::launch_pair_schedule_len(kv_len, shape->B * shape->H, nb, work_order, (hipStream_t)stream),
+                    "work order launch");
+}
+
 // ---------------------------------------------------------------------------
 bsa_status token_reorder(const bsa_tensor* x, const bsa_shape* shape, const int grid_thw[3], int order,
                          const int tile_thw[3], int inverse, const bsa_tensor* out, bsa_stream_t stream) {
@@ -350,7 +396,6 @@ bsa_status bsa_mask_to_csr(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh
   return hip_status(bsa::launch_lpt_rows(row_ptr, rows, nb, sort_ws, order, (hipStream_t)stream), "order launch");
 }
 
-static int work_order_slots(const bsa_shape* s);
 
 bsa_status bsa_mask_to_csr_ordered(const uint8_t* mask, int64_t mask_sb, int64_t mask_sh, int B, int H, int nb,
                                    int32_t* row_ptr, int32_t* col_idx, int32_t* work_order, void* ws,
@@ -401,7 +446,7 @@ size_t attn_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
 static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v, const bsa_shape* shape,
                               const int32_t* row_ptr, const int32_t* col_idx, const int32_t* work_order,
                               const float* q_scale, const float* k_scale, double scale, const bsa_tensor* o,
-                              float* lse, void* ws, hipStream_t hs) {
+                              float* lse, void* ws, hipStream_t hs, const int32_t* row_len = nullptr) {
   bsa::AttnArgs a = {};
   bsa::AttnMode mode;
   if (q->dtype == BSA_BF16) mode = bsa::ATTN_BF16;
@@ -414,6 +459,7 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   a.o = (void*)o->ptr; a.o_sb = o->sb; a.o_sh = o->sh; a.o_ss = o->ss;
   a.lse = lse;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.row_len = row_len; a.row_stride = shape->S / 64;
   a.q_scale = q_scale; a.k_scale = k_scale;
   a.B = shape->B; a.H = shape->H; a.nb = shape->S / 64; a.S = shape->S; a.S_valid = shape->S_valid; a.D = shape->D;
   a.scale_log2 = (float)(scale * 1.4426950408889634);
@@ -421,7 +467,9 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   const int slots = work_order_slots(shape);
   if (slots) {
     if (!work_order) {
-      hipError_t e = bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, (int32_t*)ws, hs);
+      hipError_t e = row_len ? bsa::launch_pair_schedule_len(row_len, shape->B * shape->H, shape->S / 64,
+                                                             (int32_t*)ws, hs)
+                             : bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, (int32_t*)ws, hs);
       if (e != hipSuccess) return hip_status(e, "schedule launch");
       work_order = (const int32_t*)ws;
     }
@@ -524,6 +572,25 @@ bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, c
   if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
   return attn_common(q, k, v, shape, row_ptr, col_idx, work_order, q_scale, k_scale, scale, o, lse, ws,
                      (hipStream_t)stream);
+}
+
+bsa_status block_sparse_attn_fwd_lists(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                       const bsa_shape* shape, const int32_t* kv_len, const int32_t* kv_idx,
+                                       const int32_t* work_order, const float* q_scale, const float* k_scale,
+                                       double scale, const bsa_tensor* o, float* lse, void* ws, size_t ws_bytes,
+                                       bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_attn(q, k, v, shape, q_scale, k_scale, o)) != BSA_OK) return st;
+  if (!std::isfinite(scale)) return fail(BSA_EINVAL, "scale is not finite");
+  if (!kv_len || !kv_idx) return fail(BSA_EINVAL, "kv_len / kv_idx is NULL");
+  const int64_t nb = shape->S / 64;
+  if ((int64_t)shape->B * shape->H * nb * nb >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "too many list entries");
+  const size_t need = attn_csr_workspace_size(shape, q->dtype);
+  if (need && (!ws || ws_bytes < need)) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+  return attn_common(q, k, v, shape, nullptr, kv_idx, work_order, q_scale, k_scale, scale, o, lse, ws,
+                     (hipStream_t)stream, kv_len);
 }
 
 // ---------------------------------------------------------------------------

@@ -99,8 +99,16 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   const int iA = 2 * pidx, iB = 2 * pidx + 1;
   const bool hasB = iB < a.nb;
   const int rowA = bh * a.nb + iA;
-  const int sA = row_ptr[rowA], eA = row_ptr[rowA + 1];
-  const int sB = hasB ? row_ptr[rowA + 1] : 0, eB = hasB ? row_ptr[rowA + 2] : 0;
+  int sA, eA, sB = 0, eB = 0;
+  if (a.row_len) {   // fixed-stride lists
+    sA = rowA * a.row_stride;
+    eA = sA + a.row_len[rowA];
+    if (hasB) { sB = sA + a.row_stride; eB = sB + a.row_len[rowA + 1]; }
+  } else {
+    sA = row_ptr[rowA];
+    eA = row_ptr[rowA + 1];
+    if (hasB) { sB = eA; eB = row_ptr[rowA + 2]; }
+  }
   const int i = pr ? iB : iA;                      // this wave's query block
   const bool mine_valid = pr == 0 || hasB;
   const int row = bh * a.nb + i;

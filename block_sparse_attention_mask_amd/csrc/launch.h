@@ -40,12 +40,19 @@ __device__ __forceinline__ bool sta_rule_near(const StaRule& s, StaCoord a, StaC
 __device__ __forceinline__ bool sta_rule_keep(const StaRule& s, int i, int j) {
   return sta_rule_near(s, sta_rule_coord(s, i), sta_rule_coord(s, j));
 }
+// kv lists written beside the mask rows (short rows, nb <= SELR_MAX_NB, only): row r's
+// kept blocks, ascending, at kv_idx[r * nb ..], their number at kv_len[r].
+struct SelLists {
+  int32_t* kv_len;
+  int32_t* kv_idx;
+};
+constexpr int SELR_MAX_NB = 256;
 // T_fixed = floor((1 - thr) 2^60) for the cumulative-mass rule; topk > 0 keeps the
 // topk largest entries of each row instead (T_fixed unused). The result is OR'd with
 // or_mask (if any) and with the sliding-tile rule sta (if sta.bpt > 0).
 hipError_t launch_select(const double* qbar, const double* kbarT, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                         StaRule sta, uint8_t* mask_out, hipStream_t st);
+                         StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists = SelLists{});
 
 // sta.hip
 struct StaGeom {
@@ -81,6 +88,8 @@ constexpr int PAIR_SCHED_MAX_ITEMS = 8192;
 bool pair_schedule_fits(int BH, int nb);
 int pair_schedule_slots(int BH, int nb);   // entries of the order = workgroups to launch
 hipError_t launch_pair_schedule(const int32_t* row_ptr, int BH, int nb, int32_t* order, hipStream_t st);
+// the same order for fixed-stride lists, from their lengths kv_len [BH * nb]
+hipError_t launch_pair_schedule_len(const int32_t* kv_len, int BH, int nb, int32_t* order, hipStream_t st);
 
 // reorder.hip
 constexpr int ORDER_ROW = 0, ORDER_TILE = 1, ORDER_SPATIAL = 2;
@@ -104,6 +113,9 @@ struct AttnArgs {
   void* o; int64_t o_sb, o_sh, o_ss;
   float* lse;
   const int32_t* row_ptr; const int32_t* col_idx;
+  // fixed-stride lists instead (row_len != NULL): row r's list is
+  // col_idx[r * row_stride .. r * row_stride + row_len[r]); row_ptr unused
+  const int32_t* row_len; int row_stride;
   const int32_t* pair_order;   // work order of the (head, query-block pair) items, or NULL;
   int n_slots;                 // its length (entries -1: no item)
   const float* q_scale; const float* k_scale;

@@ -5,6 +5,7 @@
 // of the CalibAtt page: the attention kernel visits only the listed blocks.
 #include "common.h"
 #include "launch.h"
+#include "work_order.h"
 
 namespace bsa {
 
@@ -120,9 +121,6 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(const uint8_t* __restrict
 // thread, 1024 threads; the mask is small, so the repeated reads stay in L2), stages its own rows
 // in shared memory, counts them with wave ballots, scans the counts, and writes
 // row_ptr and the ascending kept indices.
-constexpr int SCHED_RANGES = 8;   // XCD ranges of the attention work order (below)
-template <typename Cost>
-__device__ __forceinline__ void pair_schedule_block(Cost cost, int BH, int nb, int32_t* __restrict__ order, int* sm);
 
 constexpr int CSR_SMALL_ROWS = 4096;
 constexpr int CSR_SMALL_NB = 512;
@@ -177,7 +175,7 @@ __global__ __launch_bounds__(1024) void csr_small_kernel(const uint8_t* __restri
     __syncthreads();
     extern __shared__ int sched_sm[];
     const int npair = (nb + 1) / 2;
-    pair_schedule_block(
+    pair_schedule_block<1024>(
         [&](int it) {
           const int rA = (it / npair) * nb + 2 * (it % npair);
           return max(cnt[rA], 2 * (it % npair) + 1 < nb ? cnt[rA + 1] : 0);
@@ -398,76 +396,11 @@ hipError_t launch_lpt_rows(const int32_t* row_ptr, int rows, int nb, int32_t* ws
   return hipGetLastError();
 }
 
-// Work order of the attention kernel, whose work item is a pair of adjacent query
-// blocks (2p, 2p+1) walking the union of their kv lists. The items are cut into 8
-// contiguous ranges, one per XCD (workgroups are dealt to the XCDs round-robin, so
-// workgroup x runs on XCD x % 8): neighbouring query blocks keep sharing one L2. Inside
-// a range the items go longest first, by max(|list 2p|, |list 2p+1|); equal keys in
-// arbitrary order (the output does not depend on the order). Slot x of the order holds
-// the item of position x / 8 in range x % 8, or -1.
-// One workgroup of 1024 threads does it all in shared memory: per-range key
-// histograms, a descending scan per range, and a scatter with shared-memory atomics.
-template <typename Cost>
-__device__ __forceinline__ void pair_schedule_block(Cost cost, int BH, int nb, int32_t* __restrict__ order, int* sm) {
-  const int nk = nb + 1, npair = (nb + 1) / 2, items = BH * npair;
-  const int maxg = (items + SCHED_RANGES - 1) / SCHED_RANGES;
-  int* hist = sm;                                    // [ranges][nk]
-  int* cur = sm + SCHED_RANGES * nk;                 // [ranges][nk]: descending starts, then cursors
-  __shared__ int part[SCHED_RANGES][2];
-  __shared__ int gsize[SCHED_RANGES];
-  const int t = threadIdx.x;
-  for (int x = t; x < 2 * SCHED_RANGES * nk; x += 1024) sm[x] = 0;
-  __syncthreads();
-  constexpr int PER = PAIR_SCHED_MAX_ITEMS / 1024;
-  int key[PER], grp[PER];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int it = t + r * 1024;
-    key[r] = -1;
-    if (it < items) {
-      key[r] = cost(it);
-      grp[r] = (int)(((int64_t)it * SCHED_RANGES) / items);
-      atomicAdd(&hist[grp[r] * nk + key[r]], 1);
-    }
-  }
-  __syncthreads();
-  // descending exclusive scan of each range's histogram: 128 threads per range, each
-  // summing a chunk of keys (largest keys first), then a scan of the 128 chunk sums
-  {
-    const int g = t >> 7, c = t & 127;
-    const int per = (nk + 127) / 128;
-    const int k1 = nk - 1 - c * per;                 // chunk: k1, k1-1, ..., k1-per+1
-    int sum = 0;
-    for (int e = 0; e < per; ++e)
-      if (k1 - e >= 0) sum += hist[g * nk + k1 - e];
-    // exclusive scan of the 128 chunk sums of the range: two waves, then the first
-    // wave's total added to the second
-    const int incl = wave_incl_scan_i32(sum);
-    if ((c & 63) == 63) part[g][c >> 6] = incl;
-    __syncthreads();
-    int run = incl - sum + (c >= 64 ? part[g][0] : 0);
-    if (c == 127) gsize[g] = run + sum;
-    for (int e = 0; e < per; ++e)
-      if (k1 - e >= 0) { cur[g * nk + k1 - e] = run; run += hist[g * nk + k1 - e]; }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    if (key[r] >= 0) {
-      const int pos = atomicAdd(&cur[grp[r] * nk + key[r]], 1);
-      order[pos * SCHED_RANGES + grp[r]] = t + r * 1024;
-    }
-  }
-  // slots past the end of a range
-  for (int x = t; x < maxg * SCHED_RANGES; x += 1024)
-    if (x / SCHED_RANGES >= gsize[x % SCHED_RANGES]) order[x] = -1;
-}
-
 __global__ __launch_bounds__(1024) void pair_schedule_kernel(const int32_t* __restrict__ row_ptr, int BH, int nb,
                                                              int32_t* __restrict__ order) {
   extern __shared__ int sm[];
   const int npair = (nb + 1) / 2;
-  pair_schedule_block(
+  pair_schedule_block<1024>(
       [&](int it) {
         const int bh = it / npair, i = 2 * (it % npair);
         const int rA = bh * nb + i;
@@ -485,6 +418,24 @@ bool pair_schedule_fits(int BH, int nb) {
 int pair_schedule_slots(int BH, int nb) {
   const int items = BH * ((nb + 1) / 2);
   return ((items + SCHED_RANGES - 1) / SCHED_RANGES) * SCHED_RANGES;
+}
+
+__global__ __launch_bounds__(1024) void pair_schedule_len_kernel(const int32_t* __restrict__ kv_len, int BH, int nb,
+                                                                 int32_t* __restrict__ order) {
+  extern __shared__ int sm[];
+  const int npair = (nb + 1) / 2;
+  pair_schedule_block<1024>(
+      [&](int it) {
+        const int p = it % npair, rA = (it / npair) * nb + 2 * p;
+        return max(kv_len[rA], 2 * p + 1 < nb ? kv_len[rA + 1] : 0);
+      },
+      BH, nb, order, sm);
+}
+
+hipError_t launch_pair_schedule_len(const int32_t* kv_len, int BH, int nb, int32_t* order, hipStream_t st) {
+  hipLaunchKernelGGL(pair_schedule_len_kernel, dim3(1), dim3(1024), 2 * SCHED_RANGES * (nb + 1) * 4, st, kv_len, BH,
+                     nb, order);
+  return hipGetLastError();
 }
 
 hipError_t launch_pair_schedule(const int32_t* row_ptr, int BH, int nb, int32_t* order, hipStream_t st) {

@@ -522,8 +522,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
 // wave's histogram lives in its own part of shared memory; the shared-memory
 // operations of one wave are processed in program order, so a clear, the atomic
 // updates and the reads that follow need no wait between them.
+// Optionally the kept blocks of each row also go to a fixed-stride kv list (the
+// compaction the attention kernel consumes, without a pass of its own over the mask).
 // ----------------------------------------------------------------------------
-constexpr int SELR_MAX_NB = 256;
 
 // value of x in lane L (L wave-uniform)
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int L) {
@@ -532,13 +533,18 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int L) {
   return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
+// Each 16-row strip of the map is formed by SELR_SPLIT workgroups (the same small fp64
+// product, recomputed), each taking SEL_ROWS / SELR_SPLIT of its rows: more workgroups
+// and fewer rows one after the other in a wave.
+constexpr int SELR_SPLIT = 2;
 template <int NCT, int KS>   // NCT = column tiles per wave (nb <= 128 NCT)
 __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const double* __restrict__ qmf,
                                                                     const double* __restrict__ kmf, int nb,
                                                                     double scale, uint64_t T_fixed, int topk,
                                                                     const uint8_t* __restrict__ or_mask,
                                                                     int64_t or_sb, int64_t or_sh, StaRule sta,
-                                                                    int H, uint8_t* __restrict__ mask_out) {
+                                                                    int H, uint8_t* __restrict__ mask_out,
+                                                                    SelLists lists) {
   constexpr int E = 2 * NCT;                        // entries per lane per row
   constexpr int NBP = SEL_WAVES * 16 * NCT;         // map row length
   const bool by_count = topk > 0;
@@ -548,7 +554,8 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
   __shared__ uint64_t hmass[SEL_WAVES][256];
   __shared__ uint32_t hcnt[SEL_WAVES][256];
 
-  const int bh = blockIdx.y, rt = blockIdx.x, row0 = rt * SEL_ROWS;
+  // strip rt of 16 rows; part `part` of its rows is this workgroup's
+  const int bh = blockIdx.y, rt = blockIdx.x / SELR_SPLIT, part = blockIdx.x % SELR_SPLIT, row0 = rt * SEL_ROWS;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lc = l & 15;
   const int ntile = (nb + 15) / 16;
 
@@ -567,8 +574,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
   StaCoord cc[E];   // the sliding-tile rule's tile coordinates of this lane's columns
 #pragma unroll
   for (int e = 0; e < E; ++e) cc[e] = sta.bpt ? sta_rule_coord(sta, min(64 * e + l, nb - 1)) : StaCoord{0, 0, 0};
-  for (int rr = 0; rr < SEL_ROWS / SEL_WAVES; ++rr) {
-    const int r = (SEL_ROWS / SEL_WAVES) * w + rr, row = row0 + r;
+  constexpr int RPW = SEL_ROWS / SEL_WAVES / SELR_SPLIT;   // rows per wave
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int r = part * (SEL_ROWS / SELR_SPLIT) + RPW * w + rr, row = row0 + r;
     if (row >= nb) break;                            // wave-uniform
     const StaCoord rc = sta.bpt ? sta_rule_coord(sta, row) : StaCoord{0, 0, 0};
     // ---- softmax of the row in fp64, then the fixed-point mass w = floor(p 2^60) (the key)
@@ -675,10 +683,13 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
       sr = n;
     }
 
-    // ---- write the row (OR'd with the optional mask); tied keys ranked by ascending index
-    uint8_t* dst = mask_out + ((int64_t)bh * nb + row) * nb;
+    // ---- write the row (OR'd with the optional mask); tied keys ranked by ascending
+    // index; with lists, the kept blocks also go to the row's kv list in ascending order
+    const int64_t grow = (int64_t)bh * nb + row;
+    uint8_t* dst = mask_out + grow * nb;
     const uint8_t* om = or_mask ? or_mask + b * or_sb + h * or_sh + (int64_t)row * nb : nullptr;
-    int tie_base = 0;
+    int32_t* lst = lists.kv_idx ? lists.kv_idx + grow * nb : nullptr;
+    int tie_base = 0, nkept = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = 64 * e + l;
@@ -686,14 +697,21 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
       const uint64_t tb = __ballot(tied);
       const int rank = tie_base + __popcll(tb & ((1ull << l) - 1ull));
       tie_base += __popcll(tb);
-      if (!valid[e]) continue;
-      bool keep;
-      if (sr.status == ROW_ALL) keep = true;
-      else if (sr.status == ROW_PIVOT) keep = key[e] >= sr.lo;
-      else keep = tied ? rank < sr.tie_keep : key[e] > sr.lo;
-      if ((om && om[j]) || (sta.bpt && sta_rule_near(sta, rc, cc[e]))) keep = true;
-      dst[j] = keep ? 1 : 0;
+      bool keep = false;
+      if (valid[e]) {
+        if (sr.status == ROW_ALL) keep = true;
+        else if (sr.status == ROW_PIVOT) keep = key[e] >= sr.lo;
+        else keep = tied ? rank < sr.tie_keep : key[e] > sr.lo;
+        if ((om && om[j]) || (sta.bpt && sta_rule_near(sta, rc, cc[e]))) keep = true;
+        dst[j] = keep ? 1 : 0;
+      }
+      if (lst) {
+        const uint64_t kb = __ballot(keep);
+        if (keep) lst[nkept + __popcll(kb & ((1ull << l) - 1ull))] = j;
+        nkept += __popcll(kb);
+      }
     }
+    if (lists.kv_len && l == 0) lists.kv_len[grow] = nkept;
   }
 }
 
@@ -752,28 +770,30 @@ static hipError_t launch_select_c(const double* qmf, const double* kmf, int B, i
 template <int NCT>
 static hipError_t launch_select_rows(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
                                      uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                                     StaRule sta, uint8_t* mask_out, hipStream_t st) {
-  dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS, B * H);
+                                     StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists) {
+  dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS * SELR_SPLIT, B * H);
   if (D == 64)
     hipLaunchKernelGGL((select_rows_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, sta, H, mask_out, lists);
   else
     hipLaunchKernelGGL((select_rows_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
+                       topk, or_mask, or_sb, or_sh, sta, H, mask_out, lists);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                         StaRule sta, uint8_t* mask_out, hipStream_t st) {
+                         StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists) {
   const int ntile = (nb + 15) / 16;
   const int nct = (ntile + SEL_WAVES - 1) / SEL_WAVES;
   if (nb <= SELR_MAX_NB) {
     if (nct == 1)
       return launch_select_rows<1>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out,
-                                   st);
-    return launch_select_rows<2>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st);
+                                   st, lists);
+    return launch_select_rows<2>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st,
+                                 lists);
   }
+  if (lists.kv_idx || lists.kv_len) return hipErrorInvalidValue;   // short rows only
 #define BSA_SEL_CASE(n) \
   case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st);
   switch (nct) {

@@ -181,6 +181,33 @@ bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const 
                                 size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The mask of nabla_build_mask_sta (or of nabla_build_mask with no or_mask, when
+ * grid_thw is NULL) together with its per-query-block kv lists and, optionally, the
+ * attention work order [NABLA: the binary block mask tells the operator which blocks
+ * to compute; CalibAtt skip lists]. The lists come out of the same launch that writes
+ * the mask rows: there is no separate pass over the mask.
+ *   q .. mask_out  as nabla_build_mask_sta; grid_thw NULL: no sliding tiles (tile_thw,
+ *                  win_thw, token_order, order_tile_thw unused)
+ *   kv_len     int32 [B*H*nb]: the number of kept kv blocks of row r = (b*H + h)*nb + i
+ *   kv_idx     int32 [B*H*nb*nb]: row r's kept kv blocks, ascending, at
+ *              kv_idx[r*nb .. r*nb + kv_len[r]); the rest of the row is not written
+ *   work_order optional (NULL = none) int32 [attn_work_order_slots(shape)]: the
+ *              attention work order of these lists, as attn_work_order writes it (one
+ *              more small launch, from kv_len); when attn_work_order_slots(shape) is 0
+ *              a non-NULL work_order is BSA_EUNSUPPORTED
+ *   ws         at least nabla_lists_workspace_size(shape) bytes, 256-byte aligned;
+ *              calls that share a workspace must not overlap in time
+ * nb must be at most 256 (BSA_EUNSUPPORTED otherwise: build the mask, then call
+ * bsa_mask_to_csr), and B*H*nb*nb below 2^31. Errors as nabla_build_mask_sta.
+ * ------------------------------------------------------------------------- */
+size_t nabla_lists_workspace_size(const bsa_shape* shape);
+bsa_status nabla_build_mask_lists(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                                  double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
+                                  int token_order, const int order_tile_thw[3], uint8_t* mask_out, int32_t* kv_len,
+                                  int32_t* kv_idx, int32_t* work_order, void* ws, size_t ws_bytes,
+                                  bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Union of block masks [NABLA: adaptive mask OR sliding-tile mask].
  *   dst[i] = (a[i] | b[i % b_n]) != 0 for 0 <= i < n; b_n divides n (b_n == n is a
  *   plain elementwise OR; b_n == nb*nb broadcasts one plane over every head).
@@ -272,6 +299,18 @@ bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, c
                                      const float* q_scale, const float* k_scale, double scale,
                                      const bsa_tensor* o, float* lse,
                                      void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+/* block_sparse_attn_fwd_lists takes the fixed-stride kv lists of nabla_build_mask_lists
+ * (row r's kv blocks at kv_idx[r*nb .. r*nb + kv_len[r]), ascending, B*H*nb*nb below
+ * 2^31) in place of row_ptr / col_idx; everything else as block_sparse_attn_fwd_csr
+ * (workspace attn_csr_workspace_size; work_order NULL: computed from kv_len). */
+bsa_status block_sparse_attn_fwd_lists(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
+                                       const bsa_shape* shape,
+                                       const int32_t* kv_len, const int32_t* kv_idx,
+                                       const int32_t* work_order,
+                                       const float* q_scale, const float* k_scale, double scale,
+                                       const bsa_tensor* o, float* lse,
+                                       void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 int attn_work_order_slots(const bsa_shape* shape);
 bsa_status attn_work_order(const bsa_shape* shape, const int32_t* row_ptr, int32_t* order,

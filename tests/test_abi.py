@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 8
+    assert lib.bsa_abi_version() == 9
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
@@ -105,6 +105,47 @@ def test_nabla_sta_rejects(lib):
     st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 1.5, 0.0, a3(4, 8, 8), a3(4, 8, 8), a3(3, 3, 3), 0,
            None, 8192, 1 << 16, need, None)
     assert st == 1 and "thr" in lib.bsa_last_error().decode()
+
+
+def test_nabla_lists_rejects(lib):
+    # mask + kv lists in one call: every check before any launch
+    a3 = ctypes.c_int * 3
+    q, k = _t(), _t(4096)
+    f = lib.nabla_build_mask_lists
+
+    def call(shape, kv_len=8192, kv_idx=16384, order=None, ws_bytes=None, thr=0.1, grid=None):
+        need = lib.nabla_lists_workspace_size(ctypes.byref(shape))
+        return f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), thr, 0.0, grid, a3(4, 8, 8) if grid else None,
+                 a3(3, 3, 3) if grid else None, 0, None, 32768, kv_len, kv_idx, order, 1 << 16,
+                 need if ws_bytes is None else ws_bytes, None)
+    small = bsa.Shape(1, 2, 256, 256, 128, 64)
+    assert lib.nabla_lists_workspace_size(ctypes.byref(small)) >= lib.nabla_sta_workspace_size(ctypes.byref(small))
+    assert call(bsa.Shape(1, 1, 64 * 257, 64 * 257, 128, 64)) == 2          # nb > 256
+    assert "nb <= 256" in lib.bsa_last_error().decode()
+    assert call(small, kv_len=None) == 1
+    assert call(small, kv_idx=None) == 1
+    assert call(small, ws_bytes=100) == 3
+    assert call(small, thr=1.0) == 1 and "thr" in lib.bsa_last_error().decode()
+    assert call(small, grid=a3(4, 8, 9)) == 1 and "S_valid" in lib.bsa_last_error().decode()
+    # 64 heads x 128 pairs = 8192 items: more than four rounds, no work order for this shape
+    assert call(bsa.Shape(1, 64, 64 * 256, 64 * 256, 128, 64), order=8192) == 2
+    assert "default order" in lib.bsa_last_error().decode()
+
+
+def test_attention_lists_rejects(lib):
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    q, k, v, o = _t(), _t(), _t(), _t()
+    f = lib.block_sparse_attn_fwd_lists
+    need = lib.attn_csr_workspace_size(ctypes.byref(shape), bsa.BSA_BF16)
+
+    def call(kv_len=8192, kv_idx=16384, ws_bytes=need, vv=v):
+        return f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vv), ctypes.byref(shape), kv_len, kv_idx, None, None,
+                 None, 0.0, ctypes.byref(o), None, 32768, ws_bytes, None)
+    assert call(kv_len=None) == 1
+    assert call(kv_idx=None) == 1
+    assert call(vv=_t(dtype=bsa.BSA_F32)) == 1
+    if need:
+        assert call(ws_bytes=need - 1) == 3
 
 
 def test_mask_or_and_csr_reject(lib):

@@ -400,6 +400,85 @@ def test_csr_with_work_order_one_call(gpu_lib, heads):
     assert torch.equal(out_a, out_b)
 
 
+def _check_order(wo, counts, nb, items):
+    """A work order: every pair once, XCD range x % 8 a contiguous run of pairs by
+    decreasing longer-list length."""
+    o = wo.cpu().numpy()
+    npair = (nb + 1) // 2
+    assert sorted(o[o >= 0].tolist()) == list(range(items))
+    for x in range(8):
+        r = o[x::8]
+        r = r[r >= 0]
+        assert np.all(np.diff(np.sort(r)) == 1)
+        bh, p = r // npair, r % npair
+        cB = np.where(2 * p + 1 < nb, counts[np.minimum(bh * nb + 2 * p + 1, len(counts) - 1)], 0)
+        key = np.maximum(counts[bh * nb + 2 * p], cB)
+        assert np.all(np.diff(key) <= 0)
+
+
+@pytest.mark.parametrize("case", ["cfg2", "cfg2x48", "nb200", "nb200-sta-plane"])
+def test_mask_lists_one_call(gpu_lib, case):
+    """nabla_build_mask_lists: the mask bit for bit as the oracle's (and as
+    nabla_build_mask_sta), each row's kv list = its kept blocks in ascending order, the
+    work order (built by the select's last workgroup) a valid longest-first order, and
+    block_sparse_attn_fwd_lists identical to block_sparse_attn_fwd_csr on the same mask
+    (with that order, and with the order computed from the lengths)."""
+    from dataclasses import replace
+    sta_args = {}
+    if case.startswith("cfg2"):
+        cfg = get_config(2, heads=48 if case == "cfg2x48" else None)
+        thr = 0.1
+        sta_args = dict(grid=cfg.grid, tile=cfg.sta.tile, window=cfg.sta.window, order=cfg.order,
+                        order_tile=cfg.order_tile)
+        plane = _sta_plane(cfg)
+    else:
+        cfg = replace(get_config(3, heads=3), cid=9, name="short-8x40x40", grid=(8, 40, 40))
+        thr = 0.2
+        plane = None
+        if case == "nb200-sta-plane":   # row-major, not aligned with the blocks: the plane path
+            sta_args = dict(grid=cfg.grid, tile=(2, 8, 8), window=(3, 3, 3), order="row")
+            plane = oracle.sta_block_mask(cfg.grid, "row", None, (2, 8, 8), (3, 3, 3), 64, cfg.S)
+    q, k, v = make_inputs(cfg, seed=0, device=DEV)
+    nb, BH = cfg.nb, cfg.B * cfg.H
+    print(f"[lists] {case}: heads {cfg.H} nb {nb} thr {thr} sta {bool(sta_args)}", flush=True)
+    ws = gpu_lib.nabla_lists_workspace(q, cfg.S_valid)
+    mask, kv_len, kv_idx, wo = gpu_lib.nabla_build_mask_lists(q, k, thr, s_valid=cfg.S_valid, ws=ws, **sta_args)
+    torch.cuda.synchronize()
+    keep, E = oracle_masks(q, k, thr, or_plane=plane)
+    bad, near = compare_masks(mask, keep, E, thr)
+    assert bad == 0, (bad, near)
+    if sta_args:
+        ref = gpu_lib.nabla_build_mask_sta(q, k, thr, s_valid=cfg.S_valid, **sta_args)
+    else:
+        ref = gpu_lib.nabla_build_mask(q, k, thr)
+    torch.cuda.synchronize()
+    assert torch.equal(mask, ref)
+    m = mask.reshape(BH * nb, nb).cpu().numpy().astype(bool)
+    counts = m.sum(1)
+    assert np.array_equal(kv_len.cpu().numpy(), counts)
+    idx = kv_idx.cpu().numpy()
+    for r in range(BH * nb):
+        assert np.array_equal(idx[r, :counts[r]], np.flatnonzero(m[r])), r
+    assert wo is not None
+    _check_order(wo, counts, nb, BH * ((nb + 1) // 2))
+    # a second call on the same workspace (the arrival counter starts from zero again)
+    mask2, kv_len2, kv_idx2, wo2 = gpu_lib.nabla_build_mask_lists(q, k, thr, s_valid=cfg.S_valid, ws=ws, **sta_args)
+    torch.cuda.synchronize()
+    assert torch.equal(mask2, mask) and torch.equal(kv_len2, kv_len)
+    _check_order(wo2, counts, nb, BH * ((nb + 1) // 2))
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    out_csr = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=cfg.S_valid)
+    out_a = gpu_lib.block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, s_valid=cfg.S_valid, work_order=wo)
+    out_b = gpu_lib.block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, s_valid=cfg.S_valid)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_csr) and torch.equal(out_b, out_csr)
+    blocks = sample_blocks(keep, 6, seed=3)
+    refo = oracle_attention_blocks(q, k, v, keep, blocks, cfg.S_valid)
+    mx, mean = attention_errors(out_a, refo)
+    print(f"  {len(blocks)} query blocks: max err {mx:.3e}, mean err {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
+
+
 def test_longest_first_order_large(gpu_lib):
     """Several sort blocks and many equal counts (rows of a 40-head, nb=1182 mask with
     counts from a narrow band), and the largest nb the order supports in one head."""
