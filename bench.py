@@ -153,12 +153,13 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
         # one step captured as a HIP graph (the library allocates nothing, never syncs
         # and records no memset), replayed once per timed step: the kernels and their
         # order are the eager step's, without the host's per-launch overhead
-        ref = out.clone()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             step()
         torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        ref = out.clone()            # the eager step's output (also with no warmup steps)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             m_g, rp_g = step()
