@@ -479,6 +479,47 @@ def test_mask_lists_one_call(gpu_lib, case):
     assert mx <= MAX_ERR and mean <= MEAN_ERR
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_mask_lists_ragged(gpu_lib, dtype):
+    """The list path on an awkward shape: B = 2, 3 heads, nb = 37 (odd: the last pair has
+    one block), S_valid = S - 40 with zero padding; bf16 and f32 (hi/lo split) inputs."""
+    from dataclasses import replace
+    cfg = replace(get_config(1), cid=9, name="ragged-37", B=2, H=3, grid=(1, 37, 64))
+    assert cfg.nb == 37
+    q, k, v = make_inputs(cfg, seed=5, device=DEV)
+    sv = cfg.S - 40
+    for t in (q, k, v):
+        t[:, :, sv:] = 0
+    q, k, v = (t.to(dtype) for t in (q, k, v))
+    thr = 0.3
+    mask, kv_len, kv_idx, wo = gpu_lib.nabla_build_mask_lists(q, k, thr, s_valid=sv)
+    ref = gpu_lib.nabla_build_mask(q, k, thr)
+    torch.cuda.synchronize()
+    assert torch.equal(mask, ref)
+    keep, E = oracle_masks(q, k, thr)
+    bad, near = compare_masks(mask, keep, E, thr)
+    assert bad == 0, (bad, near)
+    BH, nb = cfg.B * cfg.H, cfg.nb
+    m = mask.reshape(BH * nb, nb).cpu().numpy().astype(bool)
+    counts = m.sum(1)
+    assert np.array_equal(kv_len.cpu().numpy(), counts)
+    idx = kv_idx.cpu().numpy()
+    for r in range(BH * nb):
+        assert np.array_equal(idx[r, :counts[r]], np.flatnonzero(m[r])), r
+    assert wo is not None
+    _check_order(wo, counts, nb, BH * ((nb + 1) // 2))
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    out_csr = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=sv)
+    out_l = gpu_lib.block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, s_valid=sv, work_order=wo)
+    torch.cuda.synchronize()
+    assert torch.equal(out_l, out_csr)
+    blocks = [(b, h, i) for b in range(cfg.B) for h in range(cfg.H) for i in (0, 17, nb - 1)]
+    refo = oracle_attention_blocks(q, k, v, keep, blocks, sv)
+    mx, mean = attention_errors(out_l, refo)
+    print(f"[lists ragged {dtype}] max err {mx:.3e}, mean err {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
+
+
 def test_longest_first_order_large(gpu_lib):
     """Several sort blocks and many equal counts (rows of a 40-head, nb=1182 mask with
     counts from a narrow band), and the largest nb the order supports in one head."""
