@@ -94,9 +94,10 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
     def phase_mask():
         m = mask
         if fused:
-            bsa.nabla_build_mask_lists(q, k, thr, s_valid=cfg.S_valid, out=(mask, kv_len, kv_idx, work_order),
+            # the attention kernel derives its work order from kv_len itself
+            bsa.nabla_build_mask_lists(q, k, thr, s_valid=cfg.S_valid, out=(mask, kv_len, kv_idx, None),
                                        ws=lists_ws, **sta_kw)
-            st["m"], st["wo"] = m, work_order
+            st["m"], st["wo"] = m, None
             return
         if use_nabla and not fp8 and cfg.sta is not None:
             # NABLA OR sliding tiles in one call (the rule inside the selection where the

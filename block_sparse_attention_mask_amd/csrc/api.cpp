@@ -466,10 +466,10 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   const size_t sb_sched = sched_bytes(shape);
   const int slots = work_order_slots(shape);
   if (slots) {
-    if (!work_order) {
-      hipError_t e = row_len ? bsa::launch_pair_schedule_len(row_len, shape->B * shape->H, shape->S / 64,
-                                                             (int32_t*)ws, hs)
-                             : bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, (int32_t*)ws, hs);
+    if (!work_order && row_len) {
+      a.order_from_len = 1;   // each workgroup derives its item from the lengths
+    } else if (!work_order) {
+      hipError_t e = bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, (int32_t*)ws, hs);
       if (e != hipSuccess) return hip_status(e, "schedule launch");
       work_order = (const int32_t*)ws;
     }

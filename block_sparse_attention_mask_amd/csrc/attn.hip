@@ -35,6 +35,75 @@ namespace bsa {
 // fp32 range, and the rescale of the output accumulators is skipped on most tiles.
 constexpr float RESCALE_TAU = 8.f;
 
+// The work item of workgroup x when the work order is derived from fixed-stride list
+// lengths inside the kernel: position x / 8 of range x % 8 in the longest-first order of
+// pair_schedule_block (the same ranges and cost, max of the pair's two lengths clamped
+// to [0, nb]), with equal costs in ascending item order, so that every workgroup of a
+// range derives the same order by itself. A cost histogram in shared memory, a
+// descending scan of it by one wave (the cost of position x / 8 and the number of items
+// above it), then one wave's ballots over the range find the item. sm: room for
+// nb + 1 + (items + 7) / 8 + 1 ints. Returns -1 when the range has no item there.
+// Every thread of the workgroup calls it.
+__device__ int item_from_lengths(const AttnArgs& a, int* sm) {
+  const int nb = a.nb, npair = (nb + 1) / 2, items = a.B * a.H * npair;
+  const int g = blockIdx.x % BSA_NXCD, k = blockIdx.x / BSA_NXCD;
+  // range g: the items it with floor(it * 8 / items) == g
+  const int lo = (int)(((int64_t)g * items + BSA_NXCD - 1) / BSA_NXCD);
+  const int hi = (int)(((int64_t)(g + 1) * items + BSA_NXCD - 1) / BSA_NXCD);
+  const int R = hi - lo;
+  if (k >= R) return -1;                           // the same for the whole workgroup
+  const int t = threadIdx.x, lane = t & 63, nk = nb + 1;
+  int* hist = sm;
+  int* cost = sm + nk;
+  int* res = cost + R;
+  for (int x = t; x < nk; x += 256) hist[x] = 0;
+  __syncthreads();
+  for (int i = t; i < R; i += 256) {
+    const int it = lo + i, p = it % npair, rA = (it / npair) * nb + 2 * p;
+    int c = a.row_len[rA];
+    if (2 * p + 1 < nb) c = max(c, a.row_len[rA + 1]);
+    c = min(max(c, 0), nb);
+    cost[i] = c;
+    atomicAdd(&hist[c], 1);
+  }
+  __syncthreads();
+  if (t < 64) {
+    // lane chunks of keys in descending order; the chunk holding position k names the
+    // cost K there and the number of items with a larger cost
+    const int per = (nk + 63) / 64, k1 = nk - 1 - lane * per;
+    int sum = 0;
+    for (int e = 0; e < per; ++e)
+      if (k1 - e >= 0) sum += hist[k1 - e];
+    const int incl = wave_incl_scan_i32(sum);
+    int run = incl - sum;
+    if (run <= k && k < incl) {
+      for (int e = 0; e < per; ++e) {
+        const int key = k1 - e;
+        if (key < 0) break;
+        if (k < run + hist[key]) { res[0] = key; res[1] = run; break; }
+        run += hist[key];
+      }
+    }
+  }
+  __syncthreads();
+  const int K = res[0], need = k - res[1];         // the need-th item (ascending) of cost K
+  if (t < 64) {
+    int base = 0;
+    for (int i0 = 0; i0 < R; i0 += 64) {
+      const bool f = i0 + lane < R && cost[i0 + lane] == K;
+      const uint64_t b = __ballot(f);
+      const int n = __popcll(b);
+      if (need < base + n) {
+        if (f && __popcll(b & ((1ull << lane) - 1ull)) == need - base) res[2] = lo + i0 + lane;
+        break;
+      }
+      base += n;
+    }
+  }
+  __syncthreads();
+  return res[2];
+}
+
 // MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
 //
 // One workgroup of four waves per PAIR of adjacent query blocks (2p, 2p+1): waves 0-1
@@ -88,6 +157,10 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   if (a.pair_order) {
     if ((int)blockIdx.x >= a.n_slots) return;
     lin = a.pair_order[blockIdx.x];
+    if (lin < 0) return;
+  } else if (a.order_from_len) {
+    // scratch in the second K slot: its first copy comes after the loop's opening barrier
+    lin = item_from_lengths(a, (int*)(smem + NSPLIT * KT_BYTES));
     if (lin < 0) return;
   } else {
     const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
@@ -413,7 +486,7 @@ hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, 
 template <int MODE, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * ((a.nb + 1) / 2);
-  dim3 grid(a.pair_order ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
+  dim3 grid(a.pair_order || a.order_from_len ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
   hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
                      a.k_scale);
   return hipGetLastError();

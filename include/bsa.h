@@ -303,7 +303,8 @@ bsa_status block_sparse_attn_fwd_csr(const bsa_tensor* q, const bsa_tensor* k, c
 /* block_sparse_attn_fwd_lists takes the fixed-stride kv lists of nabla_build_mask_lists
  * (row r's kv blocks at kv_idx[r*nb .. r*nb + kv_len[r]), ascending, B*H*nb*nb below
  * 2^31) in place of row_ptr / col_idx; everything else as block_sparse_attn_fwd_csr
- * (workspace attn_csr_workspace_size; work_order NULL: computed from kv_len). */
+ * (workspace attn_csr_workspace_size; work_order NULL: each attention workgroup derives
+ * its item of that order from kv_len, with no extra launch). */
 bsa_status block_sparse_attn_fwd_lists(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
                                        const bsa_shape* shape,
                                        const int32_t* kv_len, const int32_t* kv_idx,

@@ -422,7 +422,8 @@ def test_mask_lists_one_call(gpu_lib, case):
     nabla_build_mask_sta), each row's kv list = its kept blocks in ascending order, the
     work order (built by the select's last workgroup) a valid longest-first order, and
     block_sparse_attn_fwd_lists identical to block_sparse_attn_fwd_csr on the same mask
-    (with that order, and with the order computed from the lengths)."""
+    (with that order, and with the order each attention workgroup derives from the
+    lengths)."""
     from dataclasses import replace
     sta_args = {}
     if case.startswith("cfg2"):
@@ -511,8 +512,9 @@ def test_mask_lists_ragged(gpu_lib, dtype):
     rp, ci = gpu_lib.mask_to_csr(mask)
     out_csr = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=sv)
     out_l = gpu_lib.block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, s_valid=sv, work_order=wo)
+    out_k = gpu_lib.block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, s_valid=sv)   # order derived in-kernel
     torch.cuda.synchronize()
-    assert torch.equal(out_l, out_csr)
+    assert torch.equal(out_l, out_csr) and torch.equal(out_k, out_csr)
     blocks = [(b, h, i) for b in range(cfg.B) for h in range(cfg.H) for i in (0, 17, nb - 1)]
     refo = oracle_attention_blocks(q, k, v, keep, blocks, sv)
     mx, mean = attention_errors(out_l, refo)
