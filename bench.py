@@ -538,8 +538,8 @@ def run_sweep(cfg_id, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2, the 2B-DiT shape)")
     ap.add_argument("--thr", type=float, default=None, help="NABLA threshold (default: the config's first)")
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
@@ -547,8 +547,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--csr-step", action="store_true",
                     help="kv lists from a compaction launch over the mask instead of from the mask build")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time eager launches instead of replaying the step as a HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as a HIP graph (checked against the eager step) instead of eager launches")
     ap.add_argument("--topk-compare", action="store_true",
                     help="CDF vs Top-k masks at equal average kept blocks (default config 3)")
     ap.add_argument("--reorder", action="store_true",
@@ -596,7 +596,7 @@ def main():
     from synth import get_config
     cfg = get_config(args.config)
     thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
-    r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=not args.no_graph,
+    r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=args.graph,
                 csr_step=args.csr_step)
     fpt = _flops_per_tile(cfg.D)
     kept_flops = r["kept_tiles"] * fpt
@@ -619,7 +619,7 @@ def main():
                    "grid": list(cfg.grid), "token_order": cfg.order, "thr": thr,
                    "sta": None if cfg.sta is None else {"tile": list(cfg.sta.tile), "window": list(cfg.sta.window)},
                    "dense": args.dense, "fp8_qk": args.fp8,
-                   "launch": "eager" if args.no_graph else "hip_graph"},
+                   "launch": "hip_graph" if args.graph else "eager"},
         "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
         "kv_lists": r["kv_lists"],
         # per-step spread and phase times from the eager pass with events between the phases
