@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _make_step(bsa, cfg, q, k, v, fp8):
+def _make_step(bsa, cfg, q, k, v, fp8, lists=False):
     nb, B, H = cfg.nb, cfg.B, cfg.H
     plane = torch.empty(nb, nb, dtype=torch.uint8, device=DEV)
     mask = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=DEV)
@@ -31,6 +31,16 @@ def _make_step(bsa, cfg, q, k, v, fp8):
     q8, k8 = torch.empty(q.shape, dtype=torch.uint8, device=DEV), torch.empty(k.shape, dtype=torch.uint8, device=DEV)
     qs = torch.empty(B, H, nb, dtype=torch.float32, device=DEV)
     ks = torch.empty(B, H, nb, dtype=torch.float32, device=DEV)
+    kv_len = torch.empty(rows, dtype=torch.int32, device=DEV)
+    kv_idx = torch.empty(rows, nb, dtype=torch.int32, device=DEV)
+    lists_ws = bsa.nabla_lists_workspace(q, cfg.S_valid)
+
+    def step_lists():
+        # mask, kv lists from the mask build; attention derives its work order from kv_len
+        bsa.nabla_build_mask_lists(q, k, cfg.thrs[0], cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                                   order_tile=cfg.order_tile, s_valid=cfg.S_valid,
+                                   out=(mask, kv_len, kv_idx, None), ws=lists_ws)
+        bsa.block_sparse_attn_fwd_lists(q, k, v, kv_len, kv_idx, s_valid=cfg.S_valid, out=out, ws=attn_ws)
 
     def step():
         bsa.sta_build_mask(cfg.S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
@@ -44,14 +54,15 @@ def _make_step(bsa, cfg, q, k, v, fp8):
         bsa.block_sparse_attn_fwd_csr(q8 if fp8 else q, k8 if fp8 else k, v, rp, ci, s_valid=cfg.S_valid,
                                       q_scale=qs if fp8 else None, k_scale=ks if fp8 else None, out=out,
                                       ws=attn_ws, work_order=w)
-    return step, out, mask
+    return (step_lists if lists else step), out, mask
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_step_graph_replays_match_eager(gpu_lib, fp8):
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "lists"])
+def test_step_graph_replays_match_eager(gpu_lib, mode):
+    fp8 = mode == "fp8"
     cfg = get_config(2, heads=4)
     q, k, v = make_inputs(cfg, seed=0, device=DEV)
-    step, out, mask = _make_step(gpu_lib, cfg, q, k, v, fp8)
+    step, out, mask = _make_step(gpu_lib, cfg, q, k, v, fp8, lists=mode == "lists")
     step()
     torch.cuda.synchronize()
     ref, ref_mask = out.clone(), mask.clone()
@@ -70,7 +81,7 @@ def test_step_graph_replays_match_eager(gpu_lib, fp8):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        print(f"[graph] fp8={fp8} replay {r}", flush=True)
+        print(f"[graph] {mode} replay {r}", flush=True)
         assert torch.equal(mask, ref_mask)
         assert torch.equal(out, ref)
         del eager
