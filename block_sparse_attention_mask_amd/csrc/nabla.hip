@@ -516,7 +516,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
 // ----------------------------------------------------------------------------
 // Row selection for short rows (nb <= 256). The same reduced map, fixed-point keys,
 // radix digits and tie rule as select_kernel; once the map is formed it is written to
-// shared memory, and each wave then owns two whole rows: softmax, radix select, tie
+// shared memory, and each wave then owns whole rows: softmax, radix select, tie
 // ranking and the row's write use wave reductions, ballots and wave-uniform state only,
 // with no workgroup barrier. Column j of a row is entry e = j / 64 of lane j % 64. A
 // wave's histogram lives in its own part of shared memory; the shared-memory
