@@ -429,6 +429,11 @@ static int work_order_slots(const bsa_shape* s) {
   if (items > 4 * 3 * (int64_t)device_cus()) return 0;
   return bsa::pair_schedule_slots(BH, nb);
 }
+// Shapes with more work items than the work order takes run in per-XCD ranges of the
+// natural item order; from this many key blocks on, the attention kernel orders each
+// head's items longest first (at the 14B shape 46.5 ms against 49.7 ms per launch; the
+// order costs each workgroup a few microseconds, noise against items of ~2 ms).
+constexpr int HEAD_ORDER_MIN_NB = 512;
 static size_t sched_bytes(const bsa_shape* s) { return align256((size_t)work_order_slots(s) * 4); }
 
 size_t attn_csr_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
@@ -467,7 +472,7 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   const int slots = work_order_slots(shape);
   if (slots) {
     if (!work_order && row_len) {
-      a.order_from_len = 1;   // each workgroup derives its item from the lengths
+      a.derive_order = 1;     // each workgroup derives its item from the lengths
     } else if (!work_order) {
       hipError_t e = bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, (int32_t*)ws, hs);
       if (e != hipSuccess) return hip_status(e, "schedule launch");
@@ -475,6 +480,8 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
     }
     a.pair_order = work_order;
     a.n_slots = slots;
+  } else if (shape->S / 64 >= HEAD_ORDER_MIN_NB) {
+    a.derive_order = 2;       // many rounds of long rows: longest first inside each head
   }
   void* split_ws = (char*)ws + sb_sched;
   if (mode == bsa::ATTN_SPLIT_F32) {

@@ -35,33 +35,28 @@ namespace bsa {
 // fp32 range, and the rescale of the output accumulators is skipped on most tiles.
 constexpr float RESCALE_TAU = 8.f;
 
-// The work item of workgroup x when the work order is derived from fixed-stride list
-// lengths inside the kernel: position x / 8 of range x % 8 in the longest-first order of
-// pair_schedule_block (the same ranges and cost, max of the pair's two lengths clamped
-// to [0, nb]), with equal costs in ascending item order, so that every workgroup of a
-// range derives the same order by itself. A cost histogram in shared memory, a
-// descending scan of it by one wave (the cost of position x / 8 and the number of items
-// above it), then one wave's ballots over the range find the item. sm: room for
-// nb + 1 + (items + 7) / 8 + 1 ints. Returns -1 when the range has no item there.
+// Work orders derived inside the kernel. Item it = (head, pair p) costs the longer of
+// its two kv lists (clamped to [0, nb]); kth_longest_item returns the item at position k
+// of the items [lo, lo + R) ordered by decreasing cost, equal costs in ascending item
+// order, so that every workgroup derives the same order by itself: a cost histogram in
+// shared memory, a descending scan of it by one wave (the cost at position k and the
+// number of items above it), then one wave's ballots over the range find the item.
+// sm: nb + 1 + R + 3 ints; the trailing barrier lets the caller reuse them at once.
 // Every thread of the workgroup calls it.
-__device__ int item_from_lengths(const AttnArgs& a, int* sm) {
-  const int nb = a.nb, npair = (nb + 1) / 2, items = a.B * a.H * npair;
-  const int g = blockIdx.x % BSA_NXCD, k = blockIdx.x / BSA_NXCD;
-  // range g: the items it with floor(it * 8 / items) == g
-  const int lo = (int)(((int64_t)g * items + BSA_NXCD - 1) / BSA_NXCD);
-  const int hi = (int)(((int64_t)(g + 1) * items + BSA_NXCD - 1) / BSA_NXCD);
-  const int R = hi - lo;
-  if (k >= R) return -1;                           // the same for the whole workgroup
+__device__ int kth_longest_item(const AttnArgs& a, const int32_t* __restrict__ row_ptr, int* sm, int lo, int R,
+                                int k) {
+  const int nb = a.nb, npair = (nb + 1) / 2;
   const int t = threadIdx.x, lane = t & 63, nk = nb + 1;
   int* hist = sm;
   int* cost = sm + nk;
   int* res = cost + R;
+  auto len = [&](int r) { return a.row_len ? a.row_len[r] : row_ptr[r + 1] - row_ptr[r]; };
   for (int x = t; x < nk; x += 256) hist[x] = 0;
   __syncthreads();
   for (int i = t; i < R; i += 256) {
     const int it = lo + i, p = it % npair, rA = (it / npair) * nb + 2 * p;
-    int c = a.row_len[rA];
-    if (2 * p + 1 < nb) c = max(c, a.row_len[rA + 1]);
+    int c = len(rA);
+    if (2 * p + 1 < nb) c = max(c, len(rA + 1));
     c = min(max(c, 0), nb);
     cost[i] = c;
     atomicAdd(&hist[c], 1);
@@ -101,7 +96,9 @@ __device__ int item_from_lengths(const AttnArgs& a, int* sm) {
     }
   }
   __syncthreads();
-  return res[2];
+  const int item = res[2];
+  __syncthreads();
+  return item;
 }
 
 // MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
@@ -150,7 +147,11 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   // share most kv tiles, and then share one L2. With a work order, workgroup x takes
   // item order[x] (or none, -1): the order puts each range longest first, and
   // workgroups start in index order as slots free up, so short items fill the tail.
-  // Without one: the range of XCD x is [x*chunk, (x+1)*chunk) in natural order.
+  // Without one: the range of XCD x is [x*chunk, (x+1)*chunk) in natural order, or
+  // derived in the kernel from the list lengths: longest first in each range (few
+  // rounds), or longest first inside each head (many rounds of long rows: workgroups that
+  // run together have lists of similar length, start together and move through the kv
+  // blocks at the same pace, so they keep sharing tiles in L2).
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
   int lin;
@@ -158,14 +159,21 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     if ((int)blockIdx.x >= a.n_slots) return;
     lin = a.pair_order[blockIdx.x];
     if (lin < 0) return;
-  } else if (a.order_from_len) {
-    // scratch in the second K slot: its first copy comes after the loop's opening barrier
-    lin = item_from_lengths(a, (int*)(smem + NSPLIT * KT_BYTES));
-    if (lin < 0) return;
+  } else if (a.derive_order == 1) {
+    // the longest-first order of XCD range x % 8 (as pair_schedule_block cuts the ranges)
+    const int g = blockIdx.x % BSA_NXCD, k = blockIdx.x / BSA_NXCD;
+    const int lo = (int)(((int64_t)g * total + BSA_NXCD - 1) / BSA_NXCD);
+    const int hi = (int)(((int64_t)(g + 1) * total + BSA_NXCD - 1) / BSA_NXCD);
+    if (k >= hi - lo) return;
+    lin = kth_longest_item(a, row_ptr, (int*)smem, lo, hi - lo, k);
   } else {
     const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
     lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
     if (lin >= total) return;
+    if (a.derive_order == 2) {   // the same ranges, longest first inside each head
+      const int head0 = lin / npair * npair;
+      lin = kth_longest_item(a, row_ptr, (int*)smem, head0, npair, lin - head0);
+    }
   }
   const int bh = lin / npair, pidx = lin % npair;
   const int b = bh / a.H, h = bh % a.H;
@@ -486,7 +494,7 @@ hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, 
 template <int MODE, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * ((a.nb + 1) / 2);
-  dim3 grid(a.pair_order || a.order_from_len ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
+  dim3 grid(a.pair_order || a.derive_order == 1 ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
   hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
                      a.k_scale);
   return hipGetLastError();

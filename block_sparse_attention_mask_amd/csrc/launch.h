@@ -118,8 +118,9 @@ struct AttnArgs {
   const int32_t* row_len; int row_stride;
   const int32_t* pair_order;   // work order of the (head, query-block pair) items, or NULL;
   int n_slots;                 // its length (entries -1: no item)
-  int order_from_len;          // with row_len and no pair_order: each of the n_slots workgroups
-                               // derives its item of that order from the lengths
+  int derive_order;            // no pair_order: 1 = each of the n_slots workgroups derives its
+                               // item of that order from the list lengths; 2 = natural XCD
+                               // ranges, longest first inside each head; 0 = natural order
   const float* q_scale; const float* k_scale;
   int B, H, nb, S, S_valid, D;
   float scale_log2;      // softmax scale * log2(e)
