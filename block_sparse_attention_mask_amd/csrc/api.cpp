@@ -641,6 +641,7 @@ bsa_status block_sparse_attn_bwd(const bsa_tensor* q, const bsa_tensor* k, const
   if (scale <= 0.0) scale = 1.0 / std::sqrt((double)shape->D);
 
   bsa::BwdArgs a = {};
+  a.derive_order = shape->S / 64 >= HEAD_ORDER_MIN_NB ? 1 : 0;   // as the forward, for long rows
   a.q = q->ptr; a.q_sb = q->sb; a.q_sh = q->sh; a.q_ss = q->ss;
   a.k = k->ptr; a.k_sb = k->sb; a.k_sh = k->sh; a.k_ss = k->ss;
   a.v = v->ptr; a.v_sb = v->sb; a.v_sh = v->sh; a.v_ss = v->ss;

@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "item_order.h"
 #include "lds_tile.h"
 
 namespace bsa {
@@ -34,72 +35,6 @@ namespace bsa {
 // RESCALE_TAU (log2 units): the probabilities then stay below 2^TAU, far inside the
 // fp32 range, and the rescale of the output accumulators is skipped on most tiles.
 constexpr float RESCALE_TAU = 8.f;
-
-// Work orders derived inside the kernel. Item it = (head, pair p) costs the longer of
-// its two kv lists (clamped to [0, nb]); kth_longest_item returns the item at position k
-// of the items [lo, lo + R) ordered by decreasing cost, equal costs in ascending item
-// order, so that every workgroup derives the same order by itself: a cost histogram in
-// shared memory, a descending scan of it by one wave (the cost at position k and the
-// number of items above it), then one wave's ballots over the range find the item.
-// sm: nb + 1 + R + 3 ints; the trailing barrier lets the caller reuse them at once.
-// Every thread of the workgroup calls it.
-__device__ int kth_longest_item(const AttnArgs& a, const int32_t* __restrict__ row_ptr, int* sm, int lo, int R,
-                                int k) {
-  const int nb = a.nb, npair = (nb + 1) / 2;
-  const int t = threadIdx.x, lane = t & 63, nk = nb + 1;
-  int* hist = sm;
-  int* cost = sm + nk;
-  int* res = cost + R;
-  auto len = [&](int r) { return a.row_len ? a.row_len[r] : row_ptr[r + 1] - row_ptr[r]; };
-  for (int x = t; x < nk; x += 256) hist[x] = 0;
-  __syncthreads();
-  for (int i = t; i < R; i += 256) {
-    const int it = lo + i, p = it % npair, rA = (it / npair) * nb + 2 * p;
-    int c = len(rA);
-    if (2 * p + 1 < nb) c = max(c, len(rA + 1));
-    c = min(max(c, 0), nb);
-    cost[i] = c;
-    atomicAdd(&hist[c], 1);
-  }
-  __syncthreads();
-  if (t < 64) {
-    // lane chunks of keys in descending order; the chunk holding position k names the
-    // cost K there and the number of items with a larger cost
-    const int per = (nk + 63) / 64, k1 = nk - 1 - lane * per;
-    int sum = 0;
-    for (int e = 0; e < per; ++e)
-      if (k1 - e >= 0) sum += hist[k1 - e];
-    const int incl = wave_incl_scan_i32(sum);
-    int run = incl - sum;
-    if (run <= k && k < incl) {
-      for (int e = 0; e < per; ++e) {
-        const int key = k1 - e;
-        if (key < 0) break;
-        if (k < run + hist[key]) { res[0] = key; res[1] = run; break; }
-        run += hist[key];
-      }
-    }
-  }
-  __syncthreads();
-  const int K = res[0], need = k - res[1];         // the need-th item (ascending) of cost K
-  if (t < 64) {
-    int base = 0;
-    for (int i0 = 0; i0 < R; i0 += 64) {
-      const bool f = i0 + lane < R && cost[i0 + lane] == K;
-      const uint64_t b = __ballot(f);
-      const int n = __popcll(b);
-      if (need < base + n) {
-        if (f && __popcll(b & ((1ull << lane) - 1ull)) == need - base) res[2] = lo + i0 + lane;
-        break;
-      }
-      base += n;
-    }
-  }
-  __syncthreads();
-  const int item = res[2];
-  __syncthreads();
-  return item;
-}
 
 // MODE: ATTN_BF16, ATTN_SPLIT_F32, ATTN_FP8.  D: 64 or 128.
 //
@@ -154,6 +89,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   // blocks at the same pace, so they keep sharing tiles in L2).
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
+  auto list_len = [&](int r) { return a.row_len ? a.row_len[r] : row_ptr[r + 1] - row_ptr[r]; };
   int lin;
   if (a.pair_order) {
     if ((int)blockIdx.x >= a.n_slots) return;
@@ -165,14 +101,14 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     const int lo = (int)(((int64_t)g * total + BSA_NXCD - 1) / BSA_NXCD);
     const int hi = (int)(((int64_t)(g + 1) * total + BSA_NXCD - 1) / BSA_NXCD);
     if (k >= hi - lo) return;
-    lin = kth_longest_item(a, row_ptr, (int*)smem, lo, hi - lo, k);
+    lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, lo, hi - lo, k);
   } else {
     const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
     lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
     if (lin >= total) return;
     if (a.derive_order == 2) {   // the same ranges, longest first inside each head
       const int head0 = lin / npair * npair;
-      lin = kth_longest_item(a, row_ptr, (int*)smem, head0, npair, lin - head0);
+      lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, head0, npair, lin - head0);
     }
   }
   const int bh = lin / npair, pidx = lin % npair;

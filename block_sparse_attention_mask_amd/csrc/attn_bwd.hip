@@ -19,6 +19,7 @@
 //                     their kv lists (the forward's decomposition): dQ stays in registers.
 // No atomics: every output element is written once, so results are run-to-run exact.
 #include "common.h"
+#include "item_order.h"
 #include "launch.h"
 #include "lds_tile.h"
 
@@ -142,8 +143,13 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
   const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
-  const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
+  int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
   if (lin >= total) return;
+  if (a.derive_order) {   // the same ranges, longest first inside each head
+    const int head0 = lin / npair * npair;
+    lin = kth_longest_item<512>([&](int r) { return col_ptr[r + 1] - col_ptr[r]; }, a.nb, (int*)smem, head0,
+                                npair, lin - head0);
+  }
   const int bh = lin / npair, jA = 2 * (lin % npair);
   const int b = bh / a.H, h = bh % a.H;
   const bool hasB = jA + 1 < a.nb;
@@ -357,8 +363,13 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
   const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
-  const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
+  int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
   if (lin >= total) return;
+  if (a.derive_order) {   // the same ranges, longest first inside each head
+    const int head0 = lin / npair * npair;
+    lin = kth_longest_item<256>([&](int r) { return row_ptr[r + 1] - row_ptr[r]; }, a.nb, (int*)smem, head0,
+                                npair, lin - head0);
+  }
   const int bh = lin / npair, pidx = lin % npair;
   const int b = bh / a.H, h = bh % a.H;
   const int iA = 2 * pidx, iB = 2 * pidx + 1;

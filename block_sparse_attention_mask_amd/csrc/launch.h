@@ -144,6 +144,7 @@ struct BwdArgs {
   int B, H, nb, S, S_valid, D;
   float scale;           // softmax scale
   float scale_log2;      // scale * log2(e)
+  int derive_order;      // 1: longest first inside each head (kv-list lengths), else natural order
 };
 // (lse2, delta) per query into ld [B*H*S (+64 entries of padding read by the tile copies)]
 hipError_t launch_bwd_prep(const BwdArgs& a, float2* ld, hipStream_t st);
