@@ -631,3 +631,30 @@ def test_batched_model_layout_views(gpu_lib):
             O, _ = oracle.block_sparse_attention(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), keep[b, h], 64, Sv)
             err = np.abs(f64(o2[b, h]) - O)
             assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR, (b, h, err.max())
+
+
+def test_attention_head_order_writes_every_block(gpu_lib):
+    """Many rounds of long rows (nb = 512, 16 heads: more pairs than the ordered schedule
+    takes): each attention workgroup derives its pair from the kv-list lengths, longest
+    first inside each head. Every query block must be written exactly by its pair: the
+    output starts as NaN and every valid row must come back finite; sampled blocks match
+    the oracle."""
+    B, H, nb, D = 1, 16, 512, 128
+    S = nb * 64
+    sv = S - 24
+    g = torch.Generator(device="cpu").manual_seed(11)
+    q, k, v = (torch.randn(B, H, S, D, generator=g).mul_(0.5).to(torch.bfloat16).to(DEV) for _ in range(3))
+    rng = np.random.default_rng(12)
+    keep = rng.random((B, H, nb, nb)) < rng.uniform(0.02, 0.3, size=(B, H, nb, 1))   # lengths vary by row
+    keep[:, :, np.arange(nb), np.arange(nb)] = True
+    mask = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+    out = torch.full_like(q, float("nan"))
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=sv, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:, :, :sv]).all()
+    blocks = [(0, h, i) for h in (0, 7, 15) for i in (0, 1, 200, nb - 1)]
+    ref = oracle_attention_blocks(q, k, v, keep, blocks, sv)
+    mx, mean = attention_errors(out, ref)
+    print(f"[head order] max err {mx:.3e}, mean err {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
