@@ -434,11 +434,10 @@ static int work_order_slots(const bsa_shape* s) {
 // head's items longest first (at the 14B shape 46.5 ms against 49.7 ms per launch; the
 // order costs each workgroup a few microseconds, noise against items of ~2 ms).
 constexpr int HEAD_ORDER_MIN_NB = 512;
-static size_t sched_bytes(const bsa_shape* s) { return align256((size_t)work_order_slots(s) * 4); }
 
 size_t attn_csr_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
   if (!s || s->S <= 0 || s->D <= 0 || s->B < 1 || s->H < 1) return 0;
-  return sched_bytes(s) + (qk_dtype == BSA_F32 ? 6 * split_bytes(s) : 0);   // + hi/lo bf16 copies of f32 q, k, v
+  return qk_dtype == BSA_F32 ? 6 * split_bytes(s) : 0;   // hi/lo bf16 copies of f32 q, k, v
 }
 
 size_t attn_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
@@ -468,22 +467,15 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
   a.q_scale = q_scale; a.k_scale = k_scale;
   a.B = shape->B; a.H = shape->H; a.nb = shape->S / 64; a.S = shape->S; a.S_valid = shape->S_valid; a.D = shape->D;
   a.scale_log2 = (float)(scale * 1.4426950408889634);
-  const size_t sb_sched = sched_bytes(shape);
   const int slots = work_order_slots(shape);
   if (slots) {
-    if (!work_order && row_len) {
-      a.derive_order = 1;     // each workgroup derives its item from the lengths
-    } else if (!work_order) {
-      hipError_t e = bsa::launch_pair_schedule(row_ptr, shape->B * shape->H, shape->S / 64, (int32_t*)ws, hs);
-      if (e != hipSuccess) return hip_status(e, "schedule launch");
-      work_order = (const int32_t*)ws;
-    }
+    if (!work_order) a.derive_order = 1;   // each workgroup derives its item from the list lengths
     a.pair_order = work_order;
     a.n_slots = slots;
   } else if (shape->S / 64 >= HEAD_ORDER_MIN_NB) {
     a.derive_order = 2;       // many rounds of long rows: longest first inside each head
   }
-  void* split_ws = (char*)ws + sb_sched;
+  void* split_ws = ws;
   if (mode == bsa::ATTN_SPLIT_F32) {
     const size_t sb = split_bytes(shape);
     uint16_t* p[6];

@@ -269,8 +269,8 @@ bsa_status bsa_mask_to_csr_ordered(const uint8_t* mask, int64_t mask_sb, int64_t
  * base pointers 16-byte aligned).
  * block_sparse_attn_fwd_csr takes kv lists already built by bsa_mask_to_csr (for
  * masks reused across calls) and needs attn_csr_workspace_size(shape, q->dtype)
- * bytes, 256-byte aligned (room for the work order below and, for f32 inputs, the
- * hi/lo bf16 copies; ws may be NULL only when that size is 0).
+ * bytes, 256-byte aligned (for f32 inputs the hi/lo bf16 copies; the size is 0 for
+ * bf16 and fp8 inputs, and ws may then be NULL).
  *
  * Work order: one workgroup per pair of adjacent query blocks; the pairs are cut
  * into 8 contiguous ranges, one per XCD. When the pairs make at most four rounds over
@@ -280,8 +280,11 @@ bsa_status bsa_mask_to_csr_ordered(const uint8_t* mask, int64_t mask_sb, int64_t
  * runs in the natural order; -1: invalid shape); attn_work_order writes it for the
  * kv lists row_ptr into order (int32 [slots]; entry x is the pair index
  * (b*H + h) * ceil(nb/2) + p started by workgroup x, or -1). Pass it as work_order to
- * block_sparse_attn_fwd_csr to reuse it; with work_order NULL the entry points
- * compute it themselves (in ws). The order never changes the results.
+ * block_sparse_attn_fwd_csr to reuse it; with work_order NULL each attention workgroup
+ * derives its own item of that order from the kv-list lengths (no extra launch). Shapes
+ * with more pairs (0 slots) run the ranges in natural order, or, from nb = 512 on, with
+ * each head's pairs longest first, also derived in the kernel. The order never changes
+ * the results.
  * ------------------------------------------------------------------------- */
 size_t attn_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
 bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
