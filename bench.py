@@ -9,8 +9,12 @@ kept-tile FLOPs (4 * 64 * 64 * D per kept 64x64 tile) / step time. The roofline 
 is for the dominant kernel (the attention kernel), timed with HIP events on the stream
 it runs on; `cpu_baseline` times the fp64 oracle on a bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--dense] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--dense] [--dense-reps R] [--no-cpu-baseline]
     python bench.py --sweep [--config 5]    (threshold sweep table, bf16 and fp8 Q/K)
+
+The default workload is the 14B 720p shape (40 heads, 21x45x80 grid, NABLA thr 0.2); the
+line also carries dense attention of the same shape (the same kernel over an all-ones
+mask, timed after the sparse launches) and its speedup.
 """
 import argparse
 import json
@@ -46,7 +50,7 @@ def _measured_traffic(workload, fp8=False, dense=False):
     return rec["traffic_bytes_per_launch"].get(workload)
 
 
-def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_step=False):
+def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_step=False, dense_reps=0):
     import torch
     import block_sparse_attention_mask_amd as bsa
     from synth import make_inputs
@@ -210,11 +214,49 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
 
     mask_ms, csr_ms, attn_ms = phase_ms(phase_mask), phase_ms(phase_csr), phase_ms(phase_attn)
     kept = int(rp.sum().item()) if fused else int(rp[-1].item())
+    # attention launches so far (warm-ups, timed steps, the eager pass, the phase repeats);
+    # a kernel trace of this run splits its attention dispatches at this count
+    n_attn = warmup + (1 if graph else 0) + steps + steps + steps + 1
+    dense_ms = None
+    if dense_reps and not dense:
+        # dense attention of the same shape: the same kernel and call over an all-ones mask,
+        # after the sparse launches (one warm-up, then dense_reps timed back to back)
+        ones_rp, ones_ci = bsa.mask_to_csr(ones, B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
+        qd, kd = qa, ka
+        if fp8:
+            bsa.quantize_fp8_blocks(q, out=(qa, qs))
+            bsa.quantize_fp8_blocks(k, out=(ka, ks))
+
+        def dense_attn():
+            bsa.block_sparse_attn_fwd_csr(qd, kd, v, ones_rp, ones_ci, s_valid=cfg.S_valid, q_scale=qs, k_scale=ks,
+                                          out=out, ws=attn_ws)
+        dense_attn()
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for _ in range(dense_reps):
+            dense_attn()
+        d1.record()
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / dense_reps
     return dict(ms_per_step=ms_total / steps, wall_s=wall, mask_ms=mask_ms, csr_ms=csr_ms, attn_ms=attn_ms,
+                dense_ms=dense_ms, attn_launches={"sparse": n_attn, "dense": (1 + dense_reps) if dense_ms else 0},
                 eager_phase_ms=eager_ms, kv_lists="from the mask build" if fused else "compaction launch",
                 step_ms_median=per_step[len(per_step) // 2], step_ms_min=per_step[0],
                 kept_tiles=kept, kept_fraction=kept / (cfg.B * cfg.H * nb * nb), mask=m.cpu() if use_nabla else None,
                 q=q, k=k, v=v, qa=qa, ka=ka, qs=qs, ks=ks)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def run_cpu_baseline(cfg, thr, budget_s=15.0):
@@ -227,7 +269,7 @@ def run_cpu_baseline(cfg, thr, budget_s=15.0):
     except Exception:
         threads = os.cpu_count()
     from synth import make_inputs, get_config
-    c1 = get_config(cfg.cid, heads=min(cfg.H, 16))
+    c1 = get_config(cfg.cid, heads=min(cfg.H, 2))
     q, k, v = make_inputs(c1, seed=0, device="cpu")
     plane = None
     if cfg.sta is not None:
@@ -261,7 +303,8 @@ def run_cpu_baseline(cfg, thr, budget_s=15.0):
     dt = time.perf_counter() - t0
     per_block = t_attn / max(blocks_done, 1)
     full = t_mask / heads * cfg.B * cfg.H + per_block * cfg.B * cfg.H * cfg.nb
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "cpu_model": _cpu_model(),
+            "kind": "oracle",
             "oracle_s_per_head_mask": round(t_mask / heads, 4), "oracle_s_per_query_block": round(per_block, 6),
             "extrapolated_full_oracle_s": round(full, 1),
             "sample": f"{cfg.name}: NABLA/STA mask of {heads} head(s) + attention of {blocks_done} query blocks "
@@ -540,7 +583,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2, the 2B-DiT shape)")
+    ap.add_argument("--config", type=int, default=3, help="workload 1-5 (default 3, the 14B 720p shape)")
+    ap.add_argument("--dense-reps", type=int, default=3,
+                    help="timed launches of dense attention (all-ones mask, same kernel) after the sparse ones; "
+                         "0 skips the dense comparison")
     ap.add_argument("--thr", type=float, default=None, help="NABLA threshold (default: the config's first)")
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
     ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
@@ -576,11 +622,11 @@ def main():
         sys.exit(2)
 
     if args.sweep:
-        run_sweep(args.config if args.config != 2 else 5, min(args.steps, 5), min(args.warmup, 2))
+        run_sweep(args.config if args.config != 3 else 5, min(args.steps, 5), min(args.warmup, 2))
         return
     if args.topk_compare:
         from synth import get_config
-        cfg = get_config(args.config if args.config != 2 else 3)
+        cfg = get_config(args.config)
         run_topk_compare(cfg, min(args.steps, 5), min(args.warmup, 2), args.thr or cfg.thrs[0])
         return
     if args.reorder:
@@ -597,7 +643,7 @@ def main():
     cfg = get_config(args.config)
     thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
     r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=args.graph,
-                csr_step=args.csr_step)
+                csr_step=args.csr_step, dense_reps=args.dense_reps)
     fpt = _flops_per_tile(cfg.D)
     kept_flops = r["kept_tiles"] * fpt
     attn_tflops = kept_flops / (r["attn_ms"] * 1e-3) / 1e12
@@ -633,11 +679,20 @@ def main():
         # in it: the mask-build rate is then not an HBM rate
         "mask_build_llc_resident": qk_bytes <= LLC_BYTES if thr is not None else None,
         "kept_fraction": round(r["kept_fraction"], 5), "kept_tiles": r["kept_tiles"],
+        "attn_launches": r["attn_launches"],
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4),
                      "traffic": _measured_traffic(cfg.name, args.fp8, args.dense),
                      "kernel": "attn_fwd_kernel", "per_launch_flops": kept_flops},
     }
+    if r["dense_ms"]:
+        dense_flops = cfg.B * cfg.H * cfg.nb * cfg.nb * fpt
+        dense_tf = dense_flops / (r["dense_ms"] * 1e-3) / 1e12
+        line["dense"] = {"attn_ms": round(r["dense_ms"], 4), "tflops": round(dense_tf, 2),
+                         "frac_peak": round(dense_tf / peak, 4),
+                         "speedup_step_vs_dense": round(r["dense_ms"] / r["ms_per_step"], 3),
+                         "speedup_attn_vs_dense": round(r["dense_ms"] / r["attn_ms"], 3),
+                         "reps": args.dense_reps}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(cfg, None if args.dense else thr)
     print(json.dumps(line), flush=True)

@@ -67,16 +67,17 @@ def load(path: Optional[str] = None):
     i3 = ctypes.POINTER(ctypes.c_int)
     sig = {
         "nabla_workspace_size": (sz, [PS]),
-        "nabla_build_mask": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, sz, vp]),
+        "nabla_build_mask": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, vp, sz, vp]),
         "nabla_build_mask_topk": (i32, [PT, PT, PS, i32, dbl, vp, i64, i64, vp, vp, sz, vp]),
         "quantize_fp8_blocks": (i32, [PT, PS, PT, vp, vp]),
-        "nabla_build_mask_fp8": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, PT, vp, PT, vp, vp, sz, vp]),
+        "nabla_build_mask_fp8": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, PT, vp, PT, vp, vp, sz, vp]),
         "sta_workspace_size": (sz, [PS]),
         "sta_build_mask": (i32, [PS, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
         "nabla_sta_workspace_size": (sz, [PS]),
-        "nabla_build_mask_sta": (i32, [PT, PT, PS, dbl, dbl, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
+        "nabla_build_mask_sta": (i32, [PT, PT, PS, dbl, dbl, i3, i3, i3, i32, i3, vp, vp, vp, sz, vp]),
         "nabla_lists_workspace_size": (sz, [PS]),
-        "nabla_build_mask_lists": (i32, [PT, PT, PS, dbl, dbl, i3, i3, i3, i32, i3, vp, vp, vp, vp, vp, sz, vp]),
+        "nabla_build_mask_lists": (i32, [PT, PT, PS, dbl, dbl, i3, i3, i3, i32, i3, vp, vp, vp, vp, vp, vp, sz,
+                                         vp]),
         "mask_or": (i32, [vp, vp, i64, vp, i64, vp]),
         "csr_workspace_size": (sz, [i32, i32, i32]),
         "bsa_mask_to_csr": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
@@ -148,24 +149,42 @@ def _mask_strides(mask: torch.Tensor):
     return mask.data_ptr(), sb, sh, mask
 
 
+def _near_buffer(q, near):
+    """near: False (no flags), True (a new [B,H,nb,nb] uint8 buffer) or a tensor to fill."""
+    if near is None or near is False:
+        return None
+    if near is True:
+        B, H, S, _ = q.shape
+        return torch.empty(B, H, S // 64, S // 64, dtype=torch.uint8, device=q.device)
+    if near.dtype != torch.uint8 or not near.is_contiguous():
+        raise ValueError("near-threshold flags must be a contiguous uint8 [B, H, nb, nb] tensor")
+    return near
+
+
 def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Optional[float] = None,
-                     or_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """NABLA adaptive block mask of q, k [B,H,S,D] (bf16 or f32) -> uint8 [B,H,S/64,S/64]."""
+                     or_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     near=False):
+    """NABLA adaptive block mask of q, k [B,H,S,D] (bf16 or f32) -> uint8 [B,H,S/64,S/64].
+
+    near=True (or a uint8 [B,H,nb,nb] tensor): also the near-threshold flags (1 where the
+    block's exclusive cumulative mass lies within 1e-6 of 1 - thr); returns (mask, flags)."""
     lib = load()
     B, H, S, D = q.shape
     nb = S // 64
     shp = _shape(q, None)
     if out is None:
         out = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device)
+    nf = _near_buffer(q, near)
     ws = _ws(lib.nabla_workspace_size(ctypes.byref(shp)), q.device)
     om, osb, osh = None, 0, 0
     if or_mask is not None:
         om, osb, osh, _keep = _mask_strides(or_mask)
     tq, tk = _tensor(q), _tensor(k)
     _check(lib.nabla_build_mask(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
-                                float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(), ws.data_ptr(),
-                                ws.numel(), _stream(q.device)))
-    return out
+                                float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(),
+                                nf.data_ptr() if nf is not None else None, ws.data_ptr(), ws.numel(),
+                                _stream(q.device)))
+    return (out, nf) if nf is not None else out
 
 
 def nabla_build_mask_topk(q: torch.Tensor, k: torch.Tensor, topk: int, scale: Optional[float] = None,
@@ -211,10 +230,11 @@ def quantize_fp8_blocks(x: torch.Tensor, out: Optional[Tuple[torch.Tensor, torch
 
 def nabla_build_mask_fp8(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Optional[float] = None,
                          or_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                         q8_out=None, k8_out=None):
+                         q8_out=None, k8_out=None, near=False):
     """nabla_build_mask plus the fp8 block quantisation of q and k from the same read.
 
-    Returns (mask, (q codes, q scales), (k codes, k scales))."""
+    Returns (mask, (q codes, q scales), (k codes, k scales)), with near also the flags
+    (mask, flags, (q codes, q scales), (k codes, k scales))."""
     lib = load()
     B, H, S, D = q.shape
     nb = S // 64
@@ -227,11 +247,15 @@ def nabla_build_mask_fp8(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Op
     om, osb, osh = None, 0, 0
     if or_mask is not None:
         om, osb, osh, _keep = _mask_strides(or_mask)
+    nf = _near_buffer(q, near)
     tq, tk, tq8, tk8 = _tensor(q), _tensor(k), _tensor(q8), _tensor(k8)
     _check(lib.nabla_build_mask_fp8(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
                                     float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(),
+                                    nf.data_ptr() if nf is not None else None,
                                     ctypes.byref(tq8), qs.data_ptr(), ctypes.byref(tk8), ks.data_ptr(),
                                     ws.data_ptr(), ws.numel(), _stream(q.device)))
+    if nf is not None:
+        return out, nf, (q8, qs), (k8, ks)
     return out, (q8, qs), (k8, ks)
 
 
@@ -257,9 +281,10 @@ def sta_build_mask(S: int, S_valid: int, grid: Sequence[int], tile: Sequence[int
 def nabla_build_mask_sta(q: torch.Tensor, k: torch.Tensor, thr: float, grid: Sequence[int], tile: Sequence[int],
                          window: Sequence[int], order: str = "row", order_tile: Optional[Sequence[int]] = None,
                          s_valid: Optional[int] = None, scale: Optional[float] = None,
-                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         out: Optional[torch.Tensor] = None, near=False):
     """NABLA mask of q, k OR'd with the sliding-tile mask of the grid in one call
-    -> uint8 [B,H,S/64,S/64] (equal to nabla_build_mask(..., or_mask=sta_build_mask(...)))."""
+    -> uint8 [B,H,S/64,S/64] (equal to nabla_build_mask(..., or_mask=sta_build_mask(...)));
+    with near, (mask, near-threshold flags of the adaptive rule)."""
     lib = load()
     B, H, S, D = q.shape
     nb = S // 64
@@ -269,12 +294,14 @@ def nabla_build_mask_sta(q: torch.Tensor, k: torch.Tensor, thr: float, grid: Seq
     ws = _ws(lib.nabla_sta_workspace_size(ctypes.byref(shp)), q.device)
     arr = ctypes.c_int * 3
     ot = arr(*order_tile) if order_tile is not None else None
+    nf = _near_buffer(q, near)
     tq, tk = _tensor(q), _tensor(k)
     _check(lib.nabla_build_mask_sta(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
                                     float(scale) if scale else 0.0, arr(*grid), arr(*tile), arr(*window),
-                                    0 if order == "row" else 1, ot, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                    0 if order == "row" else 1, ot, out.data_ptr(),
+                                    nf.data_ptr() if nf is not None else None, ws.data_ptr(), ws.numel(),
                                     _stream(q.device)))
-    return out
+    return (out, nf) if nf is not None else out
 
 
 def nabla_lists_workspace(q: torch.Tensor, s_valid: Optional[int] = None) -> torch.Tensor:
@@ -289,11 +316,12 @@ def nabla_build_mask_lists(q: torch.Tensor, k: torch.Tensor, thr: float, grid: O
                            tile: Optional[Sequence[int]] = None, window: Optional[Sequence[int]] = None,
                            order: str = "row", order_tile: Optional[Sequence[int]] = None,
                            s_valid: Optional[int] = None, scale: Optional[float] = None, work_order: bool = True,
-                           out=None, ws: Optional[torch.Tensor] = None):
+                           out=None, ws: Optional[torch.Tensor] = None, near=None):
     """The mask of nabla_build_mask_sta (grid None: of nabla_build_mask) with, from the same
     launch, the kv lists -> (mask uint8 [B,H,nb,nb], kv_len int32 [B*H*nb], kv_idx int32
     [B*H*nb, nb] (row r's kept blocks, ascending, in kv_idx[r, :kv_len[r]]), work order
-    int32 [slots] or None when the shape runs in the default order). nb <= 256."""
+    int32 [slots] or None when the shape runs in the default order). nb <= 256. near: an
+    optional uint8 [B,H,nb,nb] tensor filled with the near-threshold flags (not returned)."""
     lib = load()
     B, H, S, D = q.shape
     nb = S // 64
@@ -313,10 +341,12 @@ def nabla_build_mask_lists(q: torch.Tensor, k: torch.Tensor, thr: float, grid: O
     t3 = arr(*tile) if tile is not None else None
     w3 = arr(*window) if window is not None else None
     ot = arr(*order_tile) if order_tile is not None else None
+    nf = _near_buffer(q, near)
     tq, tk = _tensor(q), _tensor(k)
     _check(lib.nabla_build_mask_lists(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
                                       float(scale) if scale else 0.0, g3, t3, w3, 0 if order == "row" else 1, ot,
-                                      mask.data_ptr(), kv_len.data_ptr(), kv_idx.data_ptr(),
+                                      mask.data_ptr(), nf.data_ptr() if nf is not None else None,
+                                      kv_len.data_ptr(), kv_idx.data_ptr(),
                                       wo.data_ptr() if wo is not None else None, ws.data_ptr(), ws.numel(),
                                       _stream(q.device)))
     return mask, kv_len, kv_idx, wo
@@ -409,6 +439,17 @@ def block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
     return plan.out
 
 
+def attn_work_order_slots(q: torch.Tensor, s_valid: Optional[int] = None) -> int:
+    """Length of the attention work order for tensors shaped like q (0: the shape runs in
+    the default order, each workgroup deriving its item in the kernel)."""
+    lib = load()
+    shp = _shape(q, s_valid)
+    n = lib.attn_work_order_slots(ctypes.byref(shp))
+    if n < 0:
+        raise BsaError(1, lib.bsa_last_error().decode())
+    return int(n)
+
+
 def attn_work_order(q: torch.Tensor, row_ptr: torch.Tensor, s_valid: Optional[int] = None,
                     out: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
     """Work order of the attention kernel for the kv lists row_ptr (int32 [slots], -1 =
@@ -417,7 +458,7 @@ def attn_work_order(q: torch.Tensor, row_ptr: torch.Tensor, s_valid: Optional[in
     shp = _shape(q, s_valid)
     n = lib.attn_work_order_slots(ctypes.byref(shp))
     if n < 0:
-        raise BsaError(lib.bsa_last_error().decode())
+        raise BsaError(1, lib.bsa_last_error().decode())
     if n == 0:
         return None
     if out is None:

@@ -80,7 +80,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 9; }
+int bsa_abi_version(void) { return 10; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -89,12 +89,27 @@ size_t nabla_workspace_size(const bsa_shape* s) {
   return 2 * align256(bh * nbp * (size_t)s->D * sizeof(double));
 }
 
+// Near-threshold band of the cumulative-mass rule: flagged entries have an exclusive
+// mass E with |E - (1 - thr)| <= NEAR_BAND, evaluated on the fixed-point mass E 2^60:
+// floor((1 - thr - band) 2^60) <= E 2^60 <= floor((1 - thr + band) 2^60).
+constexpr double NEAR_BAND = 1e-6;
+
+static bsa::SelNear near_targets(uint8_t* flags, double thr) {
+  bsa::SelNear n = {flags, 0, 0};
+  if (!flags) return n;
+  const double lo = 1.0 - thr - NEAR_BAND, hi = 1.0 - thr + NEAR_BAND;
+  n.t_lo = lo > 0.0 ? (uint64_t)std::floor(std::ldexp(lo, 60)) : 0;
+  n.t_hi = (uint64_t)std::floor(std::ldexp(hi, 60)) + 1;
+  return n;
+}
+
 static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
                                uint8_t* mask_out, const bsa::Fp8Out* f8, void* ws, size_t ws_bytes,
                                bsa_stream_t stream, int topk = 0, bsa::StaRule sta = {0, 0, 0, 0, 0, 0},
                                const bsa::StaGeom* plane_geom = nullptr, uint8_t* plane = nullptr,
-                               void* sta_ws = nullptr, const bsa::SelLists* lists = nullptr) {
+                               void* sta_ws = nullptr, const bsa::SelLists* lists = nullptr,
+                               uint8_t* near_out = nullptr) {
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
   if ((st = check_tensor("q", q, shape)) != BSA_OK) return st;
@@ -106,6 +121,7 @@ static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const b
   const int nb = shape->S / 64;
   if (nb > 2048) return fail(BSA_EUNSUPPORTED, "nb=%d exceeds 2048 blocks per sequence", nb);
   if (!mask_out) return fail(BSA_EINVAL, "mask_out is NULL");
+  if (near_out && near_out == mask_out) return fail(BSA_EINVAL, "near_thr_out must not alias mask_out");
   if (or_mask && (or_sb < 0 || or_sh < 0)) return fail(BSA_EINVAL, "or_mask strides must be >= 0");
   const size_t need = nabla_workspace_size(shape);
   if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
@@ -129,15 +145,16 @@ static bsa_status nabla_common(const bsa_tensor* q, const bsa_tensor* k, const b
   if (e != hipSuccess) return hip_status(e, "pool launch");
   const uint64_t T_fixed = (uint64_t)std::ldexp(1.0 - thr, 60);
   e = bsa::launch_select(qbar, kbarT, shape->B, shape->H, nb, shape->D, scale, T_fixed, topk, or_mask, or_sb,
-                         or_sh, sta, mask_out, hs, sl);
+                         or_sh, sta, mask_out, hs, sl, near_targets(topk ? nullptr : near_out, thr));
   return hip_status(e, "select launch");
 }
 
 bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                             double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh, uint8_t* mask_out,
-                            void* ws, size_t ws_bytes, bsa_stream_t stream) {
+                            uint8_t* near_thr_out, void* ws, size_t ws_bytes, bsa_stream_t stream) {
   g_err.clear();
-  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, nullptr, ws, ws_bytes, stream);
+  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, nullptr, ws, ws_bytes, stream, 0,
+                      bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr, nullptr, nullptr, near_thr_out);
 }
 
 static bsa_status check_fp8_out(const char* name, const bsa_tensor* c, const float* sc, const bsa_shape* shape) {
@@ -171,15 +188,17 @@ bsa_status nabla_build_mask_topk(const bsa_tensor* q, const bsa_tensor* k, const
 
 bsa_status nabla_build_mask_fp8(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                 double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                                uint8_t* mask_out, const bsa_tensor* q8, float* q_scale, const bsa_tensor* k8,
-                                float* k_scale, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+                                uint8_t* mask_out, uint8_t* near_thr_out, const bsa_tensor* q8, float* q_scale,
+                                const bsa_tensor* k8, float* k_scale, void* ws, size_t ws_bytes,
+                                bsa_stream_t stream) {
   g_err.clear();
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
   if ((st = check_fp8_out("q8", q8, q_scale, shape)) != BSA_OK) return st;
   if ((st = check_fp8_out("k8", k8, k_scale, shape)) != BSA_OK) return st;
   const bsa::Fp8Out f8 = fp8_out(q8, q_scale, k8, k_scale);
-  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, &f8, ws, ws_bytes, stream);
+  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, &f8, ws, ws_bytes, stream, 0,
+                      bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr, nullptr, nullptr, near_thr_out);
 }
 
 bsa_status quantize_fp8_blocks(const bsa_tensor* x, const bsa_shape* shape, const bsa_tensor* codes, float* scales,
@@ -254,8 +273,8 @@ size_t nabla_sta_workspace_size(const bsa_shape* s) {
 
 bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                 double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
-                                int token_order, const int order_tile_thw[3], uint8_t* mask_out, void* ws,
-                                size_t ws_bytes, bsa_stream_t stream) {
+                                int token_order, const int order_tile_thw[3], uint8_t* mask_out,
+                                uint8_t* near_thr_out, void* ws, size_t ws_bytes, bsa_stream_t stream) {
   g_err.clear();
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
@@ -267,11 +286,12 @@ bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const 
   const bsa::StaRule rule = bsa::sta_rule_of(g);
   const size_t nws = nabla_workspace_size(shape);
   if (rule.bpt)   // aligned layout: the rule is applied inside the select
-    return nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule);
+    return nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule, nullptr,
+                        nullptr, nullptr, nullptr, near_thr_out);
   // otherwise the sliding-tile plane is built in the workspace and OR'd like any mask
   const size_t nb = (size_t)shape->S / 64;
   return nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule, &g,
-                      (uint8_t*)ws + nws, (char*)ws + nws + align256(nb * nb));
+                      (uint8_t*)ws + nws, (char*)ws + nws + align256(nb * nb), nullptr, near_thr_out);
 }
 
 static int work_order_slots(const bsa_shape* s);
@@ -280,9 +300,9 @@ size_t nabla_lists_workspace_size(const bsa_shape* s) { return nabla_sta_workspa
 
 bsa_status nabla_build_mask_lists(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                   double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
-                                  int token_order, const int order_tile_thw[3], uint8_t* mask_out, int32_t* kv_len,
-                                  int32_t* kv_idx, int32_t* work_order, void* ws, size_t ws_bytes,
-                                  bsa_stream_t stream) {
+                                  int token_order, const int order_tile_thw[3], uint8_t* mask_out,
+                                  uint8_t* near_thr_out, int32_t* kv_len, int32_t* kv_idx, int32_t* work_order,
+                                  void* ws, size_t ws_bytes, bsa_stream_t stream) {
   g_err.clear();
   bsa_status st;
   if ((st = check_shape(shape)) != BSA_OK) return st;
@@ -301,17 +321,17 @@ bsa_status nabla_build_mask_lists(const bsa_tensor* q, const bsa_tensor* k, cons
   const bsa::SelLists lists = {kv_len, kv_idx};
   if (!grid_thw) {
     st = nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0,
-                      bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr, nullptr, &lists);
+                      bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr, nullptr, &lists, near_thr_out);
   } else {
     bsa::StaGeom g;
     if ((st = sta_geom_from(shape, grid_thw, tile_thw, win_thw, token_order, order_tile_thw, &g)) != BSA_OK) return st;
     const bsa::StaRule rule = bsa::sta_rule_of(g);
     if (rule.bpt)   // aligned layout: the rule inside the selection
       st = nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule, nullptr,
-                        nullptr, nullptr, &lists);
+                        nullptr, nullptr, &lists, near_thr_out);
     else            // the sliding-tile plane built in the workspace first
       st = nabla_common(q, k, shape, thr, scale, nullptr, 0, 0, mask_out, nullptr, ws, nws, stream, 0, rule, &g,
-                        (uint8_t*)ws + nws, (char*)ws + nws + align256((size_t)nb * nb), &lists);
+                        (uint8_t*)ws + nws, (char*)ws + nws + align256((size_t)nb * nb), &lists, near_thr_out);
   }
   if (st != BSA_OK || !work_order) return st;
   // the work order from the list lengths: one small launch (a single workgroup)

@@ -91,22 +91,32 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   const int total = a.B * a.H * npair;
   auto list_len = [&](int r) { return a.row_len ? a.row_len[r] : row_ptr[r + 1] - row_ptr[r]; };
   int lin;
+  // (the in-kernel orders keep their tables in smem; where they would not fit, the
+  // workgroups keep the natural order of the same ranges)
   if (a.pair_order) {
     if ((int)blockIdx.x >= a.n_slots) return;
     lin = a.pair_order[blockIdx.x];
-    if (lin < 0) return;
-  } else if (a.derive_order == 1) {
+    if (lin < 0 || lin >= total) return;   // -1 = no item; larger entries belong to another shape
+  } else if (a.derive_order == 1 && kth_longest_fits(a.nb, (total + BSA_NXCD - 1) / BSA_NXCD, sizeof(smem))) {
     // the longest-first order of XCD range x % 8 (as pair_schedule_block cuts the ranges)
     const int g = blockIdx.x % BSA_NXCD, k = blockIdx.x / BSA_NXCD;
     const int lo = (int)(((int64_t)g * total + BSA_NXCD - 1) / BSA_NXCD);
     const int hi = (int)(((int64_t)(g + 1) * total + BSA_NXCD - 1) / BSA_NXCD);
     if (k >= hi - lo) return;
     lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, lo, hi - lo, k);
+  } else if (a.derive_order == 1) {
+    // the same ranges as above in natural order (a grid of n_slots workgroups)
+    const int g = blockIdx.x % BSA_NXCD, k = blockIdx.x / BSA_NXCD;
+    const int lo = (int)(((int64_t)g * total + BSA_NXCD - 1) / BSA_NXCD);
+    const int hi = (int)(((int64_t)(g + 1) * total + BSA_NXCD - 1) / BSA_NXCD);
+    if (k >= hi - lo) return;
+    lin = lo + k;
   } else {
     const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
     lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
     if (lin >= total) return;
-    if (a.derive_order == 2) {   // the same ranges, longest first inside each head
+    if (a.derive_order == 2 && kth_longest_fits(a.nb, npair, sizeof(smem))) {
+      // the same ranges, longest first inside each head
       const int head0 = lin / npair * npair;
       lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, head0, npair, lin - head0);
     }

@@ -145,7 +145,9 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
   const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
   int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
   if (lin >= total) return;
-  if (a.derive_order) {   // the same ranges, longest first inside each head
+  if (a.derive_order && kth_longest_fits(a.nb, npair, sizeof(smem))) {
+    // the same ranges, longest first inside each head (natural order where its tables
+    // would not fit in smem)
     const int head0 = lin / npair * npair;
     lin = kth_longest_item<512>([&](int r) { return col_ptr[r + 1] - col_ptr[r]; }, a.nb, (int*)smem, head0,
                                 npair, lin - head0);
@@ -365,7 +367,9 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
   const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
   int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
   if (lin >= total) return;
-  if (a.derive_order) {   // the same ranges, longest first inside each head
+  if (a.derive_order && kth_longest_fits(a.nb, npair, sizeof(smem))) {
+    // the same ranges, longest first inside each head (natural order where its tables
+    // would not fit in smem)
     const int head0 = lin / npair * npair;
     lin = kth_longest_item<256>([&](int r) { return row_ptr[r + 1] - row_ptr[r]; }, a.nb, (int*)smem, head0,
                                 npair, lin - head0);

@@ -11,8 +11,14 @@ namespace bsa {
 // decreasing cost, equal costs in ascending item order, so that every workgroup derives
 // the same order by itself: a cost histogram in shared memory, a descending scan of it
 // by one wave (the cost at position k and the number of items above it), then one
-// wave's ballots over the range find the item. sm: nb + 1 + R + 3 ints; the trailing
-// barrier lets the caller reuse them at once. All NT threads of the workgroup call it.
+// wave's ballots over the range find the item. sm: kth_longest_ints(nb, R) ints; the
+// trailing barrier lets the caller reuse them at once. All NT threads of the workgroup
+// call it. A caller whose shared buffer is smaller (kth_longest_fits false) keeps the
+// natural order instead: the order never changes what is computed.
+__host__ __device__ constexpr int kth_longest_ints(int nb, int R) { return nb + 1 + R + 3; }
+__host__ __device__ constexpr bool kth_longest_fits(int nb, int R, int sm_bytes) {
+  return kth_longest_ints(nb, R) <= sm_bytes / 4;
+}
 template <int NT, typename Len>
 __device__ int kth_longest_item(Len len, int nb, int* sm, int lo, int R, int k) {
   const int npair = (nb + 1) / 2;

@@ -47,12 +47,19 @@ struct SelLists {
   int32_t* kv_idx;
 };
 constexpr int SELR_MAX_NB = 256;
+// near-threshold flags (flags == NULL: none): an entry's flag is 1 iff its exclusive
+// fixed-point mass E satisfies t_lo <= E < t_hi; flags have mask_out's layout
+struct SelNear {
+  uint8_t* flags;
+  uint64_t t_lo, t_hi;
+};
 // T_fixed = floor((1 - thr) 2^60) for the cumulative-mass rule; topk > 0 keeps the
 // topk largest entries of each row instead (T_fixed unused). The result is OR'd with
 // or_mask (if any) and with the sliding-tile rule sta (if sta.bpt > 0).
 hipError_t launch_select(const double* qbar, const double* kbarT, int B, int H, int nb, int D, double scale,
                          uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                         StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists = SelLists{});
+                         StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists = SelLists{},
+                         const SelNear& near = SelNear{});
 
 // sta.hip
 struct StaGeom {

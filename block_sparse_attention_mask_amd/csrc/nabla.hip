@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
 constexpr int SEL_ROWS = 16;
 constexpr int SEL_WAVES = 8;
 
-enum : int { ROW_ACTIVE = 0, ROW_PIVOT = 1, ROW_ALL = 2, ROW_TIE = 3, ROW_SKIP = 4 };
+enum : int { ROW_ACTIVE = 0, ROW_PIVOT = 1, ROW_ALL = 2, ROW_TIE = 3, ROW_SKIP = 4, ROW_NONE = 5 };
 
 struct SelRowState {
   uint64_t lo;         // current key range [lo, lo + 2^span)
@@ -200,6 +200,33 @@ struct SelRowState {
   int cnt;             // candidates in the range
   int tie_keep;        // number of tied entries kept (ROW_TIE)
 };
+
+// State of a row before its radix select for one target: every entry is kept when the row's
+// total fixed-point mass stays below the target (Top-k: nb <= topk), none when the target
+// is 0 (no entry has an exclusive mass below 0), else the pivot is searched.
+__device__ __forceinline__ SelRowState sel_init(bool skip, uint64_t total, uint64_t target, bool by_count, int nb,
+                                                int topk) {
+  SelRowState n;
+  n.lo = 0;
+  n.mass_above = 0;
+  n.span = -1;
+  n.cnt = 0;
+  n.tie_keep = 0;
+  if (skip) n.status = ROW_SKIP;
+  else if (by_count ? nb <= topk : total < target) n.status = ROW_ALL;
+  else if (!by_count && target == 0) n.status = ROW_NONE;
+  else n.status = ROW_ACTIVE;
+  return n;
+}
+
+// Whether an entry with this key is kept once its row's state is final; tied: the key
+// equals the row's tied key value (ROW_TIE), rank: its position among those by index.
+__device__ __forceinline__ bool sel_keep(const SelRowState& sr, uint64_t key, bool tied, int rank) {
+  if (sr.status == ROW_ALL) return true;
+  if (sr.status == ROW_PIVOT) return key >= sr.lo;
+  if (sr.status == ROW_TIE) return tied ? rank < sr.tie_keep : key > sr.lo;
+  return false;   // ROW_NONE, ROW_SKIP
+}
 
 __device__ __forceinline__ uint64_t fixed_mass(double p) {
   // p in [0, 1]  ->  floor(p * 2^60)
@@ -270,21 +297,26 @@ __device__ __forceinline__ void reduced_map_strip(const double* __restrict__ qmf
 // topk > 0 selects the Top-k alternative (NABLA review, Appendix C: a fixed number of
 // blocks per row): the same descending order, the radix passes search the key at which
 // the COUNT of entries reaches topk instead of the mass reaching 1 - thr.
-template <int NCT, int KS>   // KS = D / 4 k-steps of the f64 MFMA
+// NEAR: the near-threshold flags too. An entry's exclusive mass E lies in the band
+// [T_lo, T_hi) iff it is kept under target T_hi and not under T_lo, so the radix select
+// runs for those two targets as well (on the same keys) and the row's write ORs nothing
+// into the flags.
+template <int NCT, int KS, bool NEAR>   // KS = D / 4 k-steps of the f64 MFMA
 __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __restrict__ qmf,
                                                                const double* __restrict__ kmf, int nb, int D,
                                                                double scale, uint64_t T_fixed, int topk,
                                                                const uint8_t* __restrict__ or_mask, int64_t or_sb,
                                                                int64_t or_sh, StaRule sta, int H,
-                                                               uint8_t* __restrict__ mask_out) {
+                                                               uint8_t* __restrict__ mask_out, SelNear nr) {
+  constexpr int NTG = NEAR ? 3 : 1;   // targets: the rule; with NEAR also T_lo, T_hi
   const bool by_count = topk > 0;
-  const uint64_t target = by_count ? (uint64_t)topk : T_fixed;
   __shared__ uint64_t hmass[SEL_ROWS][256];
   __shared__ uint32_t hcnt[SEL_ROWS][256];
-  __shared__ uint32_t tiebits[SEL_ROWS][64];
+  __shared__ uint32_t tiebits[NTG][SEL_ROWS][64];
   __shared__ double red[SEL_ROWS][SEL_WAVES];
   __shared__ uint64_t redu[SEL_ROWS][SEL_WAVES];
-  __shared__ SelRowState st[SEL_ROWS];
+  __shared__ uint64_t row_total[SEL_ROWS];
+  __shared__ SelRowState st[NTG][SEL_ROWS];
   __shared__ int any_active;
   __shared__ double qa_lds[32 * 64];   // the 16 rows' Qbar operands, MFMA order
 
@@ -356,127 +388,125 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
   }
   __syncthreads();
   if (tid < SEL_ROWS) {
-    const int r = tid;
     uint64_t total = 0;
-    for (int x = 0; x < SEL_WAVES; ++x) total += redu[r][x];
-    SelRowState n;
-    n.lo = 0;
-    n.mass_above = 0;
-    n.span = -1;
-    n.cnt = 0;
-    n.tie_keep = 0;
-    if (row0 + r >= nb) n.status = ROW_SKIP;
-    else if (by_count ? nb <= topk : total < T_fixed) n.status = ROW_ALL;   // every entry is kept
-    else n.status = ROW_ACTIVE;
-    st[r] = n;
+    for (int x = 0; x < SEL_WAVES; ++x) total += redu[tid][x];
+    row_total[tid] = total;
   }
-  if (tid == 0) any_active = 1;
-  __syncthreads();
 
-  // ---- radix select of the pivot, all rows in lock step
-  for (int pass = 0; pass < 9; ++pass) {
-    if (!any_active) break;
-    for (int x = tid; x < SEL_ROWS * 256; x += SEL_WAVES * 64) {
-      hmass[x / 256][x % 256] = 0;
-      hcnt[x / 256][x % 256] = 0;
-    }
+  for (int t = 0; t < NTG; ++t) {
+    const uint64_t target = by_count ? (uint64_t)topk : (t == 0 ? T_fixed : t == 1 ? nr.t_lo : nr.t_hi);
+    __syncthreads();   // row totals written; every wave is done with the previous target's state
+    if (tid < SEL_ROWS) st[t][tid] = sel_init(row0 + tid >= nb, row_total[tid], target, by_count, nb, topk);
+    if (tid == 0) any_active = 1;
     __syncthreads();
+
+    // ---- radix select of the pivot, all rows in lock step
+    for (int pass = 0; pass < 9; ++pass) {
+      if (!any_active) break;
+      for (int x = tid; x < SEL_ROWS * 256; x += SEL_WAVES * 64) {
+        hmass[x / 256][x % 256] = 0;
+        hcnt[x / 256][x % 256] = 0;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 4 * v + g;
-      const SelRowState sr = st[r];
-      if (sr.status != ROW_ACTIVE) continue;
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * v + g;
+        const SelRowState sr = st[t][r];
+        if (sr.status != ROW_ACTIVE) continue;
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        if (colof(c) >= nb) continue;
-        const uint64_t key = (uint64_t)__double_as_longlong(acc[c][v]);
-        const int dg = sel_digit(key, sr);
-        if (dg >= 0) {
-          atomicAdd((unsigned long long*)&hmass[r][dg], (unsigned long long)key);
-          atomicAdd(&hcnt[r][dg], 1u);
+        for (int c = 0; c < NCT; ++c) {
+          if (colof(c) >= nb) continue;
+          const uint64_t key = (uint64_t)__double_as_longlong(acc[c][v]);
+          const int dg = sel_digit(key, sr);
+          if (dg >= 0) {
+            atomicAdd((unsigned long long*)&hmass[r][dg], (unsigned long long)key);
+            atomicAdd(&hcnt[r][dg], 1u);
+          }
         }
       }
-    }
-    __syncthreads();
-    // each wave scans SEL_ROWS / SEL_WAVES rows: lane l owns buckets 255-4l .. 252-4l
-    for (int r = w; r < SEL_ROWS; r += SEL_WAVES) {
-      const SelRowState sr = st[r];
-      if (sr.status != ROW_ACTIVE) continue;
-      uint64_t mb[4];
-      uint32_t cb[4];
-      uint64_t lt = 0;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        cb[x] = hcnt[r][255 - 4 * l - x];
-        mb[x] = by_count ? (uint64_t)cb[x] : hmass[r][255 - 4 * l - x];   // what the target counts
-        lt += mb[x];
-      }
-      const uint64_t incl = wave_incl_scan_u64(lt);
-      const uint64_t before = sr.mass_above + (incl - lt);
-      const uint64_t ball = __ballot(before + lt >= target);
-      const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
-      if (l == L) {
-        uint64_t cum = before;
-        int xs = 3;
+      __syncthreads();
+      // each wave scans SEL_ROWS / SEL_WAVES rows: lane l owns buckets 255-4l .. 252-4l
+      for (int r = w; r < SEL_ROWS; r += SEL_WAVES) {
+        const SelRowState sr = st[t][r];
+        if (sr.status != ROW_ACTIVE) continue;
+        uint64_t mb[4];
+        uint32_t cb[4];
+        uint64_t lt = 0;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          if (cum + mb[x] >= target) { xs = x; break; }
-          cum += mb[x];
+          cb[x] = hcnt[r][255 - 4 * l - x];
+          mb[x] = by_count ? (uint64_t)cb[x] : hmass[r][255 - 4 * l - x];   // what the target counts
+          lt += mb[x];
         }
-        const int dg = 255 - 4 * l - xs;
-        SelRowState n = sr;
-        n.mass_above = cum;
-        n.cnt = (int)cb[xs];
-        if (sr.span < 0) {
-          first_range(dg, n.lo, n.span);
-        } else {
-          const int db = sr.span < 8 ? sr.span : 8;
-          n.span = sr.span - db;
-          n.lo = sr.lo + ((uint64_t)dg << n.span);
+        const uint64_t incl = wave_incl_scan_u64(lt);
+        const uint64_t before = sr.mass_above + (incl - lt);
+        const uint64_t ball = __ballot(before + lt >= target);
+        const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
+        if (l == L) {
+          uint64_t cum = before;
+          int xs = 3;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            if (cum + mb[x] >= target) { xs = x; break; }
+            cum += mb[x];
+          }
+          const int dg = 255 - 4 * l - xs;
+          SelRowState n = sr;
+          n.mass_above = cum;
+          n.cnt = (int)cb[xs];
+          if (sr.span < 0) {
+            first_range(dg, n.lo, n.span);
+          } else {
+            const int db = sr.span < 8 ? sr.span : 8;
+            n.span = sr.span - db;
+            n.lo = sr.lo + ((uint64_t)dg << n.span);
+          }
+          if (n.cnt <= 1) n.status = ROW_PIVOT;
+          else if (n.span == 0) {
+            // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
+            const uint64_t wq = by_count ? 1 : n.lo;
+            const uint64_t need = target - n.mass_above;           // > 0
+            const uint64_t tk = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
+            n.tie_keep = (int)(tk < (uint64_t)n.cnt ? tk : (uint64_t)n.cnt);
+            n.status = ROW_TIE;
+          }
+          st[t][r] = n;
         }
-        if (n.cnt <= 1) n.status = ROW_PIVOT;
-        else if (n.span == 0) {
-          // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
-          const uint64_t wq = by_count ? 1 : n.lo;
-          const uint64_t need = target - n.mass_above;           // > 0
-          const uint64_t t = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
-          n.tie_keep = (int)(t < (uint64_t)n.cnt ? t : (uint64_t)n.cnt);
-          n.status = ROW_TIE;
-        }
-        st[r] = n;
       }
+      __syncthreads();
+      if (tid == 0) {
+        int act = 0;
+        for (int r = 0; r < SEL_ROWS; ++r) act |= st[t][r].status == ROW_ACTIVE;
+        any_active = act;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (tid == 0) {
-      int act = 0;
-      for (int r = 0; r < SEL_ROWS; ++r) act |= st[r].status == ROW_ACTIVE;
-      any_active = act;
-    }
-    __syncthreads();
-  }
 
-  // ---- ties: rank tied entries by ascending column index
-  bool need_ties = false;
-  for (int r = 0; r < SEL_ROWS; ++r) need_ties |= st[r].status == ROW_TIE;
-  if (need_ties) {
-    for (int x = tid; x < SEL_ROWS * 64; x += SEL_WAVES * 64) tiebits[x / 64][x % 64] = 0;
-    __syncthreads();
+    // ---- ties: rank tied entries by ascending column index
+    bool need_ties = false;
+    for (int r = 0; r < SEL_ROWS; ++r) need_ties |= st[t][r].status == ROW_TIE;
+    if (need_ties) {
+      for (int x = tid; x < SEL_ROWS * 64; x += SEL_WAVES * 64) tiebits[t][x / 64][x % 64] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 4 * v + g;
-      if (st[r].status != ROW_TIE) continue;
-      const uint64_t lo = st[r].lo;
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * v + g;
+        if (st[t][r].status != ROW_TIE) continue;
+        const uint64_t lo = st[t][r].lo;
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        const int j = colof(c);
-        if (j < nb && (uint64_t)__double_as_longlong(acc[c][v]) == lo) atomicOr(&tiebits[r][j >> 5], 1u << (j & 31));
+        for (int c = 0; c < NCT; ++c) {
+          const int j = colof(c);
+          if (j < nb && (uint64_t)__double_as_longlong(acc[c][v]) == lo)
+            atomicOr(&tiebits[t][r][j >> 5], 1u << (j & 31));
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---- write the mask rows (OR'd with the optional mask and the sliding-tile rule;
-  // the rule's tile coordinates of this lane's columns are formed once)
+  // the rule's tile coordinates of this lane's columns are formed once); with NEAR the
+  // flags of the band [T_lo, T_hi) (never OR'd)
   const int b = bh / H, h = bh % H;
   StaCoord cc[NCT];
 #pragma unroll
@@ -484,29 +514,33 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_kernel(const double* __
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int r = 4 * v + g;
-    const SelRowState sr = st[r];
-    if (sr.status == ROW_SKIP) continue;
+    SelRowState srs[NTG];
+#pragma unroll
+    for (int t = 0; t < NTG; ++t) srs[t] = st[t][r];
+    if (srs[0].status == ROW_SKIP) continue;
     const int row = row0 + r;
     const StaCoord rc = sta.bpt ? sta_rule_coord(sta, row) : StaCoord{0, 0, 0};
     uint8_t* dst = mask_out + ((int64_t)bh * nb + row) * nb;
+    uint8_t* ndst = NEAR ? nr.flags + ((int64_t)bh * nb + row) * nb : nullptr;
     const uint8_t* om = or_mask ? or_mask + b * or_sb + h * or_sh + (int64_t)row * nb : nullptr;
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       const int j = colof(c);
       if (j >= nb) continue;
       const uint64_t key = (uint64_t)__double_as_longlong(acc[c][v]);
-      bool keep;
-      if (sr.status == ROW_ALL) keep = true;
-      else if (sr.status == ROW_PIVOT) keep = key >= sr.lo;
-      else {   // ROW_TIE
-        if (key != sr.lo) keep = key > sr.lo;
-        else {
-          int rank = 0;
-          for (int x = 0; x < (j >> 5); ++x) rank += __popc(tiebits[r][x]);
-          rank += __popc(tiebits[r][j >> 5] & ((1u << (j & 31)) - 1u));
-          keep = rank < sr.tie_keep;
+      bool kt[NTG];
+#pragma unroll
+      for (int t = 0; t < NTG; ++t) {
+        const bool tied = srs[t].status == ROW_TIE && key == srs[t].lo;
+        int rank = 0;
+        if (tied) {
+          for (int x = 0; x < (j >> 5); ++x) rank += __popc(tiebits[t][r][x]);
+          rank += __popc(tiebits[t][r][j >> 5] & ((1u << (j & 31)) - 1u));
         }
+        kt[t] = sel_keep(srs[t], key, tied, rank);
       }
+      bool keep = kt[0];
+      if constexpr (NEAR) ndst[j] = kt[2] && !kt[1] ? 1 : 0;
       if ((om && om[j]) || (sta.bpt && sta_rule_near(sta, rc, cc[c]))) keep = true;
       dst[j] = keep ? 1 : 0;
     }
@@ -537,18 +571,18 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int L) {
 // product, recomputed), each taking SEL_ROWS / SELR_SPLIT of its rows: more workgroups
 // and fewer rows one after the other in a wave.
 constexpr int SELR_SPLIT = 2;
-template <int NCT, int KS>   // NCT = column tiles per wave (nb <= 128 NCT)
+template <int NCT, int KS, bool NEAR>   // NCT = column tiles per wave (nb <= 128 NCT)
 __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const double* __restrict__ qmf,
                                                                     const double* __restrict__ kmf, int nb,
                                                                     double scale, uint64_t T_fixed, int topk,
                                                                     const uint8_t* __restrict__ or_mask,
                                                                     int64_t or_sb, int64_t or_sh, StaRule sta,
                                                                     int H, uint8_t* __restrict__ mask_out,
-                                                                    SelLists lists) {
+                                                                    SelLists lists, SelNear nr) {
   constexpr int E = 2 * NCT;                        // entries per lane per row
   constexpr int NBP = SEL_WAVES * 16 * NCT;         // map row length
+  constexpr int NTG = NEAR ? 3 : 1;                 // targets: the rule; with NEAR also T_lo, T_hi
   const bool by_count = topk > 0;
-  const uint64_t target = by_count ? (uint64_t)topk : T_fixed;
   __shared__ double qa_lds[32 * 64];
   __shared__ double map[SEL_ROWS][NBP];
   __shared__ uint64_t hmass[SEL_WAVES][256];
@@ -607,103 +641,111 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
     }
     const uint64_t total = wave_sum_u64(ms);
 
-    // ---- radix select of the pivot; the row state is wave-uniform
-    SelRowState sr;
-    sr.lo = 0;
-    sr.mass_above = 0;
-    sr.span = -1;
-    sr.cnt = 0;
-    sr.tie_keep = 0;
-    sr.status = (by_count ? nb <= topk : total < T_fixed) ? ROW_ALL : ROW_ACTIVE;
-    for (int pass = 0; pass < 9 && sr.status == ROW_ACTIVE; ++pass) {
+    // ---- radix select of the pivot for each target; the row state is wave-uniform
+    SelRowState srs[NTG];
 #pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        hmass[w][4 * l + x4] = 0;
-        hcnt[w][4 * l + x4] = 0;
-      }
-      __builtin_amdgcn_wave_barrier();
+    for (int t = 0; t < NTG; ++t) {
+      const uint64_t target = by_count ? (uint64_t)topk : (t == 0 ? T_fixed : t == 1 ? nr.t_lo : nr.t_hi);
+      SelRowState sr = sel_init(false, total, target, by_count, nb, topk);
+      for (int pass = 0; pass < 9 && sr.status == ROW_ACTIVE; ++pass) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (!valid[e]) continue;
-        const int dg = sel_digit(key[e], sr);
-        if (dg >= 0) {
-          atomicAdd((unsigned long long*)&hmass[w][dg], (unsigned long long)key[e]);
-          atomicAdd(&hcnt[w][dg], 1u);
+        for (int x4 = 0; x4 < 4; ++x4) {
+          hmass[w][4 * l + x4] = 0;
+          hcnt[w][4 * l + x4] = 0;
         }
-      }
-      __builtin_amdgcn_wave_barrier();
-      // lane l owns buckets 255-4l .. 252-4l (descending keys)
-      uint64_t mb[4];
-      uint32_t cb[4];
-      uint64_t lt = 0;
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        cb[x4] = hcnt[w][255 - 4 * l - x4];
-        mb[x4] = by_count ? (uint64_t)cb[x4] : hmass[w][255 - 4 * l - x4];   // what the target counts
-        lt += mb[x4];
-      }
-      const uint64_t incl = wave_incl_scan_u64(lt);
-      const uint64_t before = sr.mass_above + (incl - lt);
-      const uint64_t ball = __ballot(before + lt >= target);
-      const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
-      // the crossing bucket of lane L, found by every lane from lane L's values
-      uint64_t cum = readlane_u64(before, L);
-      int xs = 3, cnt = 0;
-#pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        const uint64_t mbl = readlane_u64(mb[x4], L);
-        const int cbl = __builtin_amdgcn_readlane((int)cb[x4], L);
-        if (xs == 3 && x4 < 3) {
-          if (cum + mbl >= target) { xs = x4; cnt = cbl; }
-          else cum += mbl;
-        } else if (x4 == 3 && xs == 3) {
-          cnt = cbl;
+        for (int e = 0; e < E; ++e) {
+          if (!valid[e]) continue;
+          const int dg = sel_digit(key[e], sr);
+          if (dg >= 0) {
+            atomicAdd((unsigned long long*)&hmass[w][dg], (unsigned long long)key[e]);
+            atomicAdd(&hcnt[w][dg], 1u);
+          }
         }
+        __builtin_amdgcn_wave_barrier();
+        // lane l owns buckets 255-4l .. 252-4l (descending keys)
+        uint64_t mb[4];
+        uint32_t cb[4];
+        uint64_t lt = 0;
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+          cb[x4] = hcnt[w][255 - 4 * l - x4];
+          mb[x4] = by_count ? (uint64_t)cb[x4] : hmass[w][255 - 4 * l - x4];   // what the target counts
+          lt += mb[x4];
+        }
+        const uint64_t incl = wave_incl_scan_u64(lt);
+        const uint64_t before = sr.mass_above + (incl - lt);
+        const uint64_t ball = __ballot(before + lt >= target);
+        const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
+        // the crossing bucket of lane L, found by every lane from lane L's values
+        uint64_t cum = readlane_u64(before, L);
+        int xs = 3, cnt = 0;
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+          const uint64_t mbl = readlane_u64(mb[x4], L);
+          const int cbl = __builtin_amdgcn_readlane((int)cb[x4], L);
+          if (xs == 3 && x4 < 3) {
+            if (cum + mbl >= target) { xs = x4; cnt = cbl; }
+            else cum += mbl;
+          } else if (x4 == 3 && xs == 3) {
+            cnt = cbl;
+          }
+        }
+        const int dg = 255 - 4 * L - xs;
+        SelRowState n = sr;
+        n.mass_above = cum;
+        n.cnt = cnt;
+        if (sr.span < 0) {
+          first_range(dg, n.lo, n.span);
+        } else {
+          const int db = sr.span < 8 ? sr.span : 8;
+          n.span = sr.span - db;
+          n.lo = sr.lo + ((uint64_t)dg << n.span);
+        }
+        if (n.cnt <= 1) n.status = ROW_PIVOT;
+        else if (n.span == 0) {
+          // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
+          const uint64_t wq = by_count ? 1 : n.lo;
+          const uint64_t need = target - n.mass_above;           // > 0
+          const uint64_t tk = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
+          n.tie_keep = (int)(tk < (uint64_t)n.cnt ? tk : (uint64_t)n.cnt);
+          n.status = ROW_TIE;
+        }
+        sr = n;
       }
-      const int dg = 255 - 4 * L - xs;
-      SelRowState n = sr;
-      n.mass_above = cum;
-      n.cnt = cnt;
-      if (sr.span < 0) {
-        first_range(dg, n.lo, n.span);
-      } else {
-        const int db = sr.span < 8 ? sr.span : 8;
-        n.span = sr.span - db;
-        n.lo = sr.lo + ((uint64_t)dg << n.span);
-      }
-      if (n.cnt <= 1) n.status = ROW_PIVOT;
-      else if (n.span == 0) {
-        // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
-        const uint64_t wq = by_count ? 1 : n.lo;
-        const uint64_t need = target - n.mass_above;           // > 0
-        const uint64_t t = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
-        n.tie_keep = (int)(t < (uint64_t)n.cnt ? t : (uint64_t)n.cnt);
-        n.status = ROW_TIE;
-      }
-      sr = n;
+      srs[t] = sr;
     }
 
     // ---- write the row (OR'd with the optional mask); tied keys ranked by ascending
-    // index; with lists, the kept blocks also go to the row's kv list in ascending order
+    // index; with lists, the kept blocks also go to the row's kv list in ascending order;
+    // with NEAR the flags of the band [T_lo, T_hi) (never OR'd)
     const int64_t grow = (int64_t)bh * nb + row;
     uint8_t* dst = mask_out + grow * nb;
+    uint8_t* ndst = NEAR ? nr.flags + grow * nb : nullptr;
     const uint8_t* om = or_mask ? or_mask + b * or_sb + h * or_sh + (int64_t)row * nb : nullptr;
     int32_t* lst = lists.kv_idx ? lists.kv_idx + grow * nb : nullptr;
-    int tie_base = 0, nkept = 0;
+    int tie_base[NTG];
+#pragma unroll
+    for (int t = 0; t < NTG; ++t) tie_base[t] = 0;
+    int nkept = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = 64 * e + l;
-      const bool tied = sr.status == ROW_TIE && valid[e] && key[e] == sr.lo;
-      const uint64_t tb = __ballot(tied);
-      const int rank = tie_base + __popcll(tb & ((1ull << l) - 1ull));
-      tie_base += __popcll(tb);
-      bool keep = false;
+      bool kt[NTG];
+#pragma unroll
+      for (int t = 0; t < NTG; ++t) {
+        const bool tied = srs[t].status == ROW_TIE && valid[e] && key[e] == srs[t].lo;
+        const uint64_t tb = __ballot(tied);
+        const int rank = tie_base[t] + __popcll(tb & ((1ull << l) - 1ull));
+        tie_base[t] += __popcll(tb);
+        kt[t] = valid[e] && sel_keep(srs[t], key[e], tied, rank);
+      }
+      bool keep = kt[0];
       if (valid[e]) {
-        if (sr.status == ROW_ALL) keep = true;
-        else if (sr.status == ROW_PIVOT) keep = key[e] >= sr.lo;
-        else keep = tied ? rank < sr.tie_keep : key[e] > sr.lo;
         if ((om && om[j]) || (sta.bpt && sta_rule_near(sta, rc, cc[e]))) keep = true;
         dst[j] = keep ? 1 : 0;
+        if constexpr (NEAR) ndst[j] = kt[2] && !kt[1] ? 1 : 0;
       }
       if (lst) {
         const uint64_t kb = __ballot(keep);
@@ -753,49 +795,54 @@ hipError_t launch_pool(bool f32, int D, const void* q, const int64_t* qs, const 
                  : launch_pool_t<u16, 128>(q, qs, k, ks, B, H, nb, qbar, kbarT, f8, st);
 }
 
-template <int NCT>
+template <int NCT, bool NEAR>
 static hipError_t launch_select_c(const double* qmf, const double* kmf, int B, int H, int nb, int D,
                                   double scale, uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb,
-                                  int64_t or_sh, StaRule sta, uint8_t* mask_out, hipStream_t st) {
+                                  int64_t or_sh, StaRule sta, uint8_t* mask_out, hipStream_t st, const SelNear& nr) {
   dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS, B * H);
   if (D == 64)
-    hipLaunchKernelGGL((select_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
+    hipLaunchKernelGGL((select_kernel<NCT, 16, NEAR>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale,
+                       T_fixed, topk, or_mask, or_sb, or_sh, sta, H, mask_out, nr);
   else
-    hipLaunchKernelGGL((select_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, sta, H, mask_out);
+    hipLaunchKernelGGL((select_kernel<NCT, 32, NEAR>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, D, scale,
+                       T_fixed, topk, or_mask, or_sb, or_sh, sta, H, mask_out, nr);
   return hipGetLastError();
 }
 
-template <int NCT>
+template <int NCT, bool NEAR>
 static hipError_t launch_select_rows(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
                                      uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                                     StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists) {
+                                     StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists,
+                                     const SelNear& nr) {
   dim3 grid((nb + SEL_ROWS - 1) / SEL_ROWS * SELR_SPLIT, B * H);
   if (D == 64)
-    hipLaunchKernelGGL((select_rows_kernel<NCT, 16>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, sta, H, mask_out, lists);
+    hipLaunchKernelGGL((select_rows_kernel<NCT, 16, NEAR>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale,
+                       T_fixed, topk, or_mask, or_sb, or_sh, sta, H, mask_out, lists, nr);
   else
-    hipLaunchKernelGGL((select_rows_kernel<NCT, 32>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale, T_fixed,
-                       topk, or_mask, or_sb, or_sh, sta, H, mask_out, lists);
+    hipLaunchKernelGGL((select_rows_kernel<NCT, 32, NEAR>), grid, dim3(SEL_WAVES * 64), 0, st, qmf, kmf, nb, scale,
+                       T_fixed, topk, or_mask, or_sb, or_sh, sta, H, mask_out, lists, nr);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
-                         uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                         StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists) {
+template <bool NEAR>
+static hipError_t launch_select_n(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
+                                  uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                                  StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists,
+                                  const SelNear& nr) {
   const int ntile = (nb + 15) / 16;
   const int nct = (ntile + SEL_WAVES - 1) / SEL_WAVES;
   if (nb <= SELR_MAX_NB) {
     if (nct == 1)
-      return launch_select_rows<1>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out,
-                                   st, lists);
-    return launch_select_rows<2>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st,
-                                 lists);
+      return launch_select_rows<1, NEAR>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta,
+                                         mask_out, st, lists, nr);
+    return launch_select_rows<2, NEAR>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta,
+                                       mask_out, st, lists, nr);
   }
   if (lists.kv_idx || lists.kv_len) return hipErrorInvalidValue;   // short rows only
-#define BSA_SEL_CASE(n) \
-  case n: return launch_select_c<n>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st);
+#define BSA_SEL_CASE(n)                                                                                         \
+  case n:                                                                                                      \
+    return launch_select_c<n, NEAR>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, \
+                                    mask_out, st, nr);
   switch (nct) {
     BSA_SEL_CASE(1) BSA_SEL_CASE(2) BSA_SEL_CASE(3) BSA_SEL_CASE(4) BSA_SEL_CASE(5) BSA_SEL_CASE(6)
     BSA_SEL_CASE(7) BSA_SEL_CASE(8) BSA_SEL_CASE(9) BSA_SEL_CASE(10) BSA_SEL_CASE(11) BSA_SEL_CASE(12)
@@ -803,6 +850,17 @@ hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int
     default: return hipErrorInvalidValue;
   }
 #undef BSA_SEL_CASE
+}
+
+hipError_t launch_select(const double* qmf, const double* kmf, int B, int H, int nb, int D, double scale,
+                         uint64_t T_fixed, int topk, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                         StaRule sta, uint8_t* mask_out, hipStream_t st, const SelLists& lists,
+                         const SelNear& near) {
+  if (near.flags)
+    return launch_select_n<true>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st,
+                                 lists, near);
+  return launch_select_n<false>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, mask_out, st,
+                                lists, near);
 }
 
 }  // namespace bsa

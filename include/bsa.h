@@ -88,18 +88,30 @@ typedef struct {
  *              sliding-tile mask [NABLA: the adaptive mask may be OR'd with STA];
  *              plane strides or_sb, or_sh in bytes (0, 0 = one shared plane)
  *   mask_out   uint8 [B,H,nb,nb], contiguous; written with 0/1
+ *   near_thr_out  optional (NULL = none) uint8 [B,H,nb,nb], contiguous, distinct
+ *              from mask_out: 1 where the block's exclusive cumulative mass E (the
+ *              mass of the entries visited before it) lies within 1e-6 of the
+ *              threshold, |E - (1 - thr)| <= 1e-6, else 0 [NABLA, "Core claim": the
+ *              prefix reaching 1 - thr; blocks this close to it are the ones an fp64
+ *              evaluation in another summation order may decide either way]. The
+ *              flag describes the adaptive rule only (an OR'd mask does not change
+ *              it). Asking for the flags runs the selection for the two band edges
+ *              as well, which costs time; the mask is the same either way.
  *   ws         device workspace of at least nabla_workspace_size(shape) bytes,
  *              256-byte aligned; its contents on entry do not matter
  * The reduced map, softmax and cumulative mass are evaluated in fp64 (the
- * cumulative mass in 2^-60 fixed point), so a block whose exclusive cumulative
- * mass lies within ~1e-12 of 1 - thr may be decided differently from an
- * exact-arithmetic evaluation; all others are decided exactly.
+ * cumulative mass in 2^-60 fixed point, E 2^60 compared with floor((1 - thr) 2^60)
+ * and, for the flags, with floor((1 - thr -+ 1e-6) 2^60)), so a block whose
+ * exclusive cumulative mass lies within ~1e-12 of 1 - thr (of a band edge) may be
+ * decided (flagged) differently from an exact-arithmetic evaluation; all others
+ * are decided exactly.
  * ------------------------------------------------------------------------- */
 size_t nabla_workspace_size(const bsa_shape* shape);
 bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
                             double thr, double scale,
                             const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
-                            uint8_t* mask_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
+                            uint8_t* mask_out, uint8_t* near_thr_out,
+                            void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Top-k block selection [NABLA review, Appendix C / Theorem 1: the fixed-count
@@ -127,8 +139,9 @@ bsa_status nabla_build_mask_topk(const bsa_tensor* q, const bsa_tensor* k, const
  * quantize_fp8_blocks: x bf16 or f32 [B,H,S,D] -> codes (dtype BSA_FP8_E4M3FN,
  *   [B,H,S,D], own strides) and scales float [B,H,nb] contiguous. All S rows are
  *   quantised (zero padding gives code 0).
- * nabla_build_mask_fp8: nabla_build_mask plus the quantisation of q and k from the
- *   same read (q8, q_scale, k8, k_scale as codes, scales above); same workspace.
+ * nabla_build_mask_fp8: nabla_build_mask (with its optional near_thr_out) plus the
+ *   quantisation of q and k from the same read (q8, q_scale, k8, k_scale as codes,
+ *   scales above); same workspace.
  * Errors as for nabla_build_mask; BSA_EINVAL for a codes tensor of another dtype or
  * misaligned scales.
  * ------------------------------------------------------------------------- */
@@ -137,6 +150,7 @@ bsa_status quantize_fp8_blocks(const bsa_tensor* x, const bsa_shape* shape, cons
 bsa_status nabla_build_mask_fp8(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
                                 double thr, double scale,
                                 const uint8_t* or_mask, int64_t or_sb, int64_t or_sh, uint8_t* mask_out,
+                                uint8_t* near_thr_out,
                                 const bsa_tensor* q8, float* q_scale, const bsa_tensor* k8, float* k_scale,
                                 void* ws, size_t ws_bytes, bsa_stream_t stream);
 
@@ -169,7 +183,8 @@ bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const i
  * every head. For tile-major layouts of whole tiles made of whole blocks (no padding)
  * the sliding-tile rule is evaluated inside the selection and no plane is built;
  * otherwise the plane is built in the workspace first.
- *   q, k, shape, thr, scale, mask_out   as nabla_build_mask
+ *   q, k, shape, thr, scale, mask_out, near_thr_out   as nabla_build_mask (the flags
+ *              describe the adaptive rule, before the sliding tiles are OR'd in)
  *   grid_thw .. order_tile_thw          as sta_build_mask (T*H*W must equal S_valid)
  *   ws         at least nabla_sta_workspace_size(shape) bytes, 256-byte aligned
  * Errors as the two calls; every check precedes any launch.
@@ -177,8 +192,8 @@ bsa_status sta_build_mask(const bsa_shape* shape, const int grid_thw[3], const i
 size_t nabla_sta_workspace_size(const bsa_shape* shape);
 bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                 double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
-                                int token_order, const int order_tile_thw[3], uint8_t* mask_out, void* ws,
-                                size_t ws_bytes, bsa_stream_t stream);
+                                int token_order, const int order_tile_thw[3], uint8_t* mask_out,
+                                uint8_t* near_thr_out, void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * The mask of nabla_build_mask_sta (or of nabla_build_mask with no or_mask, when
@@ -186,8 +201,8 @@ bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const 
  * attention work order [NABLA: the binary block mask tells the operator which blocks
  * to compute; CalibAtt skip lists]. The lists come out of the same launch that writes
  * the mask rows: there is no separate pass over the mask.
- *   q .. mask_out  as nabla_build_mask_sta; grid_thw NULL: no sliding tiles (tile_thw,
- *                  win_thw, token_order, order_tile_thw unused)
+ *   q .. near_thr_out  as nabla_build_mask_sta; grid_thw NULL: no sliding tiles
+ *                  (tile_thw, win_thw, token_order, order_tile_thw unused)
  *   kv_len     int32 [B*H*nb]: the number of kept kv blocks of row r = (b*H + h)*nb + i
  *   kv_idx     int32 [B*H*nb*nb]: row r's kept kv blocks, ascending, at
  *              kv_idx[r*nb .. r*nb + kv_len[r]); the rest of the row is not written
@@ -203,9 +218,9 @@ bsa_status nabla_build_mask_sta(const bsa_tensor* q, const bsa_tensor* k, const 
 size_t nabla_lists_workspace_size(const bsa_shape* shape);
 bsa_status nabla_build_mask_lists(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
                                   double scale, const int grid_thw[3], const int tile_thw[3], const int win_thw[3],
-                                  int token_order, const int order_tile_thw[3], uint8_t* mask_out, int32_t* kv_len,
-                                  int32_t* kv_idx, int32_t* work_order, void* ws, size_t ws_bytes,
-                                  bsa_stream_t stream);
+                                  int token_order, const int order_tile_thw[3], uint8_t* mask_out,
+                                  uint8_t* near_thr_out, int32_t* kv_len, int32_t* kv_idx, int32_t* work_order,
+                                  void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Union of block masks [NABLA: adaptive mask OR sliding-tile mask].

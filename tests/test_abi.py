@@ -31,18 +31,18 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 9
+    assert lib.bsa_abi_version() == 10
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
     return bsa.Tensor(ptr, dtype, 0, 0, ss)
 
 
-def _nabla(lib, shape, thr=0.2, q=None, k=None, mask=4096, ws=8192, ws_bytes=1 << 40):
+def _nabla(lib, shape, thr=0.2, q=None, k=None, mask=4096, ws=8192, ws_bytes=1 << 40, near=None):
     q = q or _t()
     k = k or _t()
     return lib.nabla_build_mask(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), thr, 0.0, None, 0, 0, mask,
-                                ws, ws_bytes, None)
+                                near, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("shape,thr,msg", [
@@ -68,6 +68,8 @@ def test_nabla_rejects_misaligned_and_mixed(lib):
     assert _nabla(lib, shape, k=_t(dtype=bsa.BSA_F32)) == 2
     assert _nabla(lib, shape, ws_bytes=16) == 3
     assert "workspace" in lib.bsa_last_error().decode()
+    assert _nabla(lib, shape, near=4096) == 1                 # flags may not alias the mask
+    assert "alias" in lib.bsa_last_error().decode()
     assert _nabla(lib, shape, mask=None) == 1
 
 
@@ -94,16 +96,16 @@ def test_nabla_sta_rejects(lib):
     need = lib.nabla_sta_workspace_size(ctypes.byref(shape))
     assert need >= lib.nabla_workspace_size(ctypes.byref(shape)) + 16
     st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 0.1, 0.0, a3(4, 8, 8), a3(4, 8, 8), a3(3, 2, 3), 0,
-           None, 8192, 1 << 16, need, None)
+           None, 8192, None, 1 << 16, need, None)
     assert st == 1 and "odd" in lib.bsa_last_error().decode()
     st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 0.1, 0.0, a3(4, 8, 9), a3(4, 8, 8), a3(3, 3, 3), 0,
-           None, 8192, 1 << 16, need, None)
+           None, 8192, None, 1 << 16, need, None)
     assert st == 1 and "S_valid" in lib.bsa_last_error().decode()
     st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 0.1, 0.0, a3(4, 8, 8), a3(4, 8, 8), a3(3, 3, 3), 0,
-           None, 8192, 1 << 16, need - 1, None)
+           None, 8192, None, 1 << 16, need - 1, None)
     assert st == 3
     st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), 1.5, 0.0, a3(4, 8, 8), a3(4, 8, 8), a3(3, 3, 3), 0,
-           None, 8192, 1 << 16, need, None)
+           None, 8192, None, 1 << 16, need, None)
     assert st == 1 and "thr" in lib.bsa_last_error().decode()
 
 
@@ -116,7 +118,7 @@ def test_nabla_lists_rejects(lib):
     def call(shape, kv_len=8192, kv_idx=16384, order=None, ws_bytes=None, thr=0.1, grid=None):
         need = lib.nabla_lists_workspace_size(ctypes.byref(shape))
         return f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(shape), thr, 0.0, grid, a3(4, 8, 8) if grid else None,
-                 a3(3, 3, 3) if grid else None, 0, None, 32768, kv_len, kv_idx, order, 1 << 16,
+                 a3(3, 3, 3) if grid else None, 0, None, 32768, None, kv_len, kv_idx, order, 1 << 16,
                  need if ws_bytes is None else ws_bytes, None)
     small = bsa.Shape(1, 2, 256, 256, 128, 64)
     assert lib.nabla_lists_workspace_size(ctypes.byref(small)) >= lib.nabla_sta_workspace_size(ctypes.byref(small))
@@ -213,7 +215,7 @@ def test_fp8_entry_points_reject_bad_arguments(lib):
     assert lib.quantize_fp8_blocks(ctypes.byref(x), ctypes.byref(shape), ctypes.byref(codes), 4098, None) == 1
     assert lib.quantize_fp8_blocks(ctypes.byref(codes), ctypes.byref(shape), ctypes.byref(codes), 4096, None) == 2
     st = lib.nabla_build_mask_fp8(ctypes.byref(x), ctypes.byref(x), ctypes.byref(shape), 0.2, 0.0, None, 0, 0, 4096,
-                                  ctypes.byref(codes), None, ctypes.byref(codes), 4096, 8192, 1 << 40, None)
+                                  None, ctypes.byref(codes), None, ctypes.byref(codes), 4096, 8192, 1 << 40, None)
     assert st == 1 and "scales" in lib.bsa_last_error().decode()
 
 

@@ -129,6 +129,36 @@ def test_backward_full_size_sampled(gpu_lib, cid):
         _check_head(f"dv[{h}]", dv[0, h], rv, rows)
 
 
+def test_backward_order_tables_past_shared_memory(gpu_lib):
+    """D = 64 with nb = 5460 key blocks in one head: the dQ kernel's shared buffer (8192 ints)
+    cannot hold the longest-first order's tables (nb + 1 + ceil(nb/2) + 3 ints), so its
+    workgroups keep the natural order; every gradient row is still written (NaN-initialised
+    outputs) and sampled blocks match the oracle."""
+    B, H, nb, D = 1, 1, 5460, 64
+    S = nb * 64
+    sv = S - 17
+    g = torch.Generator(device="cpu").manual_seed(5)
+    q, k, v, do = (torch.randn(B, H, S, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(4))
+    rng = np.random.default_rng(6)
+    keep = np.zeros((nb, nb), bool)
+    keep[np.arange(nb), np.arange(nb)] = True
+    keep[np.arange(nb)[:, None], rng.integers(0, nb, size=(nb, 4))] = True
+    m = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+    o, lse = gpu_lib.block_sparse_attn_fwd(q, k, v, m, s_valid=sv, return_lse=True)
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    dq, dk, dv = gpu_lib.block_sparse_attn_bwd(q, k, v, o, do, lse, m, s_valid=sv, out=grads)
+    torch.cuda.synchronize()
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isfinite(x).all(), name
+    blocks = [0, 1, nb // 2, nb - 1]
+    rows = _rows(blocks, S)
+    rq, rk, rv = oracle.block_sparse_attention_bwd(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(do[0, 0]), keep,
+                                                   64, sv, q_blocks=blocks, kv_blocks=blocks)
+    _check_head("dq", dq[0, 0], rq, rows)
+    _check_head("dk", dk[0, 0], rk, rows)
+    _check_head("dv", dv[0, 0], rv, rows)
+
+
 def test_backward_deterministic(gpu_lib):
     q, k, v, do, m = _random_case(1, 2, 1024, 128, 1000, seed=11)
     a = _run(gpu_lib, q, k, v, do, m, 1000)

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from synth import get_config, make_inputs, quantize_fp8_blocks
-from parity_util import (MAX_ERR, MEAN_ERR, attention_errors, compare_masks, f64, oracle_attention_blocks,
+from parity_util import (MAX_ERR, MEAN_ERR, NEAR, attention_errors, compare_masks, f64, oracle_attention_blocks,
                          oracle_masks, sample_blocks)
 
 pytestmark = pytest.mark.gpu
@@ -185,41 +185,46 @@ def test_attention_config2_full(gpu_lib):
     _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
 
 
-def test_attention_config3_sampled(gpu_lib):
-    cfg = get_config(3)
-    q, k, v = make_inputs(cfg, seed=0, device=DEV)
-    heads = [0, 17, 39]
-    qs, ks = q[:, heads], k[:, heads]
-    keep_s, _ = oracle_masks(qs, ks, 0.2)
-    keep = np.zeros((1, cfg.H, cfg.nb, cfg.nb), dtype=bool)
-    keep[:, :, np.arange(cfg.nb), np.arange(cfg.nb)] = True       # other heads: diagonal only
-    keep[:, heads] = keep_s
-    blocks = [(0, h, i) for (_, h, i) in sample_blocks(keep[:, heads], 10, seed=1)]
-    blocks = [(0, heads[h], i) for (_, h, i) in blocks]
-    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
+# The benchmarked workloads at full size (every head with its real mask, the bench's
+# call path) are in test_gpu_workloads.py.
 
 
-def test_attention_config4_sta_sampled(gpu_lib):
-    cfg = get_config(4, heads=6)
-    q, k, v = make_inputs(cfg, seed=0, device=DEV)
-    plane = _sta_plane(cfg)
-    keep = np.broadcast_to(plane, (1, cfg.H, cfg.nb, cfg.nb)).copy()
-    blocks = sample_blocks(keep, 6, seed=2)
-    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
-
-
-def test_attention_config5_fp8_sampled(gpu_lib):
-    cfg = get_config(5, heads=3)
-    q, k, v = make_inputs(cfg, seed=0, device=DEV)
-    keep, _ = oracle_masks(q, k, 0.2, or_plane=_sta_plane(cfg))
-    blocks = sample_blocks(keep, 8, seed=3)
-    _attn_check(gpu_lib, cfg, q, k, v, keep, blocks)
-    q8, qs = quantize_fp8_blocks(q)
-    k8, ks = quantize_fp8_blocks(k)
-    deq = lambda c, s: (c.view(torch.float8_e4m3fn).to(torch.float64).reshape(*s.shape, 64, -1)
-                        * s.to(torch.float64)[..., None, None]).reshape(c.shape).cpu().numpy()
-    _attn_check(gpu_lib, cfg, q8, k8, v, keep, blocks, q_scale=qs, k_scale=ks, q_deq=deq(q8, qs),
-                k_deq=deq(k8, ks))
+@pytest.mark.parametrize("mode,D,nb", [("fp8", 64, 2736), ("bf16", 64, 4100), ("bf16", 128, 8200)])
+def test_attention_order_tables_past_shared_memory(gpu_lib, mode, D, nb):
+    """One head with more key blocks than the in-kernel longest-first order can tabulate in
+    the kernel's shared buffer (nb + 1 + ceil(nb/2) + 3 ints: past 4096 ints for fp8 D=64,
+    6144 for bf16 D=64, 12288 for bf16 D=128): the workgroups keep the natural order, and
+    every query block is still written (NaN-initialised output, every valid row finite);
+    sampled blocks match the oracle."""
+    B, H, S = 1, 1, nb * 64
+    sv = S - 40
+    g = torch.Generator(device="cpu").manual_seed(nb)
+    q, k, v = (torch.randn(B, H, S, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    rng = np.random.default_rng(nb)
+    keep = np.zeros((B, H, nb, nb), bool)
+    keep[0, 0, np.arange(nb), np.arange(nb)] = True
+    keep[0, 0, np.arange(nb)[:, None], rng.integers(0, nb, size=(nb, 6))] = True
+    mask = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+    qs = ks = None
+    qa, ka = q, k
+    if mode == "fp8":
+        qa, qs = gpu_lib.quantize_fp8_blocks(q)
+        ka, ks = gpu_lib.quantize_fp8_blocks(k)
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    print(f"[order tables] {mode} D {D} nb {nb}: slots {gpu_lib.attn_work_order_slots(q, sv)}", flush=True)
+    out = torch.full_like(v, float("nan"))
+    gpu_lib.block_sparse_attn_fwd_csr(qa, ka, v, rp, ci, s_valid=sv, q_scale=qs, k_scale=ks, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:, :, :sv]).all()
+    blocks = [(0, 0, i) for i in (0, 1, nb // 3, nb // 2, nb - 2, nb - 1)]
+    kw = {}
+    if mode == "fp8":
+        deq = lambda c, s: (c[0, 0].view(torch.float8_e4m3fn).double().view(nb, 64, D)
+                            * s[0, 0].double()[:, None, None]).view(S, D).cpu().numpy()
+        kw = dict(q_deq=lambda b, h: deq(qa, qs), k_deq=lambda b, h: deq(ka, ks))
+    mx, mean = attention_errors(out, oracle_attention_blocks(q, k, v, keep, blocks, sv, **kw))
+    print(f"  max err {mx:.3e} mean err {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
 
 
 def test_attention_edge_rows(gpu_lib):
@@ -658,3 +663,67 @@ def test_attention_head_order_writes_every_block(gpu_lib):
     mx, mean = attention_errors(out, ref)
     print(f"[head order] max err {mx:.3e}, mean err {mean:.3e}", flush=True)
     assert mx <= MAX_ERR and mean <= MEAN_ERR
+
+
+# ----------------------------------------------------------------------------- near-threshold flags
+def _check_near(flags, E, thr, name):
+    """GPU flags against the oracle's band |E - (1 - thr)| <= 1e-6, except entries whose
+    distance from the threshold lies within 1e-9 of the band edge (fixed-point vs fp64 E)."""
+    f = flags.cpu().numpy().astype(bool)
+    d = np.abs(E - (1.0 - thr))
+    ref = d <= NEAR
+    edge = np.abs(d - NEAR) <= 1e-9
+    bad = (f != ref) & ~edge
+    print(f"[near] {name}: flagged {int(f.sum())}, oracle {int(ref.sum())}, mismatches {int(bad.sum())}, "
+          f"edge entries {int(edge.sum())}", flush=True)
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("nb", [37, 300])
+def test_near_threshold_flags_equal_rows(gpu_lib, nb):
+    """q = 0: every row is uniform (p = 1/nb), so E = rank / nb exactly known. thr puts
+    1 - thr at 4e-7 from the E of rank 11 (flagged) and 3e-6 from that of rank 20 (not
+    flagged); nb = 37 runs the short-row select, nb = 300 the wide one."""
+    B, H, D = 1, 2, 128
+    q = torch.zeros(B, H, nb * 64, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(B, H, nb * 64, D, device=DEV).to(torch.bfloat16)
+    for thr in (1 - (11 / nb + 4e-7), 1 - (20 / nb - 3e-6), 0.0, 0.5):
+        m, nf = gpu_lib.nabla_build_mask(q, k, thr, near=True)
+        m0 = gpu_lib.nabla_build_mask(q, k, thr)
+        torch.cuda.synchronize()
+        assert torch.equal(m, m0)
+        keep, E = oracle_masks(q, k, thr)
+        assert compare_masks(m, keep, E, thr)[0] == 0
+        _check_near(nf, E, thr, f"uniform nb {nb} thr {thr:.9f}")
+        if thr == 1 - (11 / nb + 4e-7):
+            assert int(nf.sum()) == B * H * nb     # rank 11 of every row
+
+
+@pytest.mark.parametrize("cid,heads", [(2, 4), (3, 4)])
+def test_near_threshold_flags_random(gpu_lib, cid, heads):
+    """Seeded workload inputs; thr = 0 flags the tail of each row (entries after the first
+    1 - 1e-6 of the mass), thr 0.2 / the config's threshold flags few or none; the mask is
+    the same with and without the flags; the sliding-tile and list entry points give the
+    same flags (they describe the adaptive rule only)."""
+    cfg = get_config(cid, heads)
+    q, k, _ = make_inputs(cfg, seed=2, device=DEV)
+    for thr in (0.0, 0.2) + tuple(cfg.thrs):
+        m, nf = gpu_lib.nabla_build_mask(q, k, thr, near=True)
+        torch.cuda.synchronize()
+        keep, E = oracle_masks(q, k, thr)
+        assert compare_masks(m, keep, E, thr)[0] == 0
+        assert torch.equal(m, gpu_lib.nabla_build_mask(q, k, thr))
+        _check_near(nf, E, thr, f"{cfg.name} thr {thr}")
+        if cfg.sta is not None:
+            ms, nfs = gpu_lib.nabla_build_mask_sta(q, k, thr, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                                                   order_tile=cfg.order_tile, s_valid=cfg.S_valid, near=True)
+            torch.cuda.synchronize()
+            assert torch.equal(nfs, nf)
+        if cfg.nb <= 256:
+            nfl = torch.empty_like(nf)
+            gpu_lib.nabla_build_mask_lists(q, k, thr, s_valid=cfg.S_valid, near=nfl)
+            torch.cuda.synchronize()
+            assert torch.equal(nfl, nf)
+    _, nf8, _, _ = gpu_lib.nabla_build_mask_fp8(q, k, 0.0, near=True)
+    torch.cuda.synchronize()
+    assert torch.equal(nf8, gpu_lib.nabla_build_mask(q, k, 0.0, near=True)[1])

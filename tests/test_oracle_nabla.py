@@ -108,12 +108,14 @@ def _golden_geometric():
     return rows
 
 
+@pytest.mark.parametrize("scale", [1.0 / 8.0, None], ids=["explicit", "default"])
 @pytest.mark.parametrize("nb,thr,k_star", _golden_geometric())
-def test_geometric_rows_closed_form(nb, thr, k_star):
+def test_geometric_rows_closed_form(nb, thr, k_star, scale):
+    # scale None: the default temperature 1/sqrt(D) (D = 64 -> 1/8) must give the same rows
     rng = np.random.default_rng(nb)
     perm = rng.permutation(nb)
     q, k = _geometric_inputs(nb, perm)
-    keep, E, P = oracle.nabla_mask(q, k, 64, thr, scale=1.0 / 8.0)
+    keep, E, P = oracle.nabla_mask(q, k, 64, thr, scale=scale)
     rho = np.exp(-1.0 / 16.0)
     expect_p = rho ** np.arange(nb) * (1 - rho) / (1 - rho ** nb)
     assert np.max(np.abs(P[0, perm] - expect_p)) < 1e-13
@@ -202,6 +204,19 @@ def test_topk_brute_force_and_count():
                     for j2 in range(j + 1, nb):
                         if P[r, j] == P[r, j2]:
                             assert not (keep[r, j2] and not keep[r, j])
+
+
+@pytest.mark.parametrize("nb,thr,k_star", _golden_geometric()[:3])
+def test_topk_default_temperature_on_geometric_rows(nb, thr, k_star):
+    # the default temperature of topk_mask (1/sqrt(D), D = 64) on the geometric rows: the k*
+    # largest entries are the blocks of rank 0 .. k*-1, wherever the permutation put them
+    perm = np.random.default_rng(nb + 1).permutation(nb)
+    q, k = _geometric_inputs(nb, perm)
+    keep, P = oracle.topk_mask(q, k, 64, k_star)
+    rho = np.exp(-1.0 / 16.0)
+    assert np.max(np.abs(P[0, perm] - rho ** np.arange(nb) * (1 - rho) / (1 - rho ** nb))) < 1e-13
+    for i in range(nb):
+        assert set(np.nonzero(keep[i])[0]) == set(perm[:k_star])
 
 
 def test_topk_equals_cdf_mask_at_the_cdf_count():
