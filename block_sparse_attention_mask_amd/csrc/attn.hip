@@ -338,8 +338,11 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
 #pragma unroll
           for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
       }
+      // The normaliser sums the probabilities as rounded to bf16 for the PV product, so
+      // that O is an exact convex combination of those weights: the rounding then moves
+      // O by 2^-9 sum_k w_k |V_k - O| at most, instead of 2^-9 |O|.
       const float mr = m_run;
-      float ls = 0.f;
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         i32x4_t w;
@@ -348,12 +351,14 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
           const int v = 8 * (sp & 1) + 2 * e;
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][v], c, -mr));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[sp >> 1][v + 1], c, -mr));
-          ls += p0 + p1;
-          w[e] = (int)pk_bf16(p0, p1);
+          const unsigned pk = pk_bf16(p0, p1);
+          w[e] = (int)pk;
+          if (e & 1) ls1 = add_bf16_pair(pk, ls1);
+          else ls0 = add_bf16_pair(pk, ls0);
         }
         pop[sp] = __builtin_bit_cast(bf16x8_t, w);
       }
-      l_run += ls;
+      l_run += ls0 + ls1;
     }
     if (j1 >= 0) wait_vm<NK_W>(); else wait_vm<0>();    // own share of V(u) landed
     wg_barrier();                                        // everybody's share

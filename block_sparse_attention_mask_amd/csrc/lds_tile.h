@@ -113,6 +113,12 @@ __device__ __forceinline__ unsigned pk_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// acc + (the two bf16 halves of w), in fp32 (v_dot2c_f32_bf16 against (1, 1))
+__device__ __forceinline__ float add_bf16_pair(unsigned w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, acc,
+                                         false);
+}
+
 // Scheduling order for a run of NM MFMAs that each consume NR LDS reads: the reads of
 // the first P MFMAs, then each MFMA followed by the reads of the MFMA P places later.
 // Without it the compiler, short of registers, issues each operand read right before

@@ -248,7 +248,10 @@ def test_attention_edge_rows(gpu_lib):
             O, L = oracle.block_sparse_attention(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), keep[0, h], 64, Sv)
             assert np.abs(f64(out[0, h]) - O).max() <= MAX_ERR
             fin = np.isfinite(L)
-            assert np.abs(f64(lse[0, h])[fin] - L[fin]).max() < 1e-3
+            # lse is the log of the normaliser the kernel divides by: the sum of the weights
+            # as rounded to bf16 for the PV product, each within 2^-9 (relative) of exact,
+            # so |lse - exact| <= -log(1 - 2^-9) ~ 1.96e-3 (plus fp32 noise)
+            assert np.abs(f64(lse[0, h])[fin] - L[fin]).max() < 2.5e-3
 
 
 def test_attention_determinism_and_csr_entry(gpu_lib):

@@ -30,7 +30,7 @@ def _sta_plane(cfg):
 
 def _attention_as_benchmarked(bsa, cfg, qa, ka, v, keep, q_scale=None, k_scale=None):
     """The benchmark's attention call on the given mask; returns the output (NaN-initialised)."""
-    mask = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+    mask = torch.from_numpy(np.ascontiguousarray(keep, dtype=np.uint8)).to(DEV)
     rp, ci = bsa.mask_to_csr(mask)
     out = torch.full(v.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
     bsa.block_sparse_attn_fwd_csr(qa, ka, v, rp, ci, s_valid=cfg.S_valid, q_scale=q_scale, k_scale=k_scale, out=out)
