@@ -21,7 +21,8 @@ BSA_F32, BSA_BF16, BSA_FP8_E4M3FN = 0, 1, 2
 _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPACE", 4: "BSA_EHIP"}
 
 # every function the C header declares, in declaration order
-EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_topk", "quantize_fp8_blocks",
+EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_noalloc", "nabla_build_mask_topk",
+           "quantize_fp8_blocks",
            "nabla_build_mask_fp8",
            "sta_workspace_size", "sta_build_mask", "nabla_sta_workspace_size", "nabla_build_mask_sta",
            "nabla_lists_workspace_size", "nabla_build_mask_lists", "mask_or",
@@ -68,6 +69,7 @@ def load(path: Optional[str] = None):
     sig = {
         "nabla_workspace_size": (sz, [PS]),
         "nabla_build_mask": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, vp, sz, vp]),
+        "nabla_build_mask_noalloc": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, vp]),
         "nabla_build_mask_topk": (i32, [PT, PT, PS, i32, dbl, vp, i64, i64, vp, vp, sz, vp]),
         "quantize_fp8_blocks": (i32, [PT, PS, PT, vp, vp]),
         "nabla_build_mask_fp8": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, PT, vp, PT, vp, vp, sz, vp]),
@@ -184,6 +186,29 @@ def nabla_build_mask(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Option
                                 float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(),
                                 nf.data_ptr() if nf is not None else None, ws.data_ptr(), ws.numel(),
                                 _stream(q.device)))
+    return (out, nf) if nf is not None else out
+
+
+def nabla_build_mask_noalloc(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Optional[float] = None,
+                             or_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                             near=False):
+    """nabla_build_mask with the library's static scratch as workspace (no device allocation
+    inside the call; pass `out` (and a `near` tensor) to allocate nothing here either).
+    Calls on one GPU must not overlap in time."""
+    lib = load()
+    B, H, S, D = q.shape
+    nb = S // 64
+    shp = _shape(q, None)
+    if out is None:
+        out = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device)
+    nf = _near_buffer(q, near)
+    om, osb, osh = None, 0, 0
+    if or_mask is not None:
+        om, osb, osh, _keep = _mask_strides(or_mask)
+    tq, tk = _tensor(q), _tensor(k)
+    _check(lib.nabla_build_mask_noalloc(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
+                                        float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(),
+                                        nf.data_ptr() if nf is not None else None, _stream(q.device)))
     return (out, nf) if nf is not None else out
 
 

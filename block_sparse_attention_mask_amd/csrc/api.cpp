@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "bsa.h"
@@ -155,6 +156,59 @@ bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_
   g_err.clear();
   return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, nullptr, ws, ws_bytes, stream, 0,
                       bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr, nullptr, nullptr, near_thr_out);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The workspace of nabla_build_mask_noalloc: a static device array, one copy per GPU
+// (held until the process ends). In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[BSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// device address of the current device's scratch (looked up on the first call per device)
+bsa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(BSA_EUNSUPPORTED, "device %d: at most %d devices", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255)) return fail(BSA_EHIP, "scratch has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+bsa_status nabla_build_mask_noalloc(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape, double thr,
+                                    double scale, const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                                    uint8_t* mask_out, uint8_t* near_thr_out, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  const size_t need = nabla_workspace_size(shape);
+  if (need > (size_t)BSA_NOALLOC_SCRATCH_BYTES)
+    return fail(BSA_EUNSUPPORTED, "nabla_build_mask_noalloc: this shape needs %zu bytes of scratch, more than the %zu "
+                "the library holds (split the heads over several calls, or use nabla_build_mask)",
+                need, (size_t)BSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != BSA_OK) return st;
+  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, nullptr, ws,
+                      (size_t)BSA_NOALLOC_SCRATCH_BYTES, stream, 0, bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr,
+                      nullptr, nullptr, near_thr_out);
 }
 
 static bsa_status check_fp8_out(const char* name, const bsa_tensor* c, const float* sc, const bsa_shape* shape) {

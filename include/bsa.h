@@ -114,6 +114,26 @@ bsa_status nabla_build_mask(const bsa_tensor* q, const bsa_tensor* k, const bsa_
                             void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * nabla_build_mask for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, results and errors as nabla_build_mask, without ws / ws_bytes. The
+ * workspace is a static device array of BSA_NOALLOC_SCRATCH_BYTES (128 MiB) inside the
+ * library, one per GPU the library runs on, held until the process ends; the call
+ * allocates and frees nothing. Shapes with nabla_workspace_size(shape) above that
+ * (2 B H ceil(S/1024)*16 D 8 bytes: the 40-head 14B 720p shape needs 97 MB) return
+ * BSA_EUNSUPPORTED before any launch. Every call on one GPU uses the same array, which
+ * keeps the last call's contents (nothing in it needs to start at zero): calls that
+ * overlap in time on one GPU race, so the caller must order them (one stream, or
+ * events between streams). The array's device address is looked up on the first call
+ * on each device.
+ * ------------------------------------------------------------------------- */
+#define BSA_NOALLOC_SCRATCH_BYTES (128u << 20)
+bsa_status nabla_build_mask_noalloc(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
+                                    double thr, double scale,
+                                    const uint8_t* or_mask, int64_t or_sb, int64_t or_sh,
+                                    uint8_t* mask_out, uint8_t* near_thr_out, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Top-k block selection [NABLA review, Appendix C / Theorem 1: the fixed-count
  * alternative that CDF thresholding is compared with at equal retained blocks].
  * The same reduced map and row softmax as nabla_build_mask; each row keeps its topk

@@ -225,3 +225,19 @@ def test_topk_rejects_bad_arguments(lib):
     st = lib.nabla_build_mask_topk(ctypes.byref(q), ctypes.byref(q), ctypes.byref(shape), 0, 0.0, None, 0, 0, 4096,
                                    8192, 1 << 40, None)
     assert st == 1 and "topk" in lib.bsa_last_error().decode()
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    # more scratch than the library's static array holds: rejected on the host, no HIP call
+    big = bsa.Shape(1, 100, 64 * 2048, 64 * 2048, 128, 64)
+    assert lib.nabla_workspace_size(ctypes.byref(big)) > (128 << 20)
+    q = _t()
+    st = lib.nabla_build_mask_noalloc(ctypes.byref(q), ctypes.byref(q), ctypes.byref(big), 0.2, 0.0, None, 0, 0,
+                                      4096, None, None)
+    assert st == 2 and "scratch" in lib.bsa_last_error().decode()
+    # the 40-head 14B 720p shape fits
+    cfg3 = bsa.Shape(1, 40, 75648, 75600, 128, 64)
+    assert lib.nabla_workspace_size(ctypes.byref(cfg3)) <= (128 << 20)
+    bad = bsa.Shape(1, 2, 250, 250, 128, 64)
+    assert lib.nabla_build_mask_noalloc(ctypes.byref(q), ctypes.byref(q), ctypes.byref(bad), 0.2, 0.0, None, 0, 0,
+                                        4096, None, None) == 1
