@@ -567,9 +567,207 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int L) {
   return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
+// Radix digits of the wave-per-row selection, with NBK = 64 << SUB buckets per pass (SUB
+// = 2: 256 buckets, 8-bit digits, the scheme of select_kernel). The first pass is
+// logarithmic: w < 4 gets bucket w; otherwise, with e the position of the leading one,
+// bucket 4 + (e - 2) 2^SUB + (the SUB bits below the leading one), i.e. the range
+// [(2^SUB + m) << (e - SUB), (2^SUB + m + 1) << (e - SUB)). Later passes split the current
+// range [lo, lo + 2^span) by its top DB = 6 + SUB bits. -1: w is outside the range.
+template <int SUB>
+__device__ __forceinline__ int row_digit(uint64_t key, const SelRowState& st) {
+  constexpr int DB = 6 + SUB;
+  if (st.span < 0) {
+    if (key < 4) return (int)key;
+    const int e = 63 - __builtin_clzll(key);
+    return 4 + ((e - 2) << SUB) + (int)((key >> (e - SUB)) & ((1u << SUB) - 1));
+  }
+  if (key < st.lo || key - st.lo >= (1ull << st.span)) return -1;
+  const int db = st.span < DB ? st.span : DB;
+  return (int)((key - st.lo) >> (st.span - db));
+}
+
+// The selection of one row by one wave: the row's reduced-map values (scaled) are in
+// shared memory at mrow[0 .. nb); lane l holds columns j = 64 e + l. Softmax in fp64, the
+// fixed-point keys w = floor(p 2^60), a radix select of the pivot for each target with the
+// wave's own histograms hm, hc (NBK buckets; the shared-memory operations of one wave are
+// processed in program order, so a clear, the atomic updates and the reads that follow
+// need no wait between them), ties ranked by ascending index with ballots; then the mask
+// row (OR'd with or_row and the sliding-tile rule), the optional near-threshold flags and
+// the optional kv list. Every value is wave-uniform except the per-lane entries.
+template <int E, int SUB, bool NEAR>
+__device__ __forceinline__ void select_row(const double* mrow, int nb, int row, int64_t grow,
+                                           uint64_t T_fixed, int topk, const uint8_t* or_row, const StaRule& sta,
+                                           uint8_t* __restrict__ mask_out,
+                                           const SelLists& lists, const SelNear& nr, uint64_t* hm, uint32_t* hc) {
+  constexpr int NBK = 64 << SUB, BPL = NBK / 64, DB = 6 + SUB;
+  constexpr int NTG = NEAR ? 3 : 1;                 // targets: the rule; with NEAR also T_lo, T_hi
+  const int l = threadIdx.x & 63;
+  const bool by_count = topk > 0;
+  const StaCoord rc = sta.bpt ? sta_rule_coord(sta, row) : StaCoord{0, 0, 0};
+  // ---- softmax of the row in fp64, then the fixed-point mass w = floor(p 2^60) (the key)
+  bool valid[E];
+  double x[E];
+  double m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 64 * e + l;
+    valid[e] = j < nb;
+    x[e] = valid[e] ? mrow[j] : -INFINITY;
+    m = fmax(m, x[e]);
+  }
+  m = wave_max_f64(m);
+  double sum = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = valid[e] ? exp(x[e] - m) : 0.0;
+    sum += x[e];
+  }
+  const double inv = 1.0 / wave_sum_f64(sum);
+  uint64_t key[E];
+  uint64_t ms = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    key[e] = valid[e] ? fixed_mass(x[e] * inv) : 0;
+    ms += key[e];
+  }
+  const uint64_t total = wave_sum_u64(ms);
+
+  // ---- radix select of the pivot for each target (the row state is wave-uniform), then
+  // the target's decision for each of the lane's entries as bit e of kbits[t]; tied keys
+  // are ranked by ascending index
+  static_assert(E <= 32, "one bit per entry of a lane");
+  uint32_t kb_rule = 0, kb_lo = 0, kb_hi = 0;
+#pragma unroll 1
+  for (int t = 0; t < NTG; ++t) {
+    const uint64_t target = by_count ? (uint64_t)topk : (t == 0 ? T_fixed : t == 1 ? nr.t_lo : nr.t_hi);
+    SelRowState sr = sel_init(false, total, target, by_count, nb, topk);
+    for (int pass = 0; pass < 12 && sr.status == ROW_ACTIVE; ++pass) {
+#pragma unroll
+      for (int x4 = 0; x4 < BPL; ++x4) {
+        hm[BPL * l + x4] = 0;
+        hc[BPL * l + x4] = 0;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (!valid[e]) continue;
+        const int dg = row_digit<SUB>(key[e], sr);
+        if (dg >= 0) {
+          atomicAdd((unsigned long long*)&hm[dg], (unsigned long long)key[e]);
+          atomicAdd(&hc[dg], 1u);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // lane l owns buckets NBK-1-BPL l .. NBK-BPL(l+1) (descending keys)
+      uint64_t mb[BPL];
+      uint32_t cb[BPL];
+      uint64_t lt = 0;
+#pragma unroll
+      for (int x4 = 0; x4 < BPL; ++x4) {
+        cb[x4] = hc[NBK - 1 - BPL * l - x4];
+        mb[x4] = by_count ? (uint64_t)cb[x4] : hm[NBK - 1 - BPL * l - x4];   // what the target counts
+        lt += mb[x4];
+      }
+      const uint64_t incl = wave_incl_scan_u64(lt);
+      const uint64_t before = sr.mass_above + (incl - lt);
+      const uint64_t ball = __ballot(before + lt >= target);
+      const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
+      // the crossing bucket of lane L, found by every lane from lane L's values
+      uint64_t cum = readlane_u64(before, L);
+      int xs = BPL - 1, cnt = 0;
+#pragma unroll
+      for (int x4 = 0; x4 < BPL; ++x4) {
+        const uint64_t mbl = readlane_u64(mb[x4], L);
+        const int cbl = __builtin_amdgcn_readlane((int)cb[x4], L);
+        if (xs == BPL - 1 && x4 < BPL - 1) {
+          if (cum + mbl >= target) { xs = x4; cnt = cbl; }
+          else cum += mbl;
+        } else if (x4 == BPL - 1 && xs == BPL - 1) {
+          cnt = cbl;
+        }
+      }
+      const int dg = NBK - 1 - BPL * L - xs;
+      SelRowState n = sr;
+      n.mass_above = cum;
+      n.cnt = cnt;
+      if (sr.span < 0) {
+        if (dg < 4) {
+          n.lo = (uint64_t)dg;
+          n.span = 0;
+        } else {
+          const int e = ((dg - 4) >> SUB) + 2, mm = (dg - 4) & ((1 << SUB) - 1);
+          n.lo = (uint64_t)((1 << SUB) + mm) << (e - SUB);
+          n.span = e - SUB;
+        }
+      } else {
+        const int db = sr.span < DB ? sr.span : DB;
+        n.span = sr.span - db;
+        n.lo = sr.lo + ((uint64_t)dg << n.span);
+      }
+      if (n.cnt <= 1) n.status = ROW_PIVOT;
+      else if (n.span == 0) {
+        // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
+        const uint64_t wq = by_count ? 1 : n.lo;
+        const uint64_t need = target - n.mass_above;           // > 0
+        const uint64_t tk = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
+        n.tie_keep = (int)(tk < (uint64_t)n.cnt ? tk : (uint64_t)n.cnt);
+        n.status = ROW_TIE;
+      }
+      sr = n;
+    }
+    uint32_t bits = 0;
+    int tie_base = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool tied = sr.status == ROW_TIE && valid[e] && key[e] == sr.lo;
+      const uint64_t tb = __ballot(tied);
+      const int rank = tie_base + __popcll(tb & ((1ull << l) - 1ull));
+      tie_base += __popcll(tb);
+      if (valid[e] && sel_keep(sr, key[e], tied, rank)) bits |= 1u << e;
+    }
+    if (t == 0) kb_rule = bits;
+    else if (t == 1) kb_lo = bits;
+    else kb_hi = bits;
+  }
+
+  // ---- write the row (OR'd with the optional mask and the sliding-tile rule); with lists,
+  // the kept blocks also go to the row's kv list in ascending order; with NEAR the flags
+  // of the band [T_lo, T_hi) (never OR'd)
+  uint8_t* dst = mask_out + grow * nb;
+  uint8_t* ndst = NEAR ? nr.flags + grow * nb : nullptr;
+  int32_t* lst = lists.kv_idx ? lists.kv_idx + grow * nb : nullptr;
+  const uint32_t nbits = kb_hi & ~kb_lo;
+  int nkept = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 64 * e + l;
+    bool keep = (kb_rule >> e) & 1u;
+    if (valid[e]) {
+      if ((or_row && or_row[j]) || (sta.bpt && sta_rule_near(sta, rc, sta_rule_coord(sta, j)))) keep = true;
+      dst[j] = keep ? 1 : 0;
+      if constexpr (NEAR) ndst[j] = (nbits >> e) & 1u;
+    }
+    if (lst) {
+      const uint64_t kb = __ballot(keep);
+      if (keep) lst[nkept + __popcll(kb & ((1ull << l) - 1ull))] = j;
+      nkept += __popcll(kb);
+    }
+  }
+  if (lists.kv_len && l == 0) lists.kv_len[grow] = nkept;
+}
+
+// ----------------------------------------------------------------------------
+// Row selection for short rows (nb <= 256). The same reduced map, fixed-point keys,
+// radix digits and tie rule as select_kernel; once the map is formed it is written to
+// shared memory, and each wave then owns whole rows (select_row): softmax, radix select,
+// tie ranking and the row's write use wave reductions, ballots and wave-uniform state
+// only, with no workgroup barrier. Optionally the kept blocks of each row also go to a
+// fixed-stride kv list (the compaction the attention kernel consumes, without a pass of
+// its own over the mask).
 // Each 16-row strip of the map is formed by SELR_SPLIT workgroups (the same small fp64
 // product, recomputed), each taking SEL_ROWS / SELR_SPLIT of its rows: more workgroups
 // and fewer rows one after the other in a wave.
+// ----------------------------------------------------------------------------
 constexpr int SELR_SPLIT = 2;
 template <int NCT, int KS, bool NEAR>   // NCT = column tiles per wave (nb <= 128 NCT)
 __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const double* __restrict__ qmf,
@@ -581,8 +779,6 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
                                                                     SelLists lists, SelNear nr) {
   constexpr int E = 2 * NCT;                        // entries per lane per row
   constexpr int NBP = SEL_WAVES * 16 * NCT;         // map row length
-  constexpr int NTG = NEAR ? 3 : 1;                 // targets: the rule; with NEAR also T_lo, T_hi
-  const bool by_count = topk > 0;
   __shared__ double qa_lds[32 * 64];
   __shared__ double map[SEL_ROWS][NBP];
   __shared__ uint64_t hmass[SEL_WAVES][256];
@@ -605,155 +801,13 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void select_rows_kernel(const doubl
   __syncthreads();
 
   const int b = bh / H, h = bh % H;
-  StaCoord cc[E];   // the sliding-tile rule's tile coordinates of this lane's columns
-#pragma unroll
-  for (int e = 0; e < E; ++e) cc[e] = sta.bpt ? sta_rule_coord(sta, min(64 * e + l, nb - 1)) : StaCoord{0, 0, 0};
   constexpr int RPW = SEL_ROWS / SEL_WAVES / SELR_SPLIT;   // rows per wave
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = part * (SEL_ROWS / SELR_SPLIT) + RPW * w + rr, row = row0 + r;
     if (row >= nb) break;                            // wave-uniform
-    const StaCoord rc = sta.bpt ? sta_rule_coord(sta, row) : StaCoord{0, 0, 0};
-    // ---- softmax of the row in fp64, then the fixed-point mass w = floor(p 2^60) (the key)
-    bool valid[E];
-    double x[E];
-    double m = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = 64 * e + l;
-      valid[e] = j < nb;
-      x[e] = valid[e] ? map[r][j] : -INFINITY;
-      m = fmax(m, x[e]);
-    }
-    m = wave_max_f64(m);
-    double sum = 0.0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      x[e] = valid[e] ? exp(x[e] - m) : 0.0;
-      sum += x[e];
-    }
-    const double inv = 1.0 / wave_sum_f64(sum);
-    uint64_t key[E];
-    uint64_t ms = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      key[e] = valid[e] ? fixed_mass(x[e] * inv) : 0;
-      ms += key[e];
-    }
-    const uint64_t total = wave_sum_u64(ms);
-
-    // ---- radix select of the pivot for each target; the row state is wave-uniform
-    SelRowState srs[NTG];
-#pragma unroll
-    for (int t = 0; t < NTG; ++t) {
-      const uint64_t target = by_count ? (uint64_t)topk : (t == 0 ? T_fixed : t == 1 ? nr.t_lo : nr.t_hi);
-      SelRowState sr = sel_init(false, total, target, by_count, nb, topk);
-      for (int pass = 0; pass < 9 && sr.status == ROW_ACTIVE; ++pass) {
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-          hmass[w][4 * l + x4] = 0;
-          hcnt[w][4 * l + x4] = 0;
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (!valid[e]) continue;
-          const int dg = sel_digit(key[e], sr);
-          if (dg >= 0) {
-            atomicAdd((unsigned long long*)&hmass[w][dg], (unsigned long long)key[e]);
-            atomicAdd(&hcnt[w][dg], 1u);
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-        // lane l owns buckets 255-4l .. 252-4l (descending keys)
-        uint64_t mb[4];
-        uint32_t cb[4];
-        uint64_t lt = 0;
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-          cb[x4] = hcnt[w][255 - 4 * l - x4];
-          mb[x4] = by_count ? (uint64_t)cb[x4] : hmass[w][255 - 4 * l - x4];   // what the target counts
-          lt += mb[x4];
-        }
-        const uint64_t incl = wave_incl_scan_u64(lt);
-        const uint64_t before = sr.mass_above + (incl - lt);
-        const uint64_t ball = __ballot(before + lt >= target);
-        const int L = ball ? __builtin_ctzll(ball) : 63;   // the invariant guarantees ball != 0
-        // the crossing bucket of lane L, found by every lane from lane L's values
-        uint64_t cum = readlane_u64(before, L);
-        int xs = 3, cnt = 0;
-#pragma unroll
-        for (int x4 = 0; x4 < 4; ++x4) {
-          const uint64_t mbl = readlane_u64(mb[x4], L);
-          const int cbl = __builtin_amdgcn_readlane((int)cb[x4], L);
-          if (xs == 3 && x4 < 3) {
-            if (cum + mbl >= target) { xs = x4; cnt = cbl; }
-            else cum += mbl;
-          } else if (x4 == 3 && xs == 3) {
-            cnt = cbl;
-          }
-        }
-        const int dg = 255 - 4 * L - xs;
-        SelRowState n = sr;
-        n.mass_above = cum;
-        n.cnt = cnt;
-        if (sr.span < 0) {
-          first_range(dg, n.lo, n.span);
-        } else {
-          const int db = sr.span < 8 ? sr.span : 8;
-          n.span = sr.span - db;
-          n.lo = sr.lo + ((uint64_t)dg << n.span);
-        }
-        if (n.cnt <= 1) n.status = ROW_PIVOT;
-        else if (n.span == 0) {
-          // identical keys: visited by ascending index, each adds the same mass (Top-k: one)
-          const uint64_t wq = by_count ? 1 : n.lo;
-          const uint64_t need = target - n.mass_above;           // > 0
-          const uint64_t tk = wq ? (need + wq - 1) / wq : (uint64_t)n.cnt;
-          n.tie_keep = (int)(tk < (uint64_t)n.cnt ? tk : (uint64_t)n.cnt);
-          n.status = ROW_TIE;
-        }
-        sr = n;
-      }
-      srs[t] = sr;
-    }
-
-    // ---- write the row (OR'd with the optional mask); tied keys ranked by ascending
-    // index; with lists, the kept blocks also go to the row's kv list in ascending order;
-    // with NEAR the flags of the band [T_lo, T_hi) (never OR'd)
-    const int64_t grow = (int64_t)bh * nb + row;
-    uint8_t* dst = mask_out + grow * nb;
-    uint8_t* ndst = NEAR ? nr.flags + grow * nb : nullptr;
     const uint8_t* om = or_mask ? or_mask + b * or_sb + h * or_sh + (int64_t)row * nb : nullptr;
-    int32_t* lst = lists.kv_idx ? lists.kv_idx + grow * nb : nullptr;
-    int tie_base[NTG];
-#pragma unroll
-    for (int t = 0; t < NTG; ++t) tie_base[t] = 0;
-    int nkept = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = 64 * e + l;
-      bool kt[NTG];
-#pragma unroll
-      for (int t = 0; t < NTG; ++t) {
-        const bool tied = srs[t].status == ROW_TIE && valid[e] && key[e] == srs[t].lo;
-        const uint64_t tb = __ballot(tied);
-        const int rank = tie_base[t] + __popcll(tb & ((1ull << l) - 1ull));
-        tie_base[t] += __popcll(tb);
-        kt[t] = valid[e] && sel_keep(srs[t], key[e], tied, rank);
-      }
-      bool keep = kt[0];
-      if (valid[e]) {
-        if ((om && om[j]) || (sta.bpt && sta_rule_near(sta, rc, cc[e]))) keep = true;
-        dst[j] = keep ? 1 : 0;
-        if constexpr (NEAR) ndst[j] = kt[2] && !kt[1] ? 1 : 0;
-      }
-      if (lst) {
-        const uint64_t kb = __ballot(keep);
-        if (keep) lst[nkept + __popcll(kb & ((1ull << l) - 1ull))] = j;
-        nkept += __popcll(kb);
-      }
-    }
-    if (lists.kv_len && l == 0) lists.kv_len[grow] = nkept;
+    select_row<E, 2, NEAR>(&map[r][0], nb, row, (int64_t)bh * nb + row, T_fixed, topk, om, sta, mask_out, lists, nr,
+                           &hmass[w][0], &hcnt[w][0]);
   }
 }
 
@@ -843,10 +897,10 @@ static hipError_t launch_select_n(const double* qmf, const double* kmf, int B, i
   case n:                                                                                                      \
     return launch_select_c<n, NEAR>(qmf, kmf, B, H, nb, D, scale, T_fixed, topk, or_mask, or_sb, or_sh, sta, \
                                     mask_out, st, nr);
-  switch (nct) {
-    BSA_SEL_CASE(1) BSA_SEL_CASE(2) BSA_SEL_CASE(3) BSA_SEL_CASE(4) BSA_SEL_CASE(5) BSA_SEL_CASE(6)
-    BSA_SEL_CASE(7) BSA_SEL_CASE(8) BSA_SEL_CASE(9) BSA_SEL_CASE(10) BSA_SEL_CASE(11) BSA_SEL_CASE(12)
-    BSA_SEL_CASE(13) BSA_SEL_CASE(14) BSA_SEL_CASE(15) BSA_SEL_CASE(16)
+  switch (nct) {   // nb > SELR_MAX_NB: 17 .. 128 column tiles
+    BSA_SEL_CASE(3) BSA_SEL_CASE(4) BSA_SEL_CASE(5) BSA_SEL_CASE(6) BSA_SEL_CASE(7) BSA_SEL_CASE(8)
+    BSA_SEL_CASE(9) BSA_SEL_CASE(10) BSA_SEL_CASE(11) BSA_SEL_CASE(12) BSA_SEL_CASE(13) BSA_SEL_CASE(14)
+    BSA_SEL_CASE(15) BSA_SEL_CASE(16)
     default: return hipErrorInvalidValue;
   }
 #undef BSA_SEL_CASE

@@ -730,3 +730,36 @@ def test_near_threshold_flags_random(gpu_lib, cid, heads):
     _, nf8, _, _ = gpu_lib.nabla_build_mask_fp8(q, k, 0.0, near=True)
     torch.cuda.synchronize()
     assert torch.equal(nf8, gpu_lib.nabla_build_mask(q, k, 0.0, near=True)[1])
+
+
+@pytest.mark.parametrize("nb", [257, 700, 1216, 1217])
+def test_long_row_select_bounds(gpu_lib, nb):
+    """Rows past the short-row limit: nb 257 .. 1216 take the select that keeps the 16-row map
+    strip in shared memory (one wave per row, 6-bit digits), nb 1217 the register-resident
+    one. Thresholds (0 keeps every block with mass), Top-k and an OR'd plane; D 128 and 64."""
+    from dataclasses import replace
+    for D in (128, 64):
+        cfg = replace(get_config(3, heads=2), cid=9, name=f"long-{nb}", grid=(1, nb, 64), D=D)
+        assert cfg.nb == nb and cfg.S_valid == cfg.S
+        q, k, _ = make_inputs(cfg, seed=nb + D, device=DEV)
+        rng = np.random.default_rng(nb)
+        plane = rng.random((nb, nb)) < 0.03
+        plane_t = torch.from_numpy(plane.astype(np.uint8)).to(DEV)
+        for thr in (0.0, 0.1, 0.2, 0.6):
+            m = gpu_lib.nabla_build_mask(q, k, thr)
+            mo = gpu_lib.nabla_build_mask(q, k, thr, or_mask=plane_t)
+            torch.cuda.synchronize()
+            keep, E = oracle_masks(q, k, thr)
+            bad, near = compare_masks(m, keep, E, thr)
+            print(f"[long] nb {nb} D {D} thr {thr}: mismatches {bad}, near {near}, kept {keep.mean():.4f}", flush=True)
+            assert bad == 0
+            keep_or, _ = oracle_masks(q, k, thr, or_plane=plane)
+            assert compare_masks(mo, keep_or, E, thr)[0] == 0
+        for topk in (1, 37, nb - 1):
+            mt = gpu_lib.nabla_build_mask_topk(q, k, topk)
+            torch.cuda.synchronize()
+            for h in range(cfg.H):
+                ref, P = oracle.topk_mask(f64(q[0, h]), f64(k[0, h]), 64, topk)
+                diff = mt[0, h].cpu().numpy().astype(bool) != ref
+                kth = -np.sort(-P, axis=1)[:, topk - 1]
+                assert not (diff & ~(np.abs(P - kth[:, None]) <= 2.0 ** -59)).any(), (topk, h)
