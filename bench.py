@@ -43,11 +43,12 @@ def _measured_traffic(workload, fp8=False, dense=False):
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["attn_fwd"]
         src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
+        entry = rec["workloads"][workload]
     except (OSError, KeyError, ValueError, TypeError):
         return None
-    if hashlib.sha256(src).hexdigest()[:16] != rec["sha256_prefix"] or fp8 or dense:
+    if hashlib.sha256(src).hexdigest()[:16] != entry["sha256_prefix"] or fp8 or dense:
         return None
-    return rec["traffic_bytes_per_launch"].get(workload)
+    return entry["traffic_bytes_per_launch"]
 
 
 def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_step=False, dense_reps=0):
