@@ -27,7 +27,7 @@ EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_noalloc
            "sta_workspace_size", "sta_build_mask", "nabla_sta_workspace_size", "nabla_build_mask_sta",
            "nabla_lists_workspace_size", "nabla_build_mask_lists", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "bsa_mask_to_csr_ordered", "attn_workspace_size",
-           "block_sparse_attn_fwd",
+           "block_sparse_attn_fwd", "bsa_set_attn_kv_chunk", "attn_pair_workspace_size", "attn_pair_offsets",
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "block_sparse_attn_fwd_lists",
            "attn_work_order_slots", "attn_work_order",
            "attn_bwd_workspace_size", "block_sparse_attn_bwd", "token_reorder", "bsa_last_error",
@@ -89,6 +89,9 @@ def load(path: Optional[str] = None):
         "attn_csr_workspace_size": (sz, [PS, i32]),
         "block_sparse_attn_fwd_csr": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
         "block_sparse_attn_fwd_lists": (i32, [PT, PT, PT, PS, vp, vp, vp, vp, vp, dbl, PT, vp, vp, sz, vp]),
+        "bsa_set_attn_kv_chunk": (i32, [i32]),
+        "attn_pair_workspace_size": (sz, [PS]),
+        "attn_pair_offsets": (i32, [PS, vp, vp, vp, vp, vp, sz, vp]),
         "attn_work_order_slots": (i32, [PS]),
         "attn_work_order": (i32, [PS, vp, vp, vp]),
         "attn_bwd_workspace_size": (sz, [PS]),
@@ -462,6 +465,27 @@ def block_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
     if return_lse:
         return plan.out, plan.lse
     return plan.out
+
+
+def set_attn_kv_chunk(kv_chunk: int) -> int:
+    """Chunk width (key blocks) of the attention's kv-chunked walk for the whole process:
+    > 0 that width for every shape, < 0 never chunk, 0 the automatic choice. Returns the
+    previous setting; workspaces sized before a change do not follow it."""
+    return int(load().bsa_set_attn_kv_chunk(int(kv_chunk)))
+
+
+def attn_pair_offsets(q: torch.Tensor, row_ptr: Optional[torch.Tensor], col_idx: torch.Tensor,
+                      kv_len: Optional[torch.Tensor] = None, s_valid: Optional[int] = None) -> torch.Tensor:
+    """Pairing offset of each head (int32 [B*H]) that the attention picks for these kv lists:
+    CSR (row_ptr, col_idx), or with row_ptr None the fixed-stride lists (kv_len, col_idx)."""
+    lib = load()
+    shp = _shape(q, s_valid)
+    out = torch.empty(q.shape[0] * q.shape[1], dtype=torch.int32, device=q.device)
+    ws = _ws(lib.attn_pair_workspace_size(ctypes.byref(shp)), q.device)
+    _check(lib.attn_pair_offsets(ctypes.byref(shp), row_ptr.data_ptr() if row_ptr is not None else None,
+                                 col_idx.data_ptr(), kv_len.data_ptr() if kv_len is not None else None,
+                                 out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return out
 
 
 def attn_work_order_slots(q: torch.Tensor, s_valid: Optional[int] = None) -> int:

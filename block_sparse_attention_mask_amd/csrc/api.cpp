@@ -2,6 +2,7 @@
 // Host-side only: argument validation, workspace carving and kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -81,7 +82,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 10; }
+int bsa_abi_version(void) { return 11; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -509,9 +510,32 @@ static int work_order_slots(const bsa_shape* s) {
 // order costs each workgroup a few microseconds, noise against items of ~2 ms).
 constexpr int HEAD_ORDER_MIN_NB = 512;
 
+// Width of the kv-chunked attention walk (0: rows walked whole), set by bsa_set_attn_kv_chunk.
+// Whole rows are the default: at the 14B shape the chunked walk cuts the attention kernel's
+// L2 misses twelvefold without changing its time, and its combine then adds ~12%.
+static std::atomic<int> g_kv_chunk{0};
+static int kv_chunk_of(const bsa_shape*) { return g_kv_chunk.load(); }
+
+int bsa_set_attn_kv_chunk(int kv_chunk) { return g_kv_chunk.exchange(kv_chunk > 0 ? kv_chunk : 0); }
+
+// Shapes run with each head's pairing offset (pairs of query blocks chosen for alike kv
+// lists) from this many key blocks on, when they have no work order: at the 14B shape the
+// offset one frame apart cuts the union steps by ~7%, at a cost of three small launches.
+constexpr int PAIR_OFFSET_MIN_NB = 512;
+static bool pairing_of(const bsa_shape* s) {
+  return s->S / 64 >= PAIR_OFFSET_MIN_NB && work_order_slots(s) == 0;
+}
+static size_t pairing_bytes(const bsa_shape* s) {
+  if (!pairing_of(s)) return 0;
+  const int64_t BH = (int64_t)s->B * s->H;
+  return align256((size_t)BH * 4) + bsa::pair_bits_ws(BH * (s->S / 64), s->S / 64);
+}
+
 size_t attn_csr_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
   if (!s || s->S <= 0 || s->D <= 0 || s->B < 1 || s->H < 1) return 0;
-  return qk_dtype == BSA_F32 ? 6 * split_bytes(s) : 0;   // hi/lo bf16 copies of f32 q, k, v
+  const size_t split = qk_dtype == BSA_F32 ? 6 * split_bytes(s) : 0;   // hi/lo bf16 copies of f32 q, k, v
+  return split + bsa::chunk_ws_bytes((int64_t)s->B * s->H * (s->S / 64), s->S / 64, s->D, kv_chunk_of(s)) +
+         pairing_bytes(s);
 }
 
 size_t attn_workspace_size(const bsa_shape* s, bsa_dtype qk_dtype) {
@@ -550,6 +574,20 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
     a.derive_order = 2;       // many rounds of long rows: longest first inside each head
   }
   void* split_ws = ws;
+  char* wnext = (char*)ws + (mode == bsa::ATTN_SPLIT_F32 ? 6 * split_bytes(shape) : 0);
+  if ((a.kv_chunk = kv_chunk_of(shape)) > 0) {
+    a.pair_order = nullptr;
+    a.derive_order = 0;
+    bsa::chunk_ws_carve(a, wnext);
+    wnext += bsa::chunk_ws_bytes((int64_t)a.B * a.H * a.nb, a.nb, a.D, a.kv_chunk);
+  }
+  if (pairing_of(shape)) {
+    int32_t* pair_d = (int32_t*)wnext;
+    uint64_t* bits = (uint64_t*)(wnext + align256((size_t)a.B * a.H * 4));
+    hipError_t e = bsa::launch_pair_offsets(row_ptr, col_idx, row_len, a.row_stride, a.B * a.H, a.nb, bits, pair_d, hs);
+    if (e != hipSuccess) return hip_status(e, "pairing offsets launch");
+    a.pair_d = pair_d;
+  }
   if (mode == bsa::ATTN_SPLIT_F32) {
     const size_t sb = split_bytes(shape);
     uint16_t* p[6];
@@ -612,6 +650,28 @@ bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const
   hipError_t e = bsa::launch_csr(mask, mask_sb, mask_sh, shape->B, shape->H, nb, row_ptr, col_idx, counts, hs);
   if (e != hipSuccess) return hip_status(e, "csr launch");
   return attn_common(q, k, v, shape, row_ptr, col_idx, nullptr, q_scale, k_scale, scale, o, lse, w, hs);
+}
+
+size_t attn_pair_workspace_size(const bsa_shape* s) {
+  if (!s || s->S <= 0 || s->B < 1 || s->H < 1) return 0;
+  const int64_t BH = (int64_t)s->B * s->H;
+  return bsa::pair_bits_ws(BH * (s->S / 64), s->S / 64);
+}
+
+bsa_status attn_pair_offsets(const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                             const int32_t* kv_len, int32_t* pair_d, void* ws, size_t ws_bytes, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape, false)) != BSA_OK) return st;
+  if (!col_idx || !pair_d || (!row_ptr && !kv_len)) return fail(BSA_EINVAL, "col_idx / pair_d / lists are NULL");
+  const int nb = shape->S / 64;
+  if ((int64_t)shape->B * shape->H * nb * nb >= (1ll << 31)) return fail(BSA_EUNSUPPORTED, "too many list entries");
+  const size_t need = attn_pair_workspace_size(shape);
+  if (!ws || ws_bytes < need) return fail(BSA_EWORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws & 255) return fail(BSA_EINVAL, "workspace must be 256-byte aligned");
+  return hip_status(bsa::launch_pair_offsets(row_ptr, col_idx, row_ptr ? nullptr : kv_len, nb, shape->B * shape->H, nb,
+                                             (uint64_t*)ws, pair_d, (hipStream_t)stream),
+                    "pairing offsets launch");
 }
 
 int attn_work_order_slots(const bsa_shape* shape) {

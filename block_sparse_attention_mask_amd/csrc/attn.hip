@@ -90,10 +90,22 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
   auto list_len = [&](int r) { return a.row_len ? a.row_len[r] : row_ptr[r + 1] - row_ptr[r]; };
-  int lin;
+  int lin, cidx = 0;
   // (the in-kernel orders keep their tables in smem; where they would not fit, the
   // workgroups keep the natural order of the same ranges)
-  if (a.pair_order) {
+  if (a.kv_chunk) {
+    // kv-chunked walk: items (head, chunk, pair) in per-XCD ranges of their natural order,
+    // so that the ~96 workgroups running on one XCD take the pairs of one chunk of one head
+    // and read the same few K/V tiles, which stay in that XCD's L2
+    const int per_bh = a.nch * npair;
+    const int64_t totc = (int64_t)a.B * a.H * per_bh;
+    const int64_t chunk = (totc + BSA_NXCD - 1) / BSA_NXCD;
+    const int64_t lc = (int64_t)(blockIdx.x % BSA_NXCD) * chunk + blockIdx.x / BSA_NXCD;
+    if (lc >= totc) return;
+    const int bh0 = (int)(lc / per_bh), rem = (int)(lc - (int64_t)bh0 * per_bh);
+    cidx = rem / npair;
+    lin = bh0 * npair + (rem - cidx * npair);
+  } else if (a.pair_order) {
     if ((int)blockIdx.x >= a.n_slots) return;
     lin = a.pair_order[blockIdx.x];
     if (lin < 0 || lin >= total) return;   // -1 = no item; larger entries belong to another shape
@@ -103,7 +115,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     const int lo = (int)(((int64_t)g * total + BSA_NXCD - 1) / BSA_NXCD);
     const int hi = (int)(((int64_t)(g + 1) * total + BSA_NXCD - 1) / BSA_NXCD);
     if (k >= hi - lo) return;
-    lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, lo, hi - lo, k);
+    lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, lo, hi - lo, k, a.pair_d);
   } else if (a.derive_order == 1) {
     // the same ranges as above in natural order (a grid of n_slots workgroups)
     const int g = blockIdx.x % BSA_NXCD, k = blockIdx.x / BSA_NXCD;
@@ -118,23 +130,35 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     if (a.derive_order == 2 && kth_longest_fits(a.nb, npair, sizeof(smem))) {
       // the same ranges, longest first inside each head
       const int head0 = lin / npair * npair;
-      lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, head0, npair, lin - head0);
+      lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, head0, npair, lin - head0, a.pair_d);
     }
   }
   const int bh = lin / npair, pidx = lin % npair;
   const int b = bh / a.H, h = bh % a.H;
-  const int iA = 2 * pidx, iB = 2 * pidx + 1;
-  const bool hasB = iB < a.nb;
-  const int rowA = bh * a.nb + iA;
+  // the pair's two query blocks: adjacent, or at the head's pairing offset
+  const int2 pb = pair_blocks(pidx, a.pair_d ? a.pair_d[bh] : 1, a.nb);
+  const int iA = pb.x, iB = pb.y;
+  const bool hasB = iB >= 0;
+  const int rowA = bh * a.nb + iA, rowB = bh * a.nb + iB;
   int sA, eA, sB = 0, eB = 0;
-  if (a.row_len) {   // fixed-stride lists
+  if (a.kv_chunk) {   // the part of each list inside chunk cidx
+    const int32_t* co = a.cofs + (int64_t)rowA * (a.nch + 1) + cidx;
+    sA = co[0];
+    eA = co[1];
+    if (hasB) {
+      const int32_t* cb = a.cofs + (int64_t)rowB * (a.nch + 1) + cidx;
+      sB = cb[0];
+      eB = cb[1];
+    }
+    if (sA == eA && sB == eB) return;   // nothing of this pair in the chunk (uniform over the workgroup)
+  } else if (a.row_len) {   // fixed-stride lists
     sA = rowA * a.row_stride;
     eA = sA + a.row_len[rowA];
-    if (hasB) { sB = sA + a.row_stride; eB = sB + a.row_len[rowA + 1]; }
+    if (hasB) { sB = rowB * a.row_stride; eB = sB + a.row_len[rowB]; }
   } else {
     sA = row_ptr[rowA];
     eA = row_ptr[rowA + 1];
-    if (hasB) { sB = eA; eB = row_ptr[rowA + 2]; }
+    if (hasB) { sB = row_ptr[rowB]; eB = row_ptr[rowB + 1]; }
   }
   const int i = pr ? iB : iA;                      // this wave's query block
   const bool mine_valid = pr == 0 || hasB;
@@ -392,6 +416,21 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   // ---- epilogue: O = O^T / l, written row-major; padded rows and empty rows are 0
   if (!mine_valid) return;
   const float lt = l_run + partner(l_run);
+  if (a.kv_chunk) {
+    // the chunk's partial state of this block's rows, unnormalised; a block with nothing
+    // in the chunk writes nothing (the combine skips the chunk from the same offsets)
+    if (pr ? eB == sB : eA == sA) return;
+    const int64_t slot = ((int64_t)row * a.nch + cidx) * 64 + wv * 32 + l32;
+    if (hi == 0) a.part_ml[slot] = float2{m_run, lt};
+    float* po = a.part_o + slot * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4_t*)(po + 32 * dt + 8 * g + 4 * hi) =
+            f32x4_t{oacc[dt][4 * g], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2], oacc[dt][4 * g + 3]};
+    return;
+  }
   const int q = i * 64 + wv * 32 + l32;
   const bool live = q < a.S_valid && lt > 0.f;
   const float inv = live ? 1.f / lt : 0.f;
@@ -442,8 +481,239 @@ hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, 
   return hipGetLastError();
 }
 
+// ---- kv-chunked walk: chunk offsets and the combine
+//
+// Each chunk's partial state of a query is (m, l, u): m the running maximum of its scores
+// (log2 units), l the sum of its probabilities 2^(s - m) and u the sum of those
+// probabilities times the value rows. Online softmax is associative (FlashAttention,
+// Daily Papers listing; the split reduction of LeanAttention, same listing): with
+// M = max m_c, the whole row has l = sum_c l_c 2^(m_c - M), O = sum_c u_c 2^(m_c - M) / l
+// and lse = (M + log2 l) ln 2, whatever the split.
+
+// cofs[r][c] = position of row r's first list entry >= c W (c = 0 .. nch); lists ascending
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* __restrict__ row_ptr,
+                                                            const int32_t* __restrict__ col_idx,
+                                                            const int32_t* __restrict__ row_len, int row_stride,
+                                                            int64_t rows, int nch, int W, int32_t* __restrict__ cofs) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * (nch + 1)) return;
+  const int64_t r = t / (nch + 1);
+  const int c = (int)(t - r * (nch + 1));
+  int lo, hi;
+  if (row_len) {
+    lo = (int)(r * row_stride);
+    hi = lo + row_len[r];
+  } else {
+    lo = row_ptr[r];
+    hi = row_ptr[r + 1];
+  }
+  if (c < nch) {
+    const int target = c * W;
+    while (lo < hi) {   // first entry >= target
+      const int mid = (lo + hi) >> 1;
+      if (col_idx[mid] < target) lo = mid + 1;
+      else hi = mid;
+    }
+  } else {
+    lo = hi;
+  }
+  cofs[t] = lo;
+}
+
+// One workgroup per query block: thread t merges query t / 4, a quarter of its D columns,
+// over the block's chunks in ascending order (a fixed order: the result does not depend
+// on scheduling). Padded queries and queries with nothing kept get O = 0, lse = -inf.
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int DQ = D / 4;   // columns per thread
+  const int64_t row = blockIdx.x;
+  const int bh = (int)(row / a.nb), blk = (int)(row - (int64_t)bh * a.nb);
+  const int b = bh / a.H, h = bh % a.H;
+  const int ql = threadIdx.x >> 2, d0 = (threadIdx.x & 3) * DQ;
+  const int q = blk * 64 + ql;
+  const int32_t* co = a.cofs + row * (a.nch + 1);
+  f32x4_t acc[DQ / 4];
+#pragma unroll
+  for (int x = 0; x < DQ / 4; ++x) acc[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, L = 0.f;
+  int prev = co[0];
+  for (int c = 0; c < a.nch; ++c) {
+    const int next = co[c + 1];
+    if (next == prev) continue;   // nothing of this row in chunk c: no partial state written
+    prev = next;
+    const int64_t slot = (row * a.nch + c) * 64 + ql;
+    const float2 ml = a.part_ml[slot];
+    if (!(ml.y > 0.f)) continue;  // only padded keys in the chunk
+    const f32x4_t* u = (const f32x4_t*)(a.part_o + slot * D + d0);
+    float wc;
+    if (ml.x > M) {
+      const float r = __builtin_amdgcn_exp2f(M - ml.x);   // 0 on the first chunk (M = -inf)
+#pragma unroll
+      for (int x = 0; x < DQ / 4; ++x) acc[x] *= r;
+      L *= r;
+      M = ml.x;
+      wc = 1.f;
+    } else {
+      wc = __builtin_amdgcn_exp2f(ml.x - M);
+    }
+    L += ml.y * wc;
+#pragma unroll
+    for (int x = 0; x < DQ / 4; ++x) acc[x] += u[x] * wc;
+  }
+  const bool live = q < a.S_valid && L > 0.f;
+  const float inv = live ? 1.f / L : 0.f;
+  if (a.lse && (threadIdx.x & 3) == 0)
+    a.lse[(int64_t)bh * a.S + q] = live ? (M + log2f(L)) * 0.69314718055994530942f : -INFINITY;
+  if constexpr (F32OUT) {
+    float* o = (float*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d0;
+#pragma unroll
+    for (int x = 0; x < DQ / 4; ++x) *(f32x4_t*)(o + 4 * x) = acc[x] * inv;
+  } else {
+    u16* o = (u16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)q * a.o_ss + d0;
+#pragma unroll
+    for (int x = 0; x < DQ / 4; ++x) {
+      uint2 w;
+      w.x = pk_bf16(acc[x][0] * inv, acc[x][1] * inv);
+      w.y = pk_bf16(acc[x][2] * inv, acc[x][3] * inv);
+      *(uint2*)(o + 4 * x) = w;
+    }
+  }
+}
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- pairing offsets
+//
+// A workgroup walks the union of its two query blocks' kv lists, so each kv tile that only
+// one of them keeps costs the other block's waves a step. Adjacent blocks are not always
+// the most alike: in row-major video layouts a block's list is often closer to the block
+// one frame later. The offset d of each head minimises the number of union steps over the
+// pairings pair_blocks(., d): the lists become bit rows, then each candidate d is costed
+// by popcounts of ORed rows.
+
+// bits[r][w] = bit j - 64 w set iff row r's list holds key block j (64 w <= j < 64 w + 64)
+__global__ __launch_bounds__(256) void row_bits_kernel(const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ col_idx,
+                                                       const int32_t* __restrict__ row_len, int row_stride,
+                                                       int64_t rows, int nw, uint64_t* __restrict__ bits) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * nw) return;
+  const int64_t r = t / nw;
+  const int w = (int)(t - r * nw), base = 64 * w;
+  int lo, hi;
+  if (row_len) {
+    lo = (int)(r * row_stride);
+    hi = lo + row_len[r];
+  } else {
+    lo = row_ptr[r];
+    hi = row_ptr[r + 1];
+  }
+  while (lo < hi) {   // first entry >= base
+    const int mid = (lo + hi) >> 1;
+    if (col_idx[mid] < base) lo = mid + 1;
+    else hi = mid;
+  }
+  const int end = row_len ? (int)(r * row_stride) + row_len[r] : row_ptr[r + 1];
+  uint64_t m = 0;
+  for (int e = lo; e < end; ++e) {
+    const int j = col_idx[e] - base;
+    if (j >= 64) break;
+    m |= 1ull << j;
+  }
+  bits[t] = m;
+}
+
+// cost[bh][d - 1] = sum over the pairs of pair_blocks(., d) of |list(a) u list(b)|; grid (BH, dmax)
+__global__ __launch_bounds__(256) void pair_cost_kernel(const uint64_t* __restrict__ bits, int nb, int nw,
+                                                        unsigned long long* __restrict__ cost) {
+  const int bh = blockIdx.x, d = blockIdx.y + 1;
+  const int npair = (nb + 1) / 2;
+  const uint64_t* hb = bits + (int64_t)bh * nb * nw;
+  unsigned acc = 0;
+  for (int x = threadIdx.x; x < npair * nw; x += blockDim.x) {
+    const int p = x / nw, w = x - p * nw;
+    const int2 pb = pair_blocks(p, d, nb);
+    uint64_t m = hb[(int64_t)pb.x * nw + w];
+    if (pb.y >= 0) m |= hb[(int64_t)pb.y * nw + w];
+    acc += (unsigned)__popcll(m);
+  }
+  __shared__ unsigned long long part[4];
+  unsigned long long v = acc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) cost[(int64_t)bh * PAIR_D_MAX + d - 1] = part[0] + part[1] + part[2] + part[3];
+}
+
+// pair_d[bh] = the d of least cost, ties to the smaller d; one wave per head
+__global__ __launch_bounds__(64) void pair_pick_kernel(const unsigned long long* __restrict__ cost, int dmax,
+                                                       int32_t* __restrict__ pair_d) {
+  const int bh = blockIdx.x, l = threadIdx.x;
+  unsigned long long c = l < dmax ? cost[(int64_t)bh * PAIR_D_MAX + l] : ~0ull;
+  int d = l + 1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long c2 = __shfl_xor(c, o, 64);
+    const int d2 = __shfl_xor(d, o, 64);
+    if (c2 < c || (c2 == c && d2 < d)) { c = c2; d = d2; }
+  }
+  if (l == 0) pair_d[bh] = d;
+}
+
+size_t pair_bits_ws(int64_t rows, int nb) {
+  const int64_t BH = rows / (nb > 0 ? nb : 1);
+  return al256((size_t)rows * ((nb + 63) / 64) * 8) + al256((size_t)BH * PAIR_D_MAX * 8);
+}
+
+hipError_t launch_pair_offsets(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_len,
+                               int row_stride, int BH, int nb, uint64_t* bits, int32_t* pair_d, hipStream_t st) {
+  const int nw = (nb + 63) / 64, dmax = nb / 2 < PAIR_D_MAX ? (nb / 2 > 1 ? nb / 2 : 1) : PAIR_D_MAX;
+  const int64_t rows = (int64_t)BH * nb, n = rows * nw;
+  unsigned long long* cost = (unsigned long long*)((char*)bits + al256((size_t)n * 8));
+  hipLaunchKernelGGL(row_bits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, row_ptr, col_idx, row_len,
+                     row_stride, rows, nw, bits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_cost_kernel, dim3((unsigned)BH, (unsigned)dmax), dim3(256), 0, st, bits, nb, nw, cost);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_pick_kernel, dim3((unsigned)BH), dim3(64), 0, st, cost, dmax, pair_d);
+  return hipGetLastError();
+}
+size_t chunk_ws_bytes(int64_t rows, int nb, int D, int kv_chunk) {
+  if (kv_chunk <= 0) return 0;
+  const size_t nch = (size_t)((nb + kv_chunk - 1) / kv_chunk);
+  return al256((size_t)rows * (nch + 1) * 4) + al256((size_t)rows * nch * 64 * 8) +
+         al256((size_t)rows * nch * 64 * D * 4);
+}
+void chunk_ws_carve(AttnArgs& a, void* ws) {
+  const int64_t rows = (int64_t)a.B * a.H * a.nb;
+  a.nch = (a.nb + a.kv_chunk - 1) / a.kv_chunk;
+  char* w = (char*)ws;
+  a.cofs = (int32_t*)w;
+  w += al256((size_t)rows * (a.nch + 1) * 4);
+  a.part_ml = (float2*)w;
+  w += al256((size_t)rows * a.nch * 64 * 8);
+  a.part_o = (float*)w;
+}
+
 template <int MODE, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
+  if (a.kv_chunk) {
+    const int64_t rows = (int64_t)a.B * a.H * a.nb;
+    const int64_t nofs = rows * (a.nch + 1);
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3((unsigned)((nofs + 255) / 256)), dim3(256), 0, st, a.row_ptr,
+                       a.col_idx, a.row_len, a.row_stride, rows, a.nch, a.kv_chunk, a.cofs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = rows / a.nb * a.nch * ((a.nb + 1) / 2);
+    const int64_t grid = (items + BSA_NXCD - 1) / BSA_NXCD * BSA_NXCD;
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, st, a, a.row_ptr,
+                       a.col_idx, a.q_scale, a.k_scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_combine_kernel<D, MODE == ATTN_SPLIT_F32>), dim3((unsigned)rows), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const int total = a.B * a.H * ((a.nb + 1) / 2);
   dim3 grid(a.pair_order || a.derive_order == 1 ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
   hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,

@@ -5,8 +5,23 @@
 
 namespace bsa {
 
-// Item it = (head, pair p of adjacent rows 2p, 2p+1) costs the longer of the pair's two
-// lists, len(row) for rows (it / npair) * nb + 2p (+1), clamped to [0, nb].
+// Query blocks of pair p (of ceil(nb / 2)) when a head's blocks are paired at offset d >= 1:
+// the blocks are taken in runs of 2d, block a of a run's first half paired with a + d; the
+// blocks after the last whole run pair with their neighbour. d = 1: pairs (2p, 2p + 1).
+// y = -1 when the pair has one block (odd nb).
+__host__ __device__ inline int2 pair_blocks(int p, int d, int nb) {
+  const int full = nb / (2 * d) * (2 * d);
+  if (2 * p < full) {
+    const int r = p / d, a = 2 * r * d + (p - r * d);
+    return make_int2(a, a + d);
+  }
+  const int a = full + 2 * (p - full / 2);
+  return make_int2(a, a + 1 < nb ? a + 1 : -1);
+}
+
+// Item it = (head, pair p) costs the longer of the pair's two lists (rows of
+// pair_blocks(p, d) of head it / npair, d = pair_d[head], or 1 without pair_d), clamped
+// to [0, nb].
 // kth_longest_item returns the item at position k of the items [lo, lo + R) ordered by
 // decreasing cost, equal costs in ascending item order, so that every workgroup derives
 // the same order by itself: a cost histogram in shared memory, a descending scan of it
@@ -20,7 +35,7 @@ __host__ __device__ constexpr bool kth_longest_fits(int nb, int R, int sm_bytes)
   return kth_longest_ints(nb, R) <= sm_bytes / 4;
 }
 template <int NT, typename Len>
-__device__ int kth_longest_item(Len len, int nb, int* sm, int lo, int R, int k) {
+__device__ int kth_longest_item(Len len, int nb, int* sm, int lo, int R, int k, const int32_t* pair_d = nullptr) {
   const int npair = (nb + 1) / 2;
   const int t = threadIdx.x, lane = t & 63, nk = nb + 1;
   int* hist = sm;
@@ -29,9 +44,10 @@ __device__ int kth_longest_item(Len len, int nb, int* sm, int lo, int R, int k) 
   for (int x = t; x < nk; x += NT) hist[x] = 0;
   __syncthreads();
   for (int i = t; i < R; i += NT) {
-    const int it = lo + i, p = it % npair, rA = (it / npair) * nb + 2 * p;
-    int c = len(rA);
-    if (2 * p + 1 < nb) c = max(c, len(rA + 1));
+    const int it = lo + i, bh = it / npair;
+    const int2 pb = pair_blocks(it - bh * npair, pair_d ? pair_d[bh] : 1, nb);
+    int c = len(bh * nb + pb.x);
+    if (pb.y >= 0) c = max(c, len(bh * nb + pb.y));
     c = min(max(c, 0), nb);
     cost[i] = c;
     atomicAdd(&hist[c], 1);

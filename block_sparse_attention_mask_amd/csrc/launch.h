@@ -131,8 +131,32 @@ struct AttnArgs {
   const float* q_scale; const float* k_scale;
   int B, H, nb, S, S_valid, D;
   float scale_log2;      // softmax scale * log2(e)
+  // pairing offset of each head [B*H] (NULL: adjacent pairs): pair p walks the query
+  // blocks pair_blocks(p, pair_d[head], nb); pair_order, when given, assumes adjacent pairs
+  const int32_t* pair_d;
+  // kv-chunked walk (kv_chunk > 0; pair_order and derive_order unused): the work items
+  // are (head, chunk c, pair), chunk c = key blocks [c kv_chunk, (c+1) kv_chunk), walked
+  // chunk-major inside each head; every item leaves its rows' partial state in part_o /
+  // part_ml and a combine launch merges the chunks. Workspace: chunk_ws_bytes().
+  int kv_chunk, nch;     // chunk width in key blocks; chunks per row = ceil(nb / kv_chunk)
+  int32_t* cofs;         // [rows][nch + 1]: position in col_idx of row r's first entry >= c kv_chunk
+  float* part_o;         // [rows][nch][64][D] fp32: sum of p V over the chunk's tiles (p relative to m)
+  float2* part_ml;       // [rows][nch][64]: (m, l) = running maximum (log2 units) and sum of p
 };
 enum AttnMode { ATTN_BF16 = 0, ATTN_SPLIT_F32 = 1, ATTN_FP8 = 2 };
+// workspace bytes of the kv-chunked walk (0 when kv_chunk == 0); rows = B H nb
+size_t chunk_ws_bytes(int64_t rows, int nb, int D, int kv_chunk);
+// points a.cofs, a.part_o, a.part_ml into ws (chunk_ws_bytes bytes, 256-aligned)
+void chunk_ws_carve(AttnArgs& a, void* ws);
+// pairing offsets: for each head the d in [1, min(PAIR_D_MAX, nb / 2)] whose pairs
+// (pair_blocks) have the fewest union steps, sum over pairs of |list(a) u list(b)|, ties to
+// the smaller d; lists as in AttnArgs (row_len != NULL: fixed stride). bits: pair_bits_ws
+// bytes of workspace.
+constexpr int PAIR_D_MAX = 64;
+size_t pair_bits_ws(int64_t rows, int nb);
+hipError_t launch_pair_offsets(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_len,
+                               int row_stride, int BH, int nb, uint64_t* bits, int32_t* pair_d, hipStream_t st);
+// the attention launch (with kv_chunk > 0: the offsets, the chunk walk and the combine)
 hipError_t launch_attn(const AttnArgs& a, AttnMode mode, hipStream_t st);
 hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, int B, int H, int S, int D,
                             uint16_t* hi, uint16_t* lo, hipStream_t st);

@@ -299,13 +299,14 @@ bsa_status bsa_mask_to_csr_ordered(const uint8_t* mask, int64_t mask_sb, int64_t
  *   o          output [B,H,S,D]: bf16, or f32 when q, k are f32; o->ptr is written
  *   lse        optional (NULL = none) float [B,H,S] natural-log sum of exp
  *   ws         at least attn_workspace_size(shape, q->dtype) bytes, 256-byte
- *              aligned (holds the kv lists and, for f32 inputs, hi/lo bf16 copies)
+ *              aligned (holds the kv lists, for f32 inputs hi/lo bf16 copies, and
+ *              the partial states of the kv-chunked walk below)
  * All of q, k, v, o must have 16-byte aligned rows (ss*elem_size % 16 == 0 and the
  * base pointers 16-byte aligned).
  * block_sparse_attn_fwd_csr takes kv lists already built by bsa_mask_to_csr (for
  * masks reused across calls) and needs attn_csr_workspace_size(shape, q->dtype)
- * bytes, 256-byte aligned (for f32 inputs the hi/lo bf16 copies; the size is 0 for
- * bf16 and fp8 inputs, and ws may then be NULL).
+ * bytes, 256-byte aligned (for f32 inputs the hi/lo bf16 copies, and the partial
+ * states of the kv-chunked walk; when the size is 0, ws may be NULL).
  *
  * Work order: one workgroup per pair of adjacent query blocks; the pairs are cut
  * into 8 contiguous ranges, one per XCD. When the pairs make at most four rounds over
@@ -320,7 +321,45 @@ bsa_status bsa_mask_to_csr_ordered(const uint8_t* mask, int64_t mask_sb, int64_t
  * with more pairs (0 slots) run the ranges in natural order, or, from nb = 512 on, with
  * each head's pairs longest first, also derived in the kernel. The order never changes
  * the results.
+ *
+ * Pairing offsets: for shapes without a work order and from nb = 512 on, the two query
+ * blocks of a workgroup are not always neighbours. The workgroup walks the union of their
+ * kv lists, and a tile that only one block keeps idles the other block's waves for a step;
+ * in row-major video layouts a block's list is often closer to that of the block one
+ * frame later. So each call first picks, for every head, the offset d in [1, min(64,
+ * nb/2)] whose pairing has the fewest union steps (sum over pairs of |list(a) u list(b)|,
+ * ties to the smaller d): the blocks are taken in runs of 2d, block a of a run's first half
+ * paired with a + d, and the blocks after the last whole run pair with their neighbour
+ * (d = 1: pairs (2p, 2p + 1)). Three small launches; the workspace includes their
+ * buffers. The pairing never changes the results beyond the order of the list walk, which
+ * is ascending for every block either way: outputs are the same bit for bit.
+ * attn_pair_offsets writes the offsets the attention would choose for the kv lists
+ * (row_ptr/col_idx, or with row_ptr NULL the fixed-stride lists kv_len/col_idx of stride
+ * nb) into pair_d (int32 [B*H]); its workspace is attn_pair_workspace_size(shape) bytes,
+ * 256-byte aligned.
+ *
+ * kv-chunked walk [LeanAttention (Daily Papers listing): the online softmax of a row
+ * split into parts that are merged afterwards], taken only when asked for:
+ * bsa_set_attn_kv_chunk(w) with w > 0 makes every later attention call (and workspace
+ * query) of the process cut the key blocks into chunks of w blocks and run every
+ * (head, chunk, pair of query blocks) as a work item; the 8 XCD ranges take the items
+ * chunk-major inside each head, so that the workgroups running together on an XCD read
+ * the same K/V tiles from its L2 (w = 64 at D = 128 keeps 2 MB of K and V per chunk).
+ * Each item leaves the unnormalised partial output and (max, sum) of its rows in the
+ * workspace (B*H*nb rows x ceil(nb/w) chunks x 64 x (4 D + 8) bytes: 27.9 GB at B=1,
+ * H=40, S=75648, D=128, w=64), and a combine launch merges a row's chunks in ascending
+ * order. The results are deterministic and equal to the whole-row walk's up to rounding
+ * (each chunk rounds its probabilities to bf16 against its own running maximum). The
+ * work order is not used. w <= 0 returns to whole rows (the default); the call returns
+ * the previous width. Workspace sizes follow the setting, so query them after changing
+ * it. At the 14B shape the chunked walk cuts the attention kernel's L2 misses twelvefold
+ * but not its time, and the combine adds about 12%.
  * ------------------------------------------------------------------------- */
+int bsa_set_attn_kv_chunk(int kv_chunk);
+size_t attn_pair_workspace_size(const bsa_shape* shape);
+bsa_status attn_pair_offsets(const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                             const int32_t* kv_len, int32_t* pair_d, void* ws, size_t ws_bytes,
+                             bsa_stream_t stream);
 size_t attn_workspace_size(const bsa_shape* shape, bsa_dtype qk_dtype);
 bsa_status block_sparse_attn_fwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
                                  const bsa_shape* shape,
