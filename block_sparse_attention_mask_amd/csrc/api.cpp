@@ -587,6 +587,8 @@ static bsa_status attn_common(const bsa_tensor* q, const bsa_tensor* k, const bs
     hipError_t e = bsa::launch_pair_offsets(row_ptr, col_idx, row_len, a.row_stride, a.B * a.H, a.nb, bits, pair_d, hs);
     if (e != hipSuccess) return hip_status(e, "pairing offsets launch");
     a.pair_d = pair_d;
+    a.row_bits = bits;
+    a.nw = (a.nb + 63) / 64;
   }
   if (mode == bsa::ATTN_SPLIT_F32) {
     const size_t sb = split_bytes(shape);

@@ -52,7 +52,8 @@ constexpr float RESCALE_TAU = 8.f;
 // K(u+1) are copied next; S and the softmax of tile u run while V(u) lands; a second
 // barrier makes all parts of V(u) visible before PV. K(u+1) has a whole step to land.
 // Each wave issues a quarter of every tile copy.
-template <int MODE, int D>
+// BITS: the union walk reads the pair's lists as bit rows (a.row_bits) instead of entries.
+template <int MODE, int D, bool BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                      const float* __restrict__ q_scale, const float* __restrict__ k_scale) {
@@ -225,13 +226,36 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     cache = col_idx[x];
     if constexpr (MODE == ATTN_FP8) ksc = k_scale[bh * a.nb + cache];
   };
-  if (sA < eA) fetch(cbA, eA, cacheA, kscA);
-  if (sB < eB) fetch(cbB, eB, cacheB, kscB);
+  // BITS: word w of a bit row holds the list's blocks 64 w .. 64 w + 63; the word being
+  // walked is in scalar registers with its visited bits cleared, the next one a scalar
+  // load away (no vector registers, one load per 64 key blocks)
+  using CU64 = const uint64_t __attribute__((address_space(4)));
+  CU64* bitsA = BITS ? (CU64*)(uintptr_t)(a.row_bits + (int64_t)rowA * a.nw) : nullptr;
+  CU64* bitsB = BITS && hasB ? (CU64*)(uintptr_t)(a.row_bits + (int64_t)rowB * a.nw) : nullptr;
+  uint64_t curA = 0, curB = 0;
+  int wi = -1;
+  if constexpr (!BITS) {
+    if (sA < eA) fetch(cbA, eA, cacheA, kscA);
+    if (sB < eB) fetch(cbB, eB, cacheB, kscB);
+  }
   __builtin_amdgcn_s_waitcnt(0);            // Q and the first list chunks are in registers
 
   // next union entry: returns the kv block (or -1 when both lists are done), the use
   // flags (bit 0: block 2p, bit 1: block 2p+1) and the fp8 key scale
   auto next_entry = [&](int& flags, float& ksc) -> int {
+    if constexpr (BITS) {
+      (void)ksc;
+      while ((curA | curB) == 0) {   // the next word holding a block of either list
+        if (++wi >= a.nw) { flags = 0; return -1; }
+        curA = bitsA[wi];
+        curB = bitsB ? bitsB[wi] : 0ull;
+      }
+      const int t = __builtin_ctzll(curA | curB);
+      flags = (int)((curA >> t) & 1ull) | (int)(((curB >> t) & 1ull) << 1);
+      curA &= ~(1ull << t);
+      curB &= ~(1ull << t);
+      return 64 * wi + t;
+    }
     const int BIG = 0x7fffffff;
     if (ia < eA && ia - cbA == 64) { cbA += 64; fetch(cbA, eA, cacheA, kscA); __builtin_amdgcn_s_waitcnt(0); }
     if (ib < eB && ib - cbB == 64) { cbB += 64; fetch(cbB, eB, cacheB, kscB); __builtin_amdgcn_s_waitcnt(0); }
@@ -287,7 +311,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
         // operand reads run PD MFMAs ahead. Scheduling fences keep this order; left alone,
         // the compiler runs the chains one after the other and reads each operand right
         // before its MFMA.
-        constexpr int NM = 2 * KS, PD = 6;
+        constexpr int NM = 2 * KS, PD = BITS ? 5 : 6;
         auto kread = [&](int m) {
           return *(const bf16x8_t BSA_LDS*)(lds + (ka ^ (32 * (m >> 1))) + (m & 1) * 32 * RBK);
         };
@@ -708,7 +732,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const int64_t items = rows / a.nb * a.nch * ((a.nb + 1) / 2);
     const int64_t grid = (items + BSA_NXCD - 1) / BSA_NXCD * BSA_NXCD;
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, st, a, a.row_ptr,
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, D, false>), dim3((unsigned)grid), dim3(256), 0, st, a, a.row_ptr,
                        a.col_idx, a.q_scale, a.k_scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((attn_combine_kernel<D, MODE == ATTN_SPLIT_F32>), dim3((unsigned)rows), dim3(256), 0, st, a);
@@ -716,7 +740,14 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   }
   const int total = a.B * a.H * ((a.nb + 1) / 2);
   dim3 grid(a.pair_order || a.derive_order == 1 ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
-  hipLaunchKernelGGL((attn_fwd_kernel<MODE, D>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
+  if constexpr (MODE != ATTN_FP8) {
+    if (a.row_bits) {
+      hipLaunchKernelGGL((attn_fwd_kernel<MODE, D, true>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
+                         a.k_scale);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<MODE, D, false>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
                      a.k_scale);
   return hipGetLastError();
 }
