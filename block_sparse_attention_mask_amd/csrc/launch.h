@@ -98,6 +98,16 @@ hipError_t launch_pair_schedule(const int32_t* row_ptr, int BH, int nb, int32_t*
 // the same order for fixed-stride lists, from their lengths kv_len [BH * nb]
 hipError_t launch_pair_schedule_len(const int32_t* kv_len, int BH, int nb, int32_t* order, hipStream_t st);
 
+// pairing offsets of the attention's query-block pairs: for each head the d in
+// [1, min(PAIR_D_MAX, nb / 2)] whose pairs (pair_blocks) have the fewest union steps, sum
+// over pairs of |list(a) u list(b)|, ties to the smaller d; lists as in AttnArgs (row_len
+// != NULL: fixed stride). bits: pair_bits_ws bytes of workspace, the lists' bit rows
+// [rows][ceil(nb / 64)] first.
+constexpr int PAIR_D_MAX = 64;
+size_t pair_bits_ws(int64_t rows, int nb);
+hipError_t launch_pair_offsets(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_len,
+                               int row_stride, int BH, int nb, uint64_t* bits, int32_t* pair_d, hipStream_t st);
+
 // reorder.hip
 constexpr int ORDER_ROW = 0, ORDER_TILE = 1, ORDER_SPATIAL = 2;
 struct ReorderGeom {
@@ -151,14 +161,6 @@ enum AttnMode { ATTN_BF16 = 0, ATTN_SPLIT_F32 = 1, ATTN_FP8 = 2 };
 size_t chunk_ws_bytes(int64_t rows, int nb, int D, int kv_chunk);
 // points a.cofs, a.part_o, a.part_ml into ws (chunk_ws_bytes bytes, 256-aligned)
 void chunk_ws_carve(AttnArgs& a, void* ws);
-// pairing offsets: for each head the d in [1, min(PAIR_D_MAX, nb / 2)] whose pairs
-// (pair_blocks) have the fewest union steps, sum over pairs of |list(a) u list(b)|, ties to
-// the smaller d; lists as in AttnArgs (row_len != NULL: fixed stride). bits: pair_bits_ws
-// bytes of workspace.
-constexpr int PAIR_D_MAX = 64;
-size_t pair_bits_ws(int64_t rows, int nb);
-hipError_t launch_pair_offsets(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_len,
-                               int row_stride, int BH, int nb, uint64_t* bits, int32_t* pair_d, hipStream_t st);
 // the attention launch (with kv_chunk > 0: the offsets, the chunk walk and the combine)
 hipError_t launch_attn(const AttnArgs& a, AttnMode mode, hipStream_t st);
 hipError_t launch_split_f32(const float* x, int64_t sb, int64_t sh, int64_t ss, int B, int H, int S, int D,

@@ -5,6 +5,7 @@
 // of the CalibAtt page: the attention kernel visits only the listed blocks.
 #include "common.h"
 #include "launch.h"
+#include "item_order.h"
 #include "work_order.h"
 
 namespace bsa {
@@ -442,6 +443,107 @@ hipError_t launch_pair_schedule(const int32_t* row_ptr, int BH, int nb, int32_t*
   const int nk = nb + 1;
   hipLaunchKernelGGL(pair_schedule_kernel, dim3(1), dim3(1024), 2 * SCHED_RANGES * nk * 4, st, row_ptr, BH, nb,
                      order);
+  return hipGetLastError();
+}
+
+static size_t pairing_al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- pairing offsets
+//
+// A workgroup walks the union of its two query blocks' kv lists, so each kv tile that only
+// one of them keeps costs the other block's waves a step. Adjacent blocks are not always
+// the most alike: in row-major video layouts a block's list is often closer to the block
+// one frame later. The offset d of each head minimises the number of union steps over the
+// pairings pair_blocks(., d): the lists become bit rows, then each candidate d is costed
+// by popcounts of ORed rows.
+
+// bits[r][w] = bit j - 64 w set iff row r's list holds key block j (64 w <= j < 64 w + 64).
+// One wave per row: the row's words are cleared in shared memory, every list entry ORs its
+// bit in (LDS atomics), and the words are written out. Shared memory: 4 rows x nw words.
+__global__ __launch_bounds__(256) void row_bits_kernel(const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ col_idx,
+                                                       const int32_t* __restrict__ row_len, int row_stride,
+                                                       int64_t rows, int nw, uint64_t* __restrict__ bits) {
+  extern __shared__ unsigned long long row_words[];
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wv;
+  unsigned long long* w = row_words + wv * nw;
+  for (int x = l; x < nw; x += 64) w[x] = 0ull;
+  __syncthreads();
+  if (r < rows) {
+    int lo, hi;
+    if (row_len) {
+      lo = (int)(r * row_stride);
+      hi = lo + row_len[r];
+    } else {
+      lo = row_ptr[r];
+      hi = row_ptr[r + 1];
+    }
+    for (int e = lo + l; e < hi; e += 64) {
+      const int j = col_idx[e];
+      atomicOr(&w[j >> 6], 1ull << (j & 63));
+    }
+  }
+  __syncthreads();
+  if (r < rows)
+    for (int x = l; x < nw; x += 64) bits[r * nw + x] = w[x];
+}
+
+// cost[bh][d - 1] = sum over the pairs of pair_blocks(., d) of |list(a) u list(b)|; grid (BH, dmax)
+__global__ __launch_bounds__(256) void pair_cost_kernel(const uint64_t* __restrict__ bits, int nb, int nw,
+                                                        unsigned long long* __restrict__ cost) {
+  const int bh = blockIdx.x, d = blockIdx.y + 1;
+  const int npair = (nb + 1) / 2;
+  const uint64_t* hb = bits + (int64_t)bh * nb * nw;
+  unsigned acc = 0;
+  for (int x = threadIdx.x; x < npair * nw; x += blockDim.x) {
+    const int p = x / nw, w = x - p * nw;
+    const int2 pb = pair_blocks(p, d, nb);
+    uint64_t m = hb[(int64_t)pb.x * nw + w];
+    if (pb.y >= 0) m |= hb[(int64_t)pb.y * nw + w];
+    acc += (unsigned)__popcll(m);
+  }
+  __shared__ unsigned long long part[4];
+  unsigned long long v = acc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) cost[(int64_t)bh * PAIR_D_MAX + d - 1] = part[0] + part[1] + part[2] + part[3];
+}
+
+// pair_d[bh] = the d of least cost, ties to the smaller d; one wave per head
+__global__ __launch_bounds__(64) void pair_pick_kernel(const unsigned long long* __restrict__ cost, int dmax,
+                                                       int32_t* __restrict__ pair_d) {
+  const int bh = blockIdx.x, l = threadIdx.x;
+  unsigned long long c = l < dmax ? cost[(int64_t)bh * PAIR_D_MAX + l] : ~0ull;
+  int d = l + 1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long c2 = __shfl_xor(c, o, 64);
+    const int d2 = __shfl_xor(d, o, 64);
+    if (c2 < c || (c2 == c && d2 < d)) { c = c2; d = d2; }
+  }
+  if (l == 0) pair_d[bh] = d;
+}
+
+size_t pair_bits_ws(int64_t rows, int nb) {
+  const int64_t BH = rows / (nb > 0 ? nb : 1);
+  return pairing_al256((size_t)rows * ((nb + 63) / 64) * 8) + pairing_al256((size_t)BH * PAIR_D_MAX * 8);
+}
+
+hipError_t launch_pair_offsets(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_len,
+                               int row_stride, int BH, int nb, uint64_t* bits, int32_t* pair_d, hipStream_t st) {
+  const int nw = (nb + 63) / 64, dmax = nb / 2 < PAIR_D_MAX ? (nb / 2 > 1 ? nb / 2 : 1) : PAIR_D_MAX;
+  const int64_t rows = (int64_t)BH * nb, n = rows * nw;
+  unsigned long long* cost = (unsigned long long*)((char*)bits + pairing_al256((size_t)n * 8));
+  hipLaunchKernelGGL(row_bits_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 4 * nw * sizeof(uint64_t), st,
+                     row_ptr, col_idx, row_len, row_stride, rows, nw, bits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_cost_kernel, dim3((unsigned)BH, (unsigned)dmax), dim3(256), 0, st, bits, nb, nw, cost);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_pick_kernel, dim3((unsigned)BH), dim3(64), 0, st, cost, dmax, pair_d);
   return hipGetLastError();
 }
 
