@@ -244,7 +244,6 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
   // flags (bit 0: block 2p, bit 1: block 2p+1) and the fp8 key scale
   auto next_entry = [&](int& flags, float& ksc) -> int {
     if constexpr (BITS) {
-      (void)ksc;
       while ((curA | curB) == 0) {   // the next word holding a block of either list
         if (++wi >= a.nw) { flags = 0; return -1; }
         curA = bitsA[wi];
@@ -254,6 +253,8 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
       flags = (int)((curA >> t) & 1ull) | (int)(((curB >> t) & 1ull) << 1);
       curA &= ~(1ull << t);
       curB &= ~(1ull << t);
+      // the fp8 key scale of the entry, a scalar load used two steps later
+      if constexpr (MODE == ATTN_FP8) ksc = ((const float __attribute__((address_space(4)))*)(uintptr_t)k_scale)[bh * a.nb + 64 * wi + t];
       return 64 * wi + t;
     }
     const int BIG = 0x7fffffff;
@@ -642,7 +643,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   }
   const int total = a.B * a.H * ((a.nb + 1) / 2);
   dim3 grid(a.pair_order || a.derive_order == 1 ? a.n_slots : ((total + BSA_NXCD - 1) / BSA_NXCD) * BSA_NXCD);
-  if constexpr (MODE != ATTN_FP8) {
+  {
     if (a.row_bits) {
       hipLaunchKernelGGL((attn_fwd_kernel<MODE, D, true>), grid, dim3(256), 0, st, a, a.row_ptr, a.col_idx, a.q_scale,
                          a.k_scale);

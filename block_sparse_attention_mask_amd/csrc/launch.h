@@ -144,8 +144,8 @@ struct AttnArgs {
   // pairing offset of each head [B*H] (NULL: adjacent pairs): pair p walks the query
   // blocks pair_blocks(p, pair_d[head], nb); pair_order, when given, assumes adjacent pairs
   const int32_t* pair_d;
-  // the lists as bit rows [rows][nw] (launch_pair_offsets builds them), or NULL; bf16 and
-  // f32 inputs on the whole-row walk then read them instead of the entries
+  // the lists as bit rows [rows][nw] (launch_pair_offsets builds them), or NULL; the
+  // whole-row walk then reads them instead of the entries
   const uint64_t* row_bits; int nw;
   // kv-chunked walk (kv_chunk > 0; pair_order and derive_order unused): the work items
   // are (head, chunk c, pair), chunk c = key blocks [c kv_chunk, (c+1) kv_chunk), walked
