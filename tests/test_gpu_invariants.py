@@ -6,6 +6,8 @@ mistakes that a comparison at a few thresholds could miss:
     (measured with the oracle's probabilities; blocks the library flags as near the
     threshold are the only ones allowed to decide it differently), and the kept set grows as
     thr falls, exactly, since both are decided on the same fixed-point masses;
+  * every row keeps its top block, no dropped block outweighs a kept one, and permuting
+    whole blocks of Q and K permutes the mask alike;
   * Top-k: exactly min(k, nb) blocks per row;
   * attention (online softmax, FlashAttention abstract): every output row lies in the box
     spanned by the V rows it may attend to (a convex combination, up to the bf16 rounding
@@ -92,3 +94,46 @@ def test_attention_rows_are_convex_combinations(gpu_lib, cid, heads):
             assert np.all(np.isfinite(L[r])) and np.all(np.isneginf(L[rows[~valid]]))
             assert np.all(o[rows[~valid]] == 0)
     print(f"[invariants] {cfg.name}: {len(blocks)} blocks x {cfg.H} heads inside their V boxes", flush=True)
+
+
+def test_mask_rows_nonempty_and_separated(gpu_lib):
+    """Every row keeps its top block; no dropped block outweighs a kept one, up to flagged
+    (near-threshold) blocks."""
+    cfg = get_config(2, heads=4)
+    q, k, _ = make_inputs(cfg, seed=14, device=DEV)
+    P = oracle_probs(q, k)
+    for thr in THRS:
+        mask, near = gpu_lib.nabla_build_mask(q, k, thr, near=True)
+        torch.cuda.synchronize()
+        m = mask.cpu().numpy().astype(bool)
+        nr = near.cpu().numpy().astype(bool)
+        assert np.all(m.any(axis=-1)), thr
+        for idx in np.ndindex(m.shape[:-1]):
+            row, p, fl = m[idx], P[idx], nr[idx]
+            kept, dropped = p[row & ~fl], p[~row & ~fl]
+            if kept.size and dropped.size:   # entries equal to fp64 rounding may sort either way
+                assert kept.min() >= dropped.max() * (1.0 - 1e-12), (thr, idx)
+
+
+def test_mask_block_permutation_equivariance(gpu_lib):
+    """Permuting whole 64-token blocks of Q (rows of the map) and of K (its columns) permutes
+    the mask the same way, up to blocks flagged as near the threshold in either run (the
+    row sums are taken in another order, so the last bits of the masses move)."""
+    cfg = get_config(2, heads=3)
+    q, k, _ = make_inputs(cfg, seed=15, device=DEV)
+    nb = cfg.nb
+    rng = np.random.default_rng(15)
+    sq, sk = rng.permutation(nb), rng.permutation(nb)
+    tok = lambda perm: torch.from_numpy(np.concatenate([np.arange(j * 64, (j + 1) * 64) for j in perm])).to(DEV)
+    qp = q[:, :, tok(sq)].contiguous()
+    kp = k[:, :, tok(sk)].contiguous()
+    for thr in (0.05, 0.2, 0.6):
+        m0, n0 = gpu_lib.nabla_build_mask(q, k, thr, near=True)
+        m1, n1 = gpu_lib.nabla_build_mask(qp, kp, thr, near=True)
+        torch.cuda.synchronize()
+        a = m0.cpu().numpy().astype(bool)[:, :, sq][:, :, :, sk]
+        fa = n0.cpu().numpy().astype(bool)[:, :, sq][:, :, :, sk]
+        b = m1.cpu().numpy().astype(bool)
+        fb = n1.cpu().numpy().astype(bool)
+        diff = (a != b) & ~fa & ~fb
+        assert not diff.any(), (thr, int(diff.sum()))
