@@ -731,11 +731,20 @@ bsa_status block_sparse_attn_fwd_lists(const bsa_tensor* q, const bsa_tensor* k,
 // ---------------------------------------------------------------------------
 static size_t bwd_ld_bytes(const bsa_shape* s) { return align256(((size_t)s->B * s->H * s->S + 64) * 8); }
 
+// The backward pairs blocks at each head's offset, for its key-block pairs (dK, dV) and its
+// query-block pairs (dQ), from the same size on as the forward.
+static size_t bwd_pairing_bytes(const bsa_shape* s) {
+  const int nb = s->S / 64;
+  if (nb < PAIR_OFFSET_MIN_NB) return 0;
+  const int64_t BH = (int64_t)s->B * s->H;
+  return 2 * (align256((size_t)BH * 4) + bsa::pair_bits_ws(BH * nb, nb));
+}
+
 size_t attn_bwd_workspace_size(const bsa_shape* s) {
   if (!s || s->S <= 0 || s->B < 1 || s->H < 1) return 0;
   const size_t nb = s->S / 64, rows = (size_t)s->B * s->H * nb;
   return bwd_ld_bytes(s) + align256(rows * nb) + 2 * (align256((rows + 1) * 4) + align256(rows * nb * 4)) +
-         csr_workspace_size(s->B, s->H, (int)nb);
+         csr_workspace_size(s->B, s->H, (int)nb) + bwd_pairing_bytes(s);
 }
 
 bsa_status block_sparse_attn_bwd(const bsa_tensor* q, const bsa_tensor* k, const bsa_tensor* v,
@@ -798,6 +807,7 @@ bsa_status block_sparse_attn_bwd(const bsa_tensor* q, const bsa_tensor* k, const
   int32_t* row_idx = (int32_t*)w;
   w += align256(rows * nb * 4);
   int32_t* counts = (int32_t*)w;
+  w += csr_workspace_size(shape->B, shape->H, nb);
 
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = bsa::launch_bwd_prep(a, ld, hs);
@@ -809,6 +819,21 @@ bsa_status block_sparse_attn_bwd(const bsa_tensor* q, const bsa_tensor* k, const
   e = bsa::launch_csr(mt, (int64_t)shape->H * nb * nb, (int64_t)nb * nb, shape->B, shape->H, nb, col_ptr, row_idx,
                       counts, hs);
   if (e != hipSuccess) return hip_status(e, "csr launch (transposed)");
+  if (bwd_pairing_bytes(shape)) {
+    const int BH = shape->B * shape->H;
+    const size_t one = align256((size_t)BH * 4) + bsa::pair_bits_ws((int64_t)BH * nb, nb);
+    int32_t* pk = (int32_t*)w;
+    uint64_t* bk = (uint64_t*)(w + align256((size_t)BH * 4));
+    int32_t* pq = (int32_t*)(w + one);
+    uint64_t* bq = (uint64_t*)(w + one + align256((size_t)BH * 4));
+    e = bsa::launch_pair_offsets(col_ptr, row_idx, nullptr, nb, BH, nb, bk, pk, hs);
+    if (e != hipSuccess) return hip_status(e, "pairing offsets launch (key blocks)");
+    e = bsa::launch_pair_offsets(row_ptr, col_idx, nullptr, nb, BH, nb, bq, pq, hs);
+    if (e != hipSuccess) return hip_status(e, "pairing offsets launch (query blocks)");
+    a.pair_dk = pk; a.bits_k = bk;
+    a.pair_dq = pq; a.bits_q = bq;
+    a.nw = (nb + 63) / 64;
+  }
   return hip_status(bsa::launch_bwd(a, dq->dtype == BSA_F32, row_ptr, col_idx, col_ptr, row_idx, ld, hs),
                     "backward launch");
 }

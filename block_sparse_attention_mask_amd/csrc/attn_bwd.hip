@@ -124,7 +124,7 @@ __device__ __forceinline__ bf16x8_t pack8(const float* x) {
 //     are read with transposing LDS reads (the forward's P V step with the query
 //     index contracted).
 // The two query halves' partial dK^T, dV^T are summed through LDS at the end.
-template <int D, bool F32>
+template <int D, bool F32, bool BITS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
                      const float2* __restrict__ ld) {
@@ -150,15 +150,18 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
     // would not fit in smem)
     const int head0 = lin / npair * npair;
     lin = kth_longest_item<512>([&](int r) { return col_ptr[r + 1] - col_ptr[r]; }, a.nb, (int*)smem, head0,
-                                npair, lin - head0);
+                                npair, lin - head0, a.pair_dk);
   }
-  const int bh = lin / npair, jA = 2 * (lin % npair);
+  const int bh = lin / npair;
   const int b = bh / a.H, h = bh % a.H;
-  const bool hasB = jA + 1 < a.nb;
+  // the pair's two key blocks: adjacent, or at the head's pairing offset
+  const int2 pb = pair_blocks(lin % npair, a.pair_dk ? a.pair_dk[bh] : 1, a.nb);
+  const int jA = pb.x, jB = pb.y;
+  const bool hasB = jB >= 0;
   const int sA = col_ptr[bh * a.nb + jA], eA = col_ptr[bh * a.nb + jA + 1];
-  const int sB = hasB ? col_ptr[bh * a.nb + jA + 1] : 0, eB = hasB ? col_ptr[bh * a.nb + jA + 2] : 0;
+  const int sB = hasB ? col_ptr[bh * a.nb + jB] : 0, eB = hasB ? col_ptr[bh * a.nb + jB + 1] : 0;
   const bool mine_valid = kb == 0 || hasB;
-  const int j = mine_valid ? jA + kb : jA;          // this wave's key block
+  const int j = mine_valid && kb ? jB : jA;         // this wave's key block
 
   const char* qbase = (const char*)a.q + (b * a.q_sb + h * a.q_sh) * 2;
   const char* dobase = (const char*)a.d_o + (b * a.do_sb + h * a.do_sh) * 2;
@@ -172,7 +175,7 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
     const unsigned k_rs = (unsigned)(a.k_ss * 2), v_rs = (unsigned)(a.v_ss * 2);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      const int jx = x && hasB ? jA + 1 : jA;
+      const int jx = x && hasB ? jB : jA;
       load_tile_part<RB, false, 8>(kbase + (int64_t)jx * 64 * k_rs, k_rs, (unsigned)(uintptr_t)(lds + KV0 + 2 * x * KT),
                                    l, wave);
       load_tile_part<RB, false, 8>(vbase + (int64_t)jx * 64 * v_rs, v_rs,
@@ -199,13 +202,20 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
     if (wave == 0) dma16((const char*)(ldb + (int64_t)i * 64), (unsigned)l * 16u, (unsigned)(uintptr_t)(sl + 2 * KT));
   };
 
-  // union walk over the two query-block lists (wave-uniform scalar state)
+  // union walk over the two query-block lists (wave-uniform scalar state), or over their
+  // bit rows
   int ia = sA, ib = sB, cbA = sA, cbB = sB, cacheA = 0, cacheB = 0;
   auto fetch = [&](int base, int e, int& cache) { cache = row_idx[min(base + l, e - 1)]; };
-  if (sA < eA) fetch(cbA, eA, cacheA);
-  if (sB < eB) fetch(cbB, eB, cacheB);
+  BitUnionWalk bw;
+  if constexpr (BITS) {
+    bw.init(a.bits_k, (int64_t)bh * a.nb + jA, hasB ? (int64_t)bh * a.nb + jB : -1, a.nw);
+  } else {
+    if (sA < eA) fetch(cbA, eA, cacheA);
+    if (sB < eB) fetch(cbB, eB, cacheB);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   auto next_entry = [&](int& flags) -> int {
+    if constexpr (BITS) return bw.next(flags);
     const int BIG = 0x7fffffff;
     if (ia < eA && ia - cbA == 64) { cbA += 64; fetch(cbA, eA, cacheA); __builtin_amdgcn_s_waitcnt(0); }
     if (ib < eB && ib - cbB == 64) { cbB += 64; fetch(cbB, eB, cacheB); __builtin_amdgcn_s_waitcnt(0); }
@@ -349,7 +359,7 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
 //   * P^T = exp2(S^T scale log2e - lse2), dS^T = P^T (dP^T - delta), packed to bf16;
 //   * dQ^T += K^T dS^T with K^T read by transposing LDS reads (the K tile is
 //     V-swizzled for that; V is read by rows only and is K-swizzled).
-template <int D, bool F32>
+template <int D, bool F32, bool BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                    const float2* __restrict__ ld) {
@@ -372,15 +382,17 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     // would not fit in smem)
     const int head0 = lin / npair * npair;
     lin = kth_longest_item<256>([&](int r) { return row_ptr[r + 1] - row_ptr[r]; }, a.nb, (int*)smem, head0,
-                                npair, lin - head0);
+                                npair, lin - head0, a.pair_dq);
   }
   const int bh = lin / npair, pidx = lin % npair;
   const int b = bh / a.H, h = bh % a.H;
-  const int iA = 2 * pidx, iB = 2 * pidx + 1;
-  const bool hasB = iB < a.nb;
-  const int rowA = bh * a.nb + iA;
+  // the pair's two query blocks: adjacent, or at the head's pairing offset
+  const int2 pb = pair_blocks(pidx, a.pair_dq ? a.pair_dq[bh] : 1, a.nb);
+  const int iA = pb.x, iB = pb.y;
+  const bool hasB = iB >= 0;
+  const int rowA = bh * a.nb + iA, rowB = bh * a.nb + iB;
   const int sA = row_ptr[rowA], eA = row_ptr[rowA + 1];
-  const int sB = hasB ? row_ptr[rowA + 1] : 0, eB = hasB ? row_ptr[rowA + 2] : 0;
+  const int sB = hasB ? row_ptr[rowB] : 0, eB = hasB ? row_ptr[rowB + 1] : 0;
   const int i = pr ? iB : iA;
   const bool mine_valid = pr == 0 || hasB;
 
@@ -409,13 +421,19 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
   const float2 lq = ld[(int64_t)bh * a.S + qtok];
   const float lse2 = lq.x, delta = lq.y, c2 = a.scale_log2;
 
-  // union walk over the two kv lists (the forward's)
+  // union walk over the two kv lists (the forward's), or over their bit rows
   int ia = sA, ib = sB, cbA = sA, cbB = sB, cacheA = 0, cacheB = 0;
   auto fetch = [&](int base, int e, int& cache) { cache = col_idx[min(base + l, e - 1)]; };
-  if (sA < eA) fetch(cbA, eA, cacheA);
-  if (sB < eB) fetch(cbB, eB, cacheB);
+  BitUnionWalk bw;
+  if constexpr (BITS) {
+    bw.init(a.bits_q, rowA, hasB ? (int64_t)rowB : -1, a.nw);
+  } else {
+    if (sA < eA) fetch(cbA, eA, cacheA);
+    if (sB < eB) fetch(cbB, eB, cacheB);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   auto next_entry = [&](int& flags) -> int {
+    if constexpr (BITS) return bw.next(flags);
     const int BIG = 0x7fffffff;
     if (ia < eA && ia - cbA == 64) { cbA += 64; fetch(cbA, eA, cacheA); __builtin_amdgcn_s_waitcnt(0); }
     if (ib < eB && ib - cbB == 64) { cbB += 64; fetch(cbB, eB, cacheB); __builtin_amdgcn_s_waitcnt(0); }
@@ -537,12 +555,13 @@ template <int D, bool F32>
 static hipError_t launch_bwd_t(const BwdArgs& a, const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* col_ptr, const int32_t* row_idx, const float2* ld, hipStream_t st) {
   const int npair = a.B * a.H * ((a.nb + 1) / 2);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32>), dim3((npair + BSA_NXCD - 1) / BSA_NXCD * BSA_NXCD), dim3(512), 0, st,
-                     a, col_ptr, row_idx, ld);
+  const dim3 grid((npair + BSA_NXCD - 1) / BSA_NXCD * BSA_NXCD);
+  if (a.bits_k) hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, true>), grid, dim3(512), 0, st, a, col_ptr, row_idx, ld);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, false>), grid, dim3(512), 0, st, a, col_ptr, row_idx, ld);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, F32>), dim3((npair + BSA_NXCD - 1) / BSA_NXCD * BSA_NXCD), dim3(256), 0, st,
-                     a, row_ptr, col_idx, ld);
+  if (a.bits_q) hipLaunchKernelGGL((bwd_dq_kernel<D, F32, true>), grid, dim3(256), 0, st, a, row_ptr, col_idx, ld);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, F32, false>), grid, dim3(256), 0, st, a, row_ptr, col_idx, ld);
   return hipGetLastError();
 }
 

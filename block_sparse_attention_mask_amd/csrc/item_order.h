@@ -19,6 +19,37 @@ __host__ __device__ inline int2 pair_blocks(int p, int d, int nb) {
   return make_int2(a, a + 1 < nb ? a + 1 : -1);
 }
 
+// Union walk over the bit rows of two kv lists (word w of a row holds the row's blocks
+// 64 w .. 64 w + 63): ascending blocks of either row with use flags (bit 0: row a holds
+// the block, bit 1: row b), -1 at the end. Wave-uniform scalar state; one scalar load per
+// word of each row.
+struct BitUnionWalk {
+  using CU64 = const uint64_t __attribute__((address_space(4)));
+  CU64* ra;
+  CU64* rb;   // NULL: no second row
+  int nw, wi;
+  uint64_t ca, cb;
+  __device__ void init(const uint64_t* bits, int64_t row_a, int64_t row_b, int nw_) {
+    nw = nw_;
+    ra = (CU64*)(uintptr_t)(bits + row_a * nw);
+    rb = row_b >= 0 ? (CU64*)(uintptr_t)(bits + row_b * nw) : nullptr;
+    wi = -1;
+    ca = cb = 0;
+  }
+  __device__ int next(int& flags) {
+    while ((ca | cb) == 0) {
+      if (++wi >= nw) { flags = 0; return -1; }
+      ca = ra[wi];
+      cb = rb ? rb[wi] : 0ull;
+    }
+    const int t = __builtin_ctzll(ca | cb);
+    flags = (int)((ca >> t) & 1ull) | (int)(((cb >> t) & 1ull) << 1);
+    ca &= ~(1ull << t);
+    cb &= ~(1ull << t);
+    return 64 * wi + t;
+  }
+};
+
 // Item it = (head, pair p) costs the longer of the pair's two lists (rows of
 // pair_blocks(p, d) of head it / npair, d = pair_d[head], or 1 without pair_d), clamped
 // to [0, nb].

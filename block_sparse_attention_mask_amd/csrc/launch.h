@@ -181,6 +181,11 @@ struct BwdArgs {
   float scale;           // softmax scale
   float scale_log2;      // scale * log2(e)
   int derive_order;      // 1: longest first inside each head (kv-list lengths), else natural order
+  // pairing offsets of the key-block pairs (dK/dV, from the transposed lists) and of the
+  // query-block pairs (dQ, from the kv lists), [B*H] each, or NULL for adjacent pairs; with
+  // them the bit rows of those lists ([rows][nw]), which the walks then read
+  const int32_t* pair_dk; const int32_t* pair_dq;
+  const uint64_t* bits_k; const uint64_t* bits_q; int nw;
 };
 // (lse2, delta) per query into ld [B*H*S (+64 entries of padding read by the tile copies)]
 hipError_t launch_bwd_prep(const BwdArgs& a, float2* ld, hipStream_t st);
