@@ -140,3 +140,36 @@ def test_chunked_lists_entry_and_workspace(gpu_lib, chunked):
     b = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=cfg.S_valid)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_chunked_with_pairing_offsets(gpu_lib, chunked):
+    """Rows long enough for pairing offsets (nb = 600, lists alike one offset apart): the
+    chunked walk over offset pairs writes every block, matches the oracle on sampled blocks
+    and the whole-row walk within the tolerances."""
+    B, H, nb, D = 1, 2, 600, 128
+    S = nb * 64
+    sv = S - 30
+    rng = np.random.default_rng(600)
+    keep = np.zeros((B, H, nb, nb), bool)
+    for h, d in enumerate((55, 1)):
+        base = rng.random((d, nb)) < 0.08
+        keep[0, h] = base[np.arange(nb) % d]
+        keep[0, h, np.arange(nb), np.arange(nb)] = True
+    mask = torch.from_numpy(keep.astype(np.uint8)).to(DEV)
+    g = torch.Generator(device="cpu").manual_seed(600)
+    q, k, v = (torch.randn(B, H, S, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    rp, ci = gpu_lib.mask_to_csr(mask)
+    assert gpu_lib.attn_pair_offsets(q, rp, ci, s_valid=sv).tolist() == [55, 1]
+    chunked(64)
+    out = torch.full_like(v, float("nan"))
+    out = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=sv, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    blocks = [(0, h, i) for h in range(H) for i in (0, 1, 54, 55, 56, 299, 598, 599)]
+    mx, mean = attention_errors(out, oracle_attention_blocks(q, k, v, keep, blocks, sv))
+    print(f"[chunked + pairing] max err {mx:.3e} mean err {mean:.3e}", flush=True)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
+    chunked(0)
+    whole = gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=sv)
+    torch.cuda.synchronize()
+    assert (out.float() - whole.float()).abs().mean().item() <= MEAN_ERR
