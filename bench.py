@@ -604,6 +604,9 @@ def main():
                     help="time the backward pass (dq, dk, dv) of the config instead of the forward step")
     ap.add_argument("--sweep", action="store_true",
                     help="threshold sweep of the config (default 5) with bf16 and fp8 Q/K: table, not the bench line")
+    ap.add_argument("--kv-chunk", type=int, default=0, metavar="W",
+                    help="attention over the kv-chunked walk with chunks of W key blocks (bsa_set_attn_kv_chunk); "
+                         "attn_ms then includes the combine launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -643,6 +646,9 @@ def main():
     from synth import get_config
     cfg = get_config(args.config)
     thr = args.thr if args.thr is not None else (cfg.thrs[0] if cfg.thrs else None)
+    if args.kv_chunk:
+        import block_sparse_attention_mask_amd as bsa
+        bsa.set_attn_kv_chunk(args.kv_chunk)
     r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=args.graph,
                 csr_step=args.csr_step, dense_reps=args.dense_reps)
     fpt = _flops_per_tile(cfg.D)
@@ -666,7 +672,7 @@ def main():
                    "grid": list(cfg.grid), "token_order": cfg.order, "thr": thr,
                    "sta": None if cfg.sta is None else {"tile": list(cfg.sta.tile), "window": list(cfg.sta.window)},
                    "dense": args.dense, "fp8_qk": args.fp8,
-                   "launch": "hip_graph" if args.graph else "eager"},
+                   "launch": "hip_graph" if args.graph else "eager", "kv_chunk": args.kv_chunk or None},
         "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
         "kv_lists": r["kv_lists"],
         # per-step spread and phase times from the eager pass with events between the phases
@@ -683,7 +689,7 @@ def main():
         "attn_launches": r["attn_launches"],
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4),
-                     "traffic": _measured_traffic(cfg.name, args.fp8, args.dense),
+                     "traffic": None if args.kv_chunk else _measured_traffic(cfg.name, args.fp8, args.dense),
                      "kernel": "attn_fwd_kernel", "per_launch_flops": kept_flops},
     }
     if r["dense_ms"]:
