@@ -25,8 +25,9 @@ DEV = "cuda"
 THRS = (0.0, 0.05, 0.1, 0.2, 0.4, 0.7, 0.95)
 
 
-def test_mask_monotone_in_thr_and_covers_mass(gpu_lib):
-    cfg = get_config(2, heads=4)
+@pytest.mark.parametrize("cid,heads", [(2, 4), (3, 2)])   # short rows (nb 128) and long rows (nb 1182)
+def test_mask_monotone_in_thr_and_covers_mass(gpu_lib, cid, heads):
+    cfg = get_config(cid, heads=heads)
     q, k, _ = make_inputs(cfg, seed=11, device=DEV)
     P = oracle_probs(q, k)
     prev = None
@@ -96,10 +97,11 @@ def test_attention_rows_are_convex_combinations(gpu_lib, cid, heads):
     print(f"[invariants] {cfg.name}: {len(blocks)} blocks x {cfg.H} heads inside their V boxes", flush=True)
 
 
-def test_mask_rows_nonempty_and_separated(gpu_lib):
+@pytest.mark.parametrize("cid,heads", [(2, 4), (3, 2)])
+def test_mask_rows_nonempty_and_separated(gpu_lib, cid, heads):
     """Every row keeps its top block; no dropped block outweighs a kept one, up to flagged
     (near-threshold) blocks."""
-    cfg = get_config(2, heads=4)
+    cfg = get_config(cid, heads=heads)
     q, k, _ = make_inputs(cfg, seed=14, device=DEV)
     P = oracle_probs(q, k)
     for thr in THRS:

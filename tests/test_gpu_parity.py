@@ -734,9 +734,9 @@ def test_near_threshold_flags_random(gpu_lib, cid, heads):
 
 @pytest.mark.parametrize("nb", [257, 700, 1216, 1217])
 def test_long_row_select_bounds(gpu_lib, nb):
-    """Rows past the short-row limit: nb 257 .. 1216 take the select that keeps the 16-row map
-    strip in shared memory (one wave per row, 6-bit digits), nb 1217 the register-resident
-    one. Thresholds (0 keeps every block with mass), Top-k and an OR'd plane; D 128 and 64."""
+    """Rows past the short-row limit (nb > 256) take the register-resident select: 3 column
+    tiles per wave at nb 257, 6 at 700, 10 at 1216 and 1217 (a ragged last tile). Thresholds
+    (0 keeps every block with mass), Top-k and an OR'd plane; D 128 and 64."""
     from dataclasses import replace
     for D in (128, 64):
         cfg = replace(get_config(3, heads=2), cid=9, name=f"long-{nb}", grid=(1, nb, 64), D=D)
@@ -763,3 +763,34 @@ def test_long_row_select_bounds(gpu_lib, nb):
                 diff = mt[0, h].cpu().numpy().astype(bool) != ref
                 kth = -np.sort(-P, axis=1)[:, topk - 1]
                 assert not (diff & ~(np.abs(P - kth[:, None]) <= 2.0 ** -59)).any(), (topk, h)
+
+
+def test_long_row_select_exact_ties(gpu_lib):
+    """Long rows (nb = 300) whose key blocks repeat in threes: every reduced-map value occurs
+    three times exactly, so the pivot's bucket holds tied keys that only the column index
+    orders (descending p, then ascending index); in head 1 (q = 0) all 300 entries of a row
+    tie. Thresholds and Top-k counts that fall inside a tie group."""
+    from dataclasses import replace
+    nb = 300
+    cfg = replace(get_config(3, heads=2), cid=9, name="ties-300", grid=(1, nb, 64), D=128)
+    q, k, _ = make_inputs(cfg, seed=77, device=DEV)
+    kb = k.view(cfg.B, cfg.H, nb, 64, cfg.D)
+    kb[:, :, 100:200] = kb[:, :, 0:100]
+    kb[:, :, 200:300] = kb[:, :, 0:100]
+    q[:, 1] = 0   # head 1: every entry of a row ties (more than a gathered bucket holds)
+    for thr in (0.02, 0.05, 0.2, 0.5):
+        m = gpu_lib.nabla_build_mask(q, k, thr)
+        torch.cuda.synchronize()
+        keep, E = oracle_masks(q, k, thr)
+        bad, near = compare_masks(m, keep, E, thr)
+        print(f"[ties] thr {thr}: mismatches {bad}, near {near}, kept {keep.mean():.4f}", flush=True)
+        assert bad == 0
+    for topk in (1, 2, 50, 100, 151):
+        mt = gpu_lib.nabla_build_mask_topk(q, k, topk)
+        torch.cuda.synchronize()
+        for h in range(cfg.H):
+            ref, P = oracle.topk_mask(f64(q[0, h]), f64(k[0, h]), 64, topk)
+            diff = mt[0, h].cpu().numpy().astype(bool) != ref
+            kth = -np.sort(-P, axis=1)[:, topk - 1]   # entries within 2^-59 of the k-th may swap
+            assert not (diff & ~(np.abs(P - kth[:, None]) <= 2.0 ** -59)).any(), (topk, h)
+            assert np.all(mt[0, h].sum(dim=-1).cpu().numpy() == topk)
