@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (published)
 FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (published)
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E (published)
+PEAK_CLOCK_MHZ = 2400.0        # the engine clock the published MFMA peaks are quoted at
 LLC_BYTES = 256 << 20           # MI355X last-level (Infinity) cache
 
 
@@ -213,12 +214,15 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
         torch.cuda.synchronize()
         return p0.elapsed_time(p1) / steps
 
-    mask_ms, csr_ms, attn_ms = phase_ms(phase_mask), phase_ms(phase_csr), phase_ms(phase_attn)
+    mask_ms, csr_ms = phase_ms(phase_mask), phase_ms(phase_csr)
+    with _SclkSampler() as clk_attn:      # the shader clock while the attention repeats run
+        attn_ms = phase_ms(phase_attn)
     kept = int(rp.sum().item()) if fused else int(rp[-1].item())
     # attention launches so far (warm-ups, timed steps, the eager pass, the phase repeats);
     # a kernel trace of this run splits its attention dispatches at this count
     n_attn = warmup + (1 if graph else 0) + steps + steps + steps + 1
     dense_ms = None
+    clk_dense = None
     if dense_reps and not dense:
         # dense attention of the same shape: the same kernel and call over an all-ones mask,
         # after the sparse launches (one warm-up, then dense_reps timed back to back)
@@ -234,18 +238,71 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
         dense_attn()
         torch.cuda.synchronize()
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record()
-        for _ in range(dense_reps):
-            dense_attn()
-        d1.record()
-        torch.cuda.synchronize()
+        with _SclkSampler() as clk_dense:
+            d0.record()
+            for _ in range(dense_reps):
+                dense_attn()
+            d1.record()
+            torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / dense_reps
     return dict(ms_per_step=ms_total / steps, wall_s=wall, mask_ms=mask_ms, csr_ms=csr_ms, attn_ms=attn_ms,
-                dense_ms=dense_ms, attn_launches={"sparse": n_attn, "dense": (1 + dense_reps) if dense_ms else 0},
+                dense_ms=dense_ms, sclk_attn=clk_attn.summary(), sclk_dense=clk_dense.summary() if clk_dense else None,
+                attn_launches={"sparse": n_attn, "dense": (1 + dense_reps) if dense_ms else 0},
                 eager_phase_ms=eager_ms, kv_lists="from the mask build" if fused else "compaction launch",
                 step_ms_median=per_step[len(per_step) // 2], step_ms_min=per_step[0],
                 kept_tiles=kept, kept_fraction=kept / (cfg.B * cfg.H * nb * nb), mask=m.cpu() if use_nabla else None,
                 q=q, k=k, v=v, qa=qa, ka=ka, qs=qs, ks=ks)
+
+
+class _SclkSampler:
+    """Samples the shader clock the driver reports (pp_dpm_sclk, the starred level) from a host
+    thread while the block runs; summary() gives the median, min and max in MHz of the card
+    with the highest median (the busy one), or None where the file is not readable."""
+
+    def __init__(self, period_s=0.02):
+        import glob
+        self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = {f: [] for f in self.files}
+
+    def _read(self, f):
+        try:
+            with open(f) as fh:
+                for ln in fh:
+                    if "*" in ln:
+                        return float(ln.split(":", 1)[1].lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            for f in self.files:
+                v = self._read(f)
+                if v is not None:
+                    self.samples[f].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._loop, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        best = None
+        for f, v in self.samples.items():
+            if v:
+                v = sorted(v)
+                cur = {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
+                if best is None or cur["median"] > best["median"]:
+                    best = cur
+        return best
 
 
 def _cpu_model():
@@ -700,6 +757,17 @@ def main():
                          "speedup_step_vs_dense": round(r["dense_ms"] / r["ms_per_step"], 3),
                          "speedup_attn_vs_dense": round(r["dense_ms"] / r["attn_ms"], 3),
                          "reps": args.dense_reps}
+    # The published peaks assume the 2400 MHz peak engine clock; the clock the part holds
+    # under this load is lower, and the MFMA rate scales with it.
+    if r["sclk_attn"]:
+        ca = r["sclk_attn"]
+        sc = {"source": "pp_dpm_sclk", "peak_assumes_mhz": PEAK_CLOCK_MHZ,
+              "attn_mhz": ca, "attn_frac_of_peak_at_clock": round(attn_tflops / (peak * ca["median"] / PEAK_CLOCK_MHZ), 4)}
+        if r["dense_ms"] and r["sclk_dense"]:
+            cd = r["sclk_dense"]
+            sc["dense_mhz"] = cd
+            sc["dense_frac_of_peak_at_clock"] = round(line["dense"]["tflops"] / (peak * cd["median"] / PEAK_CLOCK_MHZ), 4)
+        line["shader_clock"] = sc
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(cfg, None if args.dense else thr)
     print(json.dumps(line), flush=True)
