@@ -13,7 +13,8 @@ pages by eye:
   attention.py  softmax attention restricted to the kept N x N blocks
   attention_bwd.py  its gradients dQ, dK, dV (plain derivative of the same definition)
   csr.py        union of masks and the per-query-block kv index lists
-  fp8.py        e4m3fn encoding and per-block fp8 quantisation of Q and K
+  fp8.py        e4m3fn encoding and per-block fp8 quantisation of Q and K (optionally after
+                the randomised Hadamard rotation of incoherent processing)
   reorder.py    token orders (tile-major / fractal flattening, spatial-major) and reordering
 
 Pins: every function is checked by `tests/test_oracle_*.py` against closed forms,
@@ -24,7 +25,7 @@ from .sta import sta_block_mask, sta_token_mask
 from .attention import block_sparse_attention
 from .attention_bwd import block_sparse_attention_bwd
 from .csr import mask_or, mask_to_csr, longest_first_order
-from .fp8 import decode_e4m3fn, encode_e4m3fn, quantize_blocks
+from .fp8 import decode_e4m3fn, encode_e4m3fn, fwht_rows, quantize_blocks, quantize_blocks_rotated
 from .reorder import order_coords, reorder_tokens
 
 __all__ = ["block_pool", "reduced_map", "row_softmax", "cdf_select", "nabla_mask", "topk_select", "topk_mask",

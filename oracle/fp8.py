@@ -12,6 +12,16 @@ is divided by the scale in fp32 (correctly rounded) and encoded round-to-nearest
 (ties to the code with an even mantissa), saturating at +-448. Both the rounding of
 the quotient and the choice of the code are taken in fp32, the precision the GPU
 takes them in.
+
+Incoherent processing (FlashAttention-3 abstract, Daily Papers listing, named beside block
+quantisation with no formula; reading): Q and K are multiplied by the same orthogonal
+matrix M = diag(s) H / sqrt(D) before quantisation, H the D x D Sylvester Hadamard matrix
+and s a vector of random signs that the caller draws, so that Q M (K M)^T = Q K^T while
+a few large channels are spread over all of them. Each row x becomes y = H (s . x),
+formed by the fast Walsh-Hadamard transform in fp32 (stages of stride 1, 2, ..., D/2,
+each pair (i, i + stride) -> (a + b, a - b)), the order and precision the GPU uses, so
+that both sides take the same fp8 codes; the 1/D of M M^T is carried by the key side's
+scales (a power of two, exact).
 """
 import numpy as np
 
@@ -67,4 +77,30 @@ def quantize_blocks(x, n: int = 64):
     scales = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
     q = (blk / scales[..., None, None]).astype(np.float32)
     codes = encode_e4m3fn(q).reshape(*lead, S, D)
+    return codes, scales
+
+
+def fwht_rows(x, signs) -> np.ndarray:
+    """y = H (s . x) for every row of x [..., D] (D a power of two), in fp32 with the stage
+    order stated above."""
+    y = (np.asarray(x, dtype=np.float32) * np.asarray(signs, dtype=np.float32)).astype(np.float32)
+    D = y.shape[-1]
+    assert D & (D - 1) == 0, "D must be a power of two"
+    h = 1
+    while h < D:
+        v = y.reshape(*y.shape[:-1], D // (2 * h), 2, h)
+        a, b = v[..., 0, :], v[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(*y.shape[:-1], D).astype(np.float32)
+        h *= 2
+    return y
+
+
+def quantize_blocks_rotated(x, signs, key_side: bool, n: int = 64):
+    """Incoherent processing then block quantisation: codes and scales of fwht_rows(x, s);
+    on the key side the scales also carry the 1/D of M M^T, so that dequantised q . k
+    equals q . k of the unrotated rows."""
+    y = fwht_rows(x, signs)
+    codes, scales = quantize_blocks(y, n)
+    if key_side:
+        scales = (scales * np.float32(1.0 / y.shape[-1])).astype(np.float32)
     return codes, scales

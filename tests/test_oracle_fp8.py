@@ -8,7 +8,8 @@ properties; the block quantiser against its defining properties.
 import numpy as np
 import torch
 
-from oracle.fp8 import decode_e4m3fn, e4m3fn_values, encode_e4m3fn, quantize_blocks
+from oracle.fp8 import (decode_e4m3fn, e4m3fn_values, encode_e4m3fn, fwht_rows, quantize_blocks,
+                        quantize_blocks_rotated)
 
 
 def _torch_codes(x32: np.ndarray) -> np.ndarray:
@@ -83,3 +84,72 @@ def test_block_quantiser_equals_torch_reference_path():
     tq = (xf / ts[..., None, None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(1, 2, 192, 128)
     assert np.array_equal(scales, ts.numpy())
     assert np.array_equal(codes, tq.numpy())
+
+
+# --------------------------------------------------------------------------- incoherent processing
+def test_fwht_equals_the_hadamard_matrix_product():
+    """fwht_rows(x, s) = H (s . x) with H from scipy's Sylvester construction (computed in
+    fp64 there): equal up to the fp32 rounding of the butterflies."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(0)
+    for D in (2, 8, 64, 128):
+        x = rng.normal(0.0, 1.0, (5, D)).astype(np.float32)
+        s = rng.choice([-1.0, 1.0], D)
+        ref = (x.astype(np.float64) * s) @ hadamard(D).T.astype(np.float64)
+        got = fwht_rows(x, s).astype(np.float64)
+        assert np.allclose(got, ref, rtol=0, atol=1e-5 * np.sqrt(D) * np.abs(x).max())
+
+
+def test_fwht_special_rows_and_orthogonality():
+    """A unit row e_j with all signs +1 maps to column j of H (entries +-1, exact); the
+    transform with signs is orthogonal up to 1/D: <y_q, y_k> = D <q, k>, |y|^2 = D |x|^2."""
+    from scipy.linalg import hadamard
+    D = 64
+    Hm = hadamard(D)
+    for j in (0, 1, 17, 63):
+        e = np.zeros((1, D), dtype=np.float32)
+        e[0, j] = 1.0
+        assert np.array_equal(fwht_rows(e, np.ones(D))[0], Hm[:, j].astype(np.float32))
+    rng = np.random.default_rng(1)
+    s = rng.choice([-1.0, 1.0], D)
+    q = rng.normal(0.0, 1.0, (7, D)).astype(np.float32)
+    k = rng.normal(0.0, 1.0, (7, D)).astype(np.float32)
+    yq, yk = fwht_rows(q, s).astype(np.float64), fwht_rows(k, s).astype(np.float64)
+    assert np.allclose(yq @ yk.T, D * (q.astype(np.float64) @ k.astype(np.float64).T), rtol=1e-5, atol=1e-4)
+    assert np.allclose((yq ** 2).sum(1), D * (q.astype(np.float64) ** 2).sum(1), rtol=1e-5)
+
+
+def test_rotated_quantisation_lowers_attention_error_with_outliers():
+    """The point of the rotation (FlashAttention-3 abstract: lower fp8 error than a plain fp8
+    attention): Gaussian Q, K, V with 1% of the entries of Q and K scaled by 10 (outliers at
+    random places). Attention from the dequantised fp8 Q and K is compared with attention in
+    fp64 on the exact inputs; the rotated quantisation (key scales carrying the 1/D) lowers the
+    RMS error well below the plain block quantisation's, and changes nothing much on
+    Gaussian inputs without outliers."""
+    rng = np.random.default_rng(2)
+    S, D = 256, 128
+
+    def attn(q, k, v):
+        L = q @ k.T / np.sqrt(D)
+        P = np.exp(L - L.max(1, keepdims=True))
+        return (P / P.sum(1, keepdims=True)) @ v
+
+    def deq(c, sc):
+        return (decode_e4m3fn(c).reshape(-1, 64, D) * sc[:, None, None]).reshape(c.shape)
+
+    def errors(q, k, v, s):
+        ref = attn(q, k, v)
+        (cq, sq), (ck, sk) = quantize_blocks(q), quantize_blocks(k)
+        (rq, rsq), (rk, rsk) = quantize_blocks_rotated(q, s, key_side=False), quantize_blocks_rotated(k, s, key_side=True)
+        rms = lambda o: float(np.sqrt(((o - ref) ** 2).mean()))
+        return rms(attn(deq(cq, sq), deq(ck, sk), v)), rms(attn(deq(rq, rsq), deq(rk, rsk), v))
+
+    s = rng.choice([-1.0, 1.0], D)
+    q, k, v = rng.normal(0.0, 1.0, (3, S, D))
+    for x in (q, k):
+        x[rng.random(x.shape) < 0.01] *= 10.0
+    plain, rot = errors(q, k, v, s)
+    assert rot < 0.75 * plain, (plain, rot)
+    q, k, v = rng.normal(0.0, 1.0, (3, S, D))
+    plain, rot = errors(q, k, v, s)
+    assert 0.8 * plain < rot < 1.25 * plain, (plain, rot)
