@@ -52,7 +52,8 @@ def _measured_traffic(workload, fp8=False, dense=False):
     return entry["traffic_bytes_per_launch"]
 
 
-def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_step=False, dense_reps=0):
+def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_step=False, dense_reps=0,
+            rotate=False):
     import torch
     import block_sparse_attention_mask_amd as bsa
     from synth import make_inputs
@@ -68,6 +69,19 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
         qa, ka = torch.empty(q.shape, dtype=torch.uint8, device=dev), torch.empty(k.shape, dtype=torch.uint8, device=dev)
         qs = torch.empty(cfg.B, cfg.H, cfg.nb, dtype=torch.float32, device=dev)
         ks = torch.empty(cfg.B, cfg.H, cfg.nb, dtype=torch.float32, device=dev)
+    signs = None
+    if rotate:
+        # incoherent processing: random signs of the Hadamard rotation, drawn once
+        from synth import make_signs
+        signs = make_signs(cfg.D, seed=0)
+
+    def quantize_qk():
+        if rotate:
+            bsa.quantize_fp8_blocks_rotated(q, signs, False, out=(qa, qs))
+            bsa.quantize_fp8_blocks_rotated(k, signs, True, out=(ka, ks))
+        else:
+            bsa.quantize_fp8_blocks(q, out=(qa, qs))
+            bsa.quantize_fp8_blocks(k, out=(ka, ks))
     nb, S = cfg.nb, cfg.S
     use_nabla = (thr is not None) and not dense
     plane = torch.empty(nb, nb, dtype=torch.uint8, device=dev)
@@ -115,7 +129,10 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
         if cfg.sta is not None and not dense:
             bsa.sta_build_mask(S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
                                order_tile=cfg.order_tile, device=dev, out=plane)
-        if use_nabla and fp8:
+        if use_nabla and fp8 and rotate:
+            bsa.nabla_build_mask_fp8_rotated(q, k, thr, signs, or_mask=plane if cfg.sta is not None else None,
+                                             out=mask, q8_out=(qa, qs), k8_out=(ka, ks))
+        elif use_nabla and fp8:
             bsa.nabla_build_mask_fp8(q, k, thr, or_mask=plane if cfg.sta is not None else None, out=mask,
                                      q8_out=(qa, qs), k8_out=(ka, ks))
         elif use_nabla:
@@ -123,8 +140,7 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
         else:
             m = ones if dense else plane
             if fp8:
-                bsa.quantize_fp8_blocks(q, out=(qa, qs))
-                bsa.quantize_fp8_blocks(k, out=(ka, ks))
+                quantize_qk()
         st["m"] = m
 
     def phase_csr():
@@ -229,8 +245,7 @@ def run_gpu(cfg, steps, warmup, thr, dense=False, fp8=False, graph=True, csr_ste
         ones_rp, ones_ci = bsa.mask_to_csr(ones, B=cfg.B, H=cfg.H, row_ptr=row_ptr, col_idx=col_idx, ws=csr_ws)
         qd, kd = qa, ka
         if fp8:
-            bsa.quantize_fp8_blocks(q, out=(qa, qs))
-            bsa.quantize_fp8_blocks(k, out=(ka, ks))
+            quantize_qk()
 
         def dense_attn():
             bsa.block_sparse_attn_fwd_csr(qd, kd, v, ones_rp, ones_ci, s_valid=cfg.S_valid, q_scale=qs, k_scale=ks,
@@ -647,6 +662,8 @@ def main():
                          "0 skips the dense comparison")
     ap.add_argument("--thr", type=float, default=None, help="NABLA threshold (default: the config's first)")
     ap.add_argument("--fp8", action="store_true", help="fp8 e4m3 Q/K with per-block scales (config 5 run)")
+    ap.add_argument("--rotate", action="store_true",
+                    help="with --fp8: Hadamard rotation of Q and K before the quantisation (incoherent processing)")
     ap.add_argument("--dense", action="store_true", help="all-ones mask (dense comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--csr-step", action="store_true",
@@ -706,8 +723,10 @@ def main():
     if args.kv_chunk:
         import block_sparse_attention_mask_amd as bsa
         bsa.set_attn_kv_chunk(args.kv_chunk)
+    if args.rotate and not args.fp8:
+        ap.error("--rotate needs --fp8")
     r = run_gpu(cfg, args.steps, args.warmup, thr, dense=args.dense, fp8=args.fp8, graph=args.graph,
-                csr_step=args.csr_step, dense_reps=args.dense_reps)
+                csr_step=args.csr_step, dense_reps=args.dense_reps, rotate=args.rotate)
     fpt = _flops_per_tile(cfg.D)
     kept_flops = r["kept_tiles"] * fpt
     attn_tflops = kept_flops / (r["attn_ms"] * 1e-3) / 1e12
@@ -728,7 +747,7 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "S": cfg.S, "S_valid": cfg.S_valid, "D": cfg.D,
                    "grid": list(cfg.grid), "token_order": cfg.order, "thr": thr,
                    "sta": None if cfg.sta is None else {"tile": list(cfg.sta.tile), "window": list(cfg.sta.window)},
-                   "dense": args.dense, "fp8_qk": args.fp8,
+                   "dense": args.dense, "fp8_qk": args.fp8, "fp8_rotation": args.rotate,
                    "launch": "hip_graph" if args.graph else "eager", "kv_chunk": args.kv_chunk or None},
         "attn_ms": round(r["attn_ms"], 4), "mask_ms": round(r["mask_ms"], 4), "csr_ms": round(r["csr_ms"], 4),
         "kv_lists": r["kv_lists"],

@@ -23,7 +23,7 @@ _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPA
 # every function the C header declares, in declaration order
 EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_noalloc", "nabla_build_mask_topk",
            "quantize_fp8_blocks",
-           "nabla_build_mask_fp8",
+           "nabla_build_mask_fp8", "quantize_fp8_blocks_rotated", "nabla_build_mask_fp8_rotated",
            "sta_workspace_size", "sta_build_mask", "nabla_sta_workspace_size", "nabla_build_mask_sta",
            "nabla_lists_workspace_size", "nabla_build_mask_lists", "mask_or",
            "csr_workspace_size", "bsa_mask_to_csr", "bsa_mask_to_csr_ordered", "attn_workspace_size",
@@ -73,6 +73,9 @@ def load(path: Optional[str] = None):
         "nabla_build_mask_topk": (i32, [PT, PT, PS, i32, dbl, vp, i64, i64, vp, vp, sz, vp]),
         "quantize_fp8_blocks": (i32, [PT, PS, PT, vp, vp]),
         "nabla_build_mask_fp8": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, PT, vp, PT, vp, vp, sz, vp]),
+        "quantize_fp8_blocks_rotated": (i32, [PT, PS, vp, i32, PT, vp, vp]),
+        "nabla_build_mask_fp8_rotated": (i32, [PT, PT, PS, dbl, dbl, vp, i64, i64, vp, vp, vp, PT, vp, PT, vp, vp,
+                                               sz, vp]),
         "sta_workspace_size": (sz, [PS]),
         "sta_build_mask": (i32, [PS, i3, i3, i3, i32, i3, vp, vp, sz, vp]),
         "nabla_sta_workspace_size": (sz, [PS]),
@@ -284,6 +287,60 @@ def nabla_build_mask_fp8(q: torch.Tensor, k: torch.Tensor, thr: float, scale: Op
                                     ws.data_ptr(), ws.numel(), _stream(q.device)))
     if nf is not None:
         return out, nf, (q8, qs), (k8, ks)
+    return out, (q8, qs), (k8, ks)
+
+
+def _sign_words(signs, D: int):
+    """Random signs s (+1 / -1, length D) -> the header's host bit words (bit set where s = -1)."""
+    s = [float(x) for x in (signs.tolist() if hasattr(signs, "tolist") else signs)]
+    if len(s) != D or any(x not in (1.0, -1.0) for x in s):
+        raise ValueError(f"signs must be {D} values of +1 or -1")
+    words = (ctypes.c_uint64 * max(1, D // 64))()
+    for d, x in enumerate(s):
+        if x < 0:
+            words[d // 64] |= 1 << (d % 64)
+    return words
+
+
+def quantize_fp8_blocks_rotated(x: torch.Tensor, signs, key_side: bool,
+                                out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Incoherent processing, then fp8 block quantisation: codes and scales of the rows
+    H (s . x); with key_side the scales also carry 1/D."""
+    lib = load()
+    shp = _shape(x, None)
+    codes, scales = _fp8_buffers(x, out)
+    if not scales.is_contiguous() or scales.dtype != torch.float32:
+        raise ValueError("scales must be contiguous float32 [B, H, S/64]")
+    words = _sign_words(signs, x.shape[3])
+    tx, tc = _tensor(x), _tensor(codes)
+    _check(lib.quantize_fp8_blocks_rotated(ctypes.byref(tx), ctypes.byref(shp), words, 1 if key_side else 0,
+                                           ctypes.byref(tc), scales.data_ptr(), _stream(x.device)))
+    return codes, scales
+
+
+def nabla_build_mask_fp8_rotated(q: torch.Tensor, k: torch.Tensor, thr: float, signs,
+                                 scale: Optional[float] = None, or_mask: Optional[torch.Tensor] = None,
+                                 out: Optional[torch.Tensor] = None, q8_out=None, k8_out=None):
+    """nabla_build_mask plus the rotated fp8 quantisation of q (query side) and k (key side)
+    from the same read. Returns (mask, (q codes, q scales), (k codes, k scales))."""
+    lib = load()
+    B, H, S, D = q.shape
+    nb = S // 64
+    shp = _shape(q, None)
+    if out is None:
+        out = torch.empty(B, H, nb, nb, dtype=torch.uint8, device=q.device)
+    q8, qs = _fp8_buffers(q, q8_out)
+    k8, ks = _fp8_buffers(k, k8_out)
+    ws = _ws(lib.nabla_workspace_size(ctypes.byref(shp)), q.device)
+    om, osb, osh = None, 0, 0
+    if or_mask is not None:
+        om, osb, osh, _keep = _mask_strides(or_mask)
+    words = _sign_words(signs, D)
+    tq, tk, tq8, tk8 = _tensor(q), _tensor(k), _tensor(q8), _tensor(k8)
+    _check(lib.nabla_build_mask_fp8_rotated(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(shp), float(thr),
+                                            float(scale) if scale else 0.0, om, osb, osh, out.data_ptr(), None,
+                                            words, ctypes.byref(tq8), qs.data_ptr(), ctypes.byref(tk8),
+                                            ks.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device)))
     return out, (q8, qs), (k8, ks)
 
 

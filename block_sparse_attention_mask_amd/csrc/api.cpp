@@ -82,7 +82,7 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 11; }
+int bsa_abi_version(void) { return 12; }
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {
@@ -269,6 +269,53 @@ bsa_status quantize_fp8_blocks(const bsa_tensor* x, const bsa_shape* shape, cons
   return hip_status(bsa::launch_pool(x->dtype == BSA_F32, shape->D, x->ptr, xs, x->ptr, xs, shape->B, shape->H,
                                      shape->S / 64, nullptr, nullptr, &f8, (hipStream_t)stream),
                     "quantize launch");
+}
+
+// incoherent processing: the signs (host bit words) and the key side's 1/D
+static bsa_status fp8_rotation(bsa::Fp8Out* f, const uint64_t* sign_bits, const bsa_shape* shape, bool key0,
+                               bool key1) {
+  if (!sign_bits) return fail(BSA_EINVAL, "sign_bits is NULL");
+  f->rot = 1;
+  f->sbits[0] = sign_bits[0];
+  f->sbits[1] = shape->D > 64 ? sign_bits[1] : 0ull;
+  const float inv_d = 1.f / (float)shape->D;   // a power of two: exact
+  f->smul[0] = key0 ? inv_d : 1.f;
+  f->smul[1] = key1 ? inv_d : 1.f;
+  return BSA_OK;
+}
+
+bsa_status quantize_fp8_blocks_rotated(const bsa_tensor* x, const bsa_shape* shape, const uint64_t* sign_bits,
+                                       int key_side, const bsa_tensor* codes, float* scales, bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  if ((st = check_tensor("x", x, shape)) != BSA_OK) return st;
+  if (x->dtype != BSA_BF16 && x->dtype != BSA_F32) return fail(BSA_EUNSUPPORTED, "x must be bf16 or f32");
+  if ((st = check_fp8_out("codes", codes, scales, shape)) != BSA_OK) return st;
+  if (key_side != 0 && key_side != 1) return fail(BSA_EINVAL, "key_side=%d (0 query side, 1 key side)", key_side);
+  bsa::Fp8Out f8 = fp8_out(codes, scales, nullptr, nullptr);
+  if ((st = fp8_rotation(&f8, sign_bits, shape, key_side == 1, false)) != BSA_OK) return st;
+  const int64_t xs[3] = {x->sb, x->sh, x->ss};
+  return hip_status(bsa::launch_pool(x->dtype == BSA_F32, shape->D, x->ptr, xs, x->ptr, xs, shape->B, shape->H,
+                                     shape->S / 64, nullptr, nullptr, &f8, (hipStream_t)stream),
+                    "quantize launch");
+}
+
+bsa_status nabla_build_mask_fp8_rotated(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
+                                        double thr, double scale, const uint8_t* or_mask, int64_t or_sb,
+                                        int64_t or_sh, uint8_t* mask_out, uint8_t* near_thr_out,
+                                        const uint64_t* sign_bits, const bsa_tensor* q8, float* q_scale,
+                                        const bsa_tensor* k8, float* k_scale, void* ws, size_t ws_bytes,
+                                        bsa_stream_t stream) {
+  g_err.clear();
+  bsa_status st;
+  if ((st = check_shape(shape)) != BSA_OK) return st;
+  if ((st = check_fp8_out("q8", q8, q_scale, shape)) != BSA_OK) return st;
+  if ((st = check_fp8_out("k8", k8, k_scale, shape)) != BSA_OK) return st;
+  bsa::Fp8Out f8 = fp8_out(q8, q_scale, k8, k_scale);
+  if ((st = fp8_rotation(&f8, sign_bits, shape, false, true)) != BSA_OK) return st;
+  return nabla_common(q, k, shape, thr, scale, or_mask, or_sb, or_sh, mask_out, &f8, ws, ws_bytes, stream, 0,
+                      bsa::StaRule{0, 0, 0, 0, 0, 0}, nullptr, nullptr, nullptr, nullptr, near_thr_out);
 }
 
 // ---------------------------------------------------------------------------

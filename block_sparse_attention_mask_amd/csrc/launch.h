@@ -14,6 +14,12 @@ struct Fp8Out {
   uint8_t* codes[2];
   int64_t sb[2], sh[2], ss[2];
   float* scale[2];
+  // incoherent processing: rot != 0 rotates every row to H (s . x) before the
+  // quantisation (H the Sylvester Hadamard matrix, bit d of sbits set where s_d = -1)
+  // and multiplies tensor x's stored scales by smul[x] (1, or 1/D on the key side)
+  int rot;
+  uint64_t sbits[2];
+  float smul[2];
 };
 // Block means of q and k into qbar / kbarT; with f8, also their fp8 block quantisation
 // from the same read. qbar == NULL: quantisation of q alone (f8 index 0).

@@ -60,9 +60,17 @@ __device__ __forceinline__ unsigned pack_e4m3x4(float a, float b, float c, float
 // Q8: from the same registers, the block's fp8 quantisation (scale = amax / 448 in
 // fp32, codes = e4m3(x / scale)), so a run with fp8 Q/K reads Q and K once.
 // POOL = false skips the means (quantisation alone, of the tensor in q).
+// ROT (with Q8): incoherent processing (FlashAttention-3 abstract, Daily Papers listing:
+// named beside block quantisation) before the quantisation: each row x becomes
+// y = H (s . x), H the Sylvester Hadamard matrix and s the caller's random signs, by the
+// fast Walsh-Hadamard transform in fp32, butterflies (a, b) -> (a + b, a - b) at strides
+// 1, 2, ..., D/2 in that order (strides below E inside a thread, the others between the
+// lanes of the row); the amax, scale and codes are then those of y, and the stored scale
+// is multiplied by f8.smul (1/D on the key side, exact), so that dequantised codes give
+// q . k of the unrotated rows. The means are still those of the unrotated rows.
 // ----------------------------------------------------------------------------
 constexpr int POOL_BPW = 2;   // blocks per workgroup
-template <typename T, int D, bool NT, bool POOL, bool Q8>
+template <typename T, int D, bool NT, bool POOL, bool Q8, bool ROT = false>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
                                                    int64_t q_ss, const T* __restrict__ k, int64_t k_sb,
                                                    int64_t k_sh, int64_t k_ss, int H, int nb,
@@ -104,13 +112,50 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
   if constexpr (Q8) {
     __shared__ float wmax[POOL_BPW][4];
     const int lane = t & 63, wave = t >> 6;
+    // the values quantised: x itself, or its rotation y = H (s . x)
+    float rv[ROT ? POOL_BPW : 1][ROT ? PASSES : 1][ROT ? E : 1];
+    if constexpr (ROT) {
+      const int d0 = cg * E;   // first channel of this thread
+      const unsigned sgn = (unsigned)(f8.sbits[d0 >> 6] >> (d0 & 63)) & ((1u << E) - 1u);
+#pragma unroll
+      for (int bb = 0; bb < POOL_BPW; ++bb)
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+          float* y = rv[bb][ps];
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            y[e] = __uint_as_float(__float_as_uint(elem(raw[bb][ps], e)) ^ (((sgn >> e) & 1u) << 31));
+#pragma unroll
+          for (int hs = 1; hs < E; hs *= 2)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if (!(e & hs)) {
+                const float a0 = y[e], b0 = y[e + hs];
+                y[e] = a0 + b0;
+                y[e + hs] = a0 - b0;
+              }
+#pragma unroll
+          for (int m = 1; m < TPR; m *= 2) {   // stride m * E: the partner lane cg ^ m of the same row
+            const bool upper = (cg & m) != 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const float o = __shfl_xor(y[e], m, 64);
+              y[e] = upper ? o - y[e] : y[e] + o;
+            }
+          }
+        }
+    }
+    auto qval = [&](int bb, int ps, int e) -> float {
+      if constexpr (ROT) return rv[bb][ps][e];
+      else return elem(raw[bb][ps], e);
+    };
 #pragma unroll
     for (int bb = 0; bb < POOL_BPW; ++bb) {
       float m = 0.f;
 #pragma unroll
       for (int ps = 0; ps < PASSES; ++ps)
 #pragma unroll
-        for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(elem(raw[bb][ps], e)));
+        for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(qval(bb, ps, e)));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       if (lane == 0) wmax[bb][wave] = m;
@@ -126,7 +171,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
       // 2^-100 <= amax <= 2^100 the quotient is formed as q = x r with r = 1 / sc and one FMA
       // correction q + (x - q sc) r (Markstein), which gives the same code for every bf16 x <= amax
       // (checked exhaustively on the host: 4.2e8 pairs); elsewhere the division itself is used.
-      const bool recip = sizeof(T) == 2 && amax >= 0x1p-100f && amax <= 0x1p100f;
+      // (Rotated values are fp32 sums, not bf16: they always take the division.)
+      const bool recip = !ROT && sizeof(T) == 2 && amax >= 0x1p-100f && amax <= 0x1p100f;
       const float r = 1.f / sc;
       auto quot = [&](float x) -> float {
         if (!recip) return x / sc;
@@ -139,13 +185,13 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
         unsigned w[E / 4];
 #pragma unroll
         for (int x = 0; x < E / 4; ++x)
-          w[x] = pack_e4m3x4(quot(elem(raw[bb][ps], 4 * x)), quot(elem(raw[bb][ps], 4 * x + 1)),
-                             quot(elem(raw[bb][ps], 4 * x + 2)), quot(elem(raw[bb][ps], 4 * x + 3)));
+          w[x] = pack_e4m3x4(quot(qval(bb, ps, 4 * x)), quot(qval(bb, ps, 4 * x + 1)),
+                             quot(qval(bb, ps, 4 * x + 2)), quot(qval(bb, ps, 4 * x + 3)));
         uint8_t* dst = cbase + ((int64_t)i * BSA_N + r0 + ps * RPP) * f8.ss[which] + cg * E;
         if constexpr (E == 8) *(uint2*)dst = make_uint2(w[0], w[1]);
         else *(unsigned*)dst = w[0];
       }
-      if (t == 0) f8.scale[which][(int64_t)bh * nb + i] = sc;
+      if (t == 0) f8.scale[which][(int64_t)bh * nb + i] = ROT ? sc * f8.smul[which] : sc;
     }
   }
   if constexpr (!POOL) return;
@@ -821,6 +867,12 @@ static void launch_pool_v(dim3 grid, hipStream_t st, const void* q, const int64_
   if (!f8)
     hipLaunchKernelGGL((pool_kernel<T, D, NT, true, false>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1],
                        qs[2], (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT, none);
+  else if (f8->rot && qbar)
+    hipLaunchKernelGGL((pool_kernel<T, D, NT, true, true, true>), grid, dim3(256), 0, st, (const T*)q, qs[0],
+                       qs[1], qs[2], (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT, *f8);
+  else if (f8->rot)
+    hipLaunchKernelGGL((pool_kernel<T, D, NT, false, true, true>), grid, dim3(256), 0, st, (const T*)q, qs[0],
+                       qs[1], qs[2], (const T*)q, qs[0], qs[1], qs[2], H, nb, nullptr, nullptr, *f8);
   else if (qbar)
     hipLaunchKernelGGL((pool_kernel<T, D, NT, true, true>), grid, dim3(256), 0, st, (const T*)q, qs[0], qs[1],
                        qs[2], (const T*)k, ks[0], ks[1], ks[2], H, nb, qbar, kbarT, *f8);

@@ -175,6 +175,38 @@ bsa_status nabla_build_mask_fp8(const bsa_tensor* q, const bsa_tensor* k, const 
                                 void* ws, size_t ws_bytes, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Incoherent processing before the fp8 block quantisation [FA3 abstract: named
+ * beside block quantisation as the means of lowering the fp8 error; the pages give no
+ * formula, so this is a reading]. Q and K are both multiplied by the orthogonal matrix
+ * M = diag(s) H / sqrt(D), H the D x D Sylvester Hadamard matrix and s a vector of
+ * random signs the caller draws: Q M (K M)^T = Q K^T, while a few large channels are
+ * spread over all D of them, so the block amax (and the quantisation step) shrinks.
+ * Each row x is rotated to y = H (s . x), computed in fp32 by the fast Walsh-Hadamard
+ * transform, butterflies (a, b) -> (a + b, a - b) at strides 1, 2, ..., D/2 in that
+ * order; y is then quantised exactly as by quantize_fp8_blocks (amax, scale, codes of
+ * y). The 1/D of M M^T is carried by the KEY side's stored scales (scale / D, exact:
+ * D is a power of two), so block_sparse_attn_fwd on the codes with q_scale, k_scale
+ * computes the attention of the unrotated Q and K. V is not rotated.
+ *
+ * sign_bits: HOST array of D/64 words (one for D = 64, two for D = 128); bit (d % 64)
+ *   of word d / 64 is set where s_d = -1. Read during the call; not retained.
+ * quantize_fp8_blocks_rotated: one tensor; key_side = 0 (query side, scales as
+ *   computed) or 1 (key side, scales / D). Otherwise as quantize_fp8_blocks.
+ * nabla_build_mask_fp8_rotated: as nabla_build_mask_fp8 (the mask is that of the
+ *   unrotated q, k), with q's codes rotated on the query side and k's on the key side.
+ * Errors: BSA_EINVAL for sign_bits == NULL or key_side not 0/1; otherwise as the
+ * unrotated calls.
+ * ------------------------------------------------------------------------- */
+bsa_status quantize_fp8_blocks_rotated(const bsa_tensor* x, const bsa_shape* shape, const uint64_t* sign_bits,
+                                       int key_side, const bsa_tensor* codes, float* scales, bsa_stream_t stream);
+bsa_status nabla_build_mask_fp8_rotated(const bsa_tensor* q, const bsa_tensor* k, const bsa_shape* shape,
+                                        double thr, double scale,
+                                        const uint8_t* or_mask, int64_t or_sb, int64_t or_sh, uint8_t* mask_out,
+                                        uint8_t* near_thr_out, const uint64_t* sign_bits,
+                                        const bsa_tensor* q8, float* q_scale, const bsa_tensor* k8,
+                                        float* k_scale, void* ws, size_t ws_bytes, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Static sliding-tile block mask [STA, "Observation & Proposed Method"].
  *
  * The T x H x W latent grid (T*H*W == shape->S_valid) is cut into tiles of

@@ -84,6 +84,15 @@ def make_inputs(cfg: Config, seed: int = 0, device="cpu"):
     return q, k, v
 
 
+def make_signs(D: int, seed: int = 0):
+    """D random signs (+1.0 / -1.0, float64 numpy array) from a seeded torch generator: the
+    random draw of the incoherent processing, passed to both the library and the oracle."""
+    g = torch.Generator()
+    g.manual_seed(0x5167 + seed)
+    bits = torch.randint(0, 2, (D,), generator=g)
+    return (1.0 - 2.0 * bits.double()).numpy()
+
+
 def quantize_fp8_blocks(x: torch.Tensor, N: int = 64):
     """Per (b, h, N-token block) fp8 e4m3fn quantization with scale = amax / 448.
 

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 11
+    assert lib.bsa_abi_version() == 12
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
