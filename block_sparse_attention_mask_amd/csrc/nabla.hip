@@ -22,6 +22,8 @@
 //     not depend on the order of the atomic additions (run-to-run deterministic).
 //     For short rows (nb <= 256) select_rows_kernel does the same per row with one
 //     wave per row after the map is formed, without workgroup barriers.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -50,6 +52,29 @@ __device__ __forceinline__ int64_t mf_index(int bh, int nb, int D, int blk, int 
 __device__ __forceinline__ unsigned pack_e4m3x4(float a, float b, float c, float d) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// One cross-lane butterfly of the fast Walsh-Hadamard transform on chunk bit X of the
+// rotated pool's lane map: the lower lane of the pair keeps a + b, the upper a - b (a the
+// lower lane's value, b the upper's), each as one fma with the lane's sign su = +1 / -1:
+// fma(+-1, b, a) is a +- b rounded once, signed zeros included. Partners 1 or 2 lanes apart
+// come from a DPP quad permute ([1,0,3,2], [2,3,0,1]): there the own value is b in the
+// upper lane, so the lower lane's fma(1, y, o) = y + o and the upper's fma(-1, y, o) = o - y.
+// Partners 16 or 32 apart come from a permlane swap, which leaves a in r[0] and b in r[1]
+// in both lanes of the pair; 4 apart from a shuffle.
+template <int X>
+__device__ __forceinline__ float wht_lane_stage(float y, float su) {
+  const unsigned u = __float_as_uint(y);
+  if constexpr (X < 2) {
+    const float o = __uint_as_float((unsigned)__builtin_amdgcn_mov_dpp((int)u, X == 0 ? 0xB1 : 0x4E, 0xF, 0xF, true));
+    return __builtin_fmaf(su, y, o);
+  } else if constexpr (X == 2 || X == 3) {
+    const auto r = X == 2 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                          : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_fmaf(su, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  } else {
+    return __builtin_fmaf(su, y, __shfl_xor(y, 4, 64));
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -86,7 +111,36 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
   const int b = bh / H, h = bh % H;
   const T* base = which == 0 ? q + b * q_sb + h * q_sh : k + b * k_sb + h * k_sh;
   const int64_t ss = which == 0 ? q_ss : k_ss;
-  const int t = threadIdx.x, cg = t % TPR, r0 = t / TPR;
+  const int t = threadIdx.x;
+  // (row, 16-byte column chunk) of this thread. ROT: the chunk's bits sit on lane bits 0, 1,
+  // 4, 5 (then 2, 3), so that the butterfly partners of the cross-lane stages are 1 or 2
+  // lanes apart (DPP quad permutes) or 16 or 32 apart (permlane swaps); the other lane bits
+  // and the wave index give the row. Either map is a bijection of the threads onto the
+  // (row, chunk) pairs of a pass, and a wave still covers whole rows.
+  int cg, r0;
+  if constexpr (ROT) {
+    constexpr int LB[6] = {0, 1, 4, 5, 2, 3};
+    constexpr int NCB = TPR == 8 ? 3 : TPR == 16 ? 4 : 5;   // chunk bits
+    const int l = t & 63;
+    cg = 0;
+    int rl = 0, nr = 0;
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      const int bit = (l >> LB[x]) & 1;
+      if (x < NCB) cg |= bit << x;
+    }
+#pragma unroll
+    for (int lb = 0; lb < 6; ++lb) {
+      bool is_chunk = false;
+#pragma unroll
+      for (int x = 0; x < NCB; ++x) is_chunk |= LB[x] == lb;
+      if (!is_chunk) rl |= ((l >> lb) & 1) << nr++;
+    }
+    r0 = (t >> 6) * (64 / TPR) + rl;
+  } else {
+    cg = t % TPR;
+    r0 = t / TPR;
+  }
 
   i32x4_t raw[POOL_BPW][PASSES];
 #pragma unroll
@@ -109,6 +163,33 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
       return __int_as_float(wv[e]);
     }
   };
+  // fp64 partial sums of the block means: part[bb][r][d] = sum over this thread's rows
+  auto pool_partials = [&]() {
+#pragma unroll
+    for (int bb = 0; bb < POOL_BPW; ++bb) {
+      double acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = 0.0;
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            unsigned u = (unsigned)raw[bb][ps][w];
+            acc[2 * w] += (double)__uint_as_float(u << 16);
+            acc[2 * w + 1] += (double)__uint_as_float(u & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[w] += (double)__int_as_float(raw[bb][ps][w]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) part[bb][r0][cg * E + e] = acc[e];
+    }
+  };
+  // ROT: the sums come first, so that the loaded words can die as they are rotated
+  if constexpr (POOL && ROT) pool_partials();
   if constexpr (Q8) {
     __shared__ float wmax[POOL_BPW][4];
     const int lane = t & 63, wave = t >> 6;
@@ -134,15 +215,20 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
                 y[e] = a0 + b0;
                 y[e + hs] = a0 - b0;
               }
+          // stride E 2^X: chunk bit X, the partner lane 1, 2, 16, 32 or 4 apart
+          auto stage = [&](auto xc) {
+            constexpr int X = decltype(xc)::value;
+            if constexpr ((1 << X) < TPR) {
+              const float su = (cg >> X) & 1 ? -1.f : 1.f;
 #pragma unroll
-          for (int m = 1; m < TPR; m *= 2) {   // stride m * E: the partner lane cg ^ m of the same row
-            const bool upper = (cg & m) != 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-              const float o = __shfl_xor(y[e], m, 64);
-              y[e] = upper ? o - y[e] : y[e] + o;
+              for (int e = 0; e < E; ++e) y[e] = wht_lane_stage<X>(y[e], su);
             }
-          }
+          };
+          stage(std::integral_constant<int, 0>{});
+          stage(std::integral_constant<int, 1>{});
+          stage(std::integral_constant<int, 2>{});
+          stage(std::integral_constant<int, 3>{});
+          stage(std::integral_constant<int, 4>{});
         }
     }
     auto qval = [&](int bb, int ps, int e) -> float {
@@ -194,29 +280,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
       if (t == 0) f8.scale[which][(int64_t)bh * nb + i] = ROT ? sc * f8.smul[which] : sc;
     }
   }
+  if constexpr (POOL && !ROT) pool_partials();
   if constexpr (!POOL) return;
-#pragma unroll
-  for (int bb = 0; bb < POOL_BPW; ++bb) {
-    double acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0;
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          unsigned u = (unsigned)raw[bb][ps][w];
-          acc[2 * w] += (double)__uint_as_float(u << 16);
-          acc[2 * w + 1] += (double)__uint_as_float(u & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[w] += (double)__int_as_float(raw[bb][ps][w]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) part[bb][r0][cg * E + e] = acc[e];
-  }
   __syncthreads();
   for (int x = t; x < POOL_BPW * D; x += 256) {
     const int bb = x / D, d = x % D, i = i0 + bb;
