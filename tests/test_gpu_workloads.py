@@ -132,3 +132,38 @@ def test_config5_sweep_all_heads(gpu_lib, sweep_data, thr, qk):
     blocks = sample_blocks(keep, 16, seed=int(thr * 100) + (7 if qk == "fp8" else 0), full_heads=full)
     _check_blocks(f"cfg5 {qk} thr {thr}", out,
                   oracle_attention_blocks(q, k, v, keep, blocks, cfg.S_valid, q_deq=qd, k_deq=kd))
+
+
+@pytest.mark.timeout(900)
+def test_config5_fp8_rotated_all_heads(gpu_lib, sweep_data):
+    """The fp8 sweep case with incoherent processing (thr 0.05, the fp8 bench threshold): the
+    mask from nabla_build_mask_fp8_rotated equals the oracle's, the rotated codes and scales of
+    heads 0 and H-1 equal the oracle's bit for bit, and the attention on the library's rotated
+    codes matches the oracle fed their dequantised values on sampled blocks of every head."""
+    from synth import make_signs
+    cfg, q, k, v, P, plane = sweep_data
+    thr = 0.05
+    signs = make_signs(cfg.D, seed=0)
+    sta = gpu_lib.sta_build_mask(cfg.S, cfg.S_valid, cfg.grid, cfg.sta.tile, cfg.sta.window, order=cfg.order,
+                                 device=DEV)
+    keep, E = masks_from_probs(P, thr, or_plane=plane)
+    m, (qa, qs), (ka, ks) = gpu_lib.nabla_build_mask_fp8_rotated(q, k, thr, signs, or_mask=sta)
+    torch.cuda.synchronize()
+    bad, near = compare_masks(m, keep, E, thr, P=P)
+    print(f"[cfg5 fp8 rotated thr {thr}] mask: mismatches {bad}, near-threshold {near}", flush=True)
+    assert bad == 0
+    for h in (0, cfg.H - 1):
+        for x, codes, scales, key in ((q, qa, qs, False), (k, ka, ks, True)):
+            rc, rs = oracle.quantize_blocks_rotated(x[0, h].float().cpu().numpy(), signs, key, 64)
+            assert np.array_equal(scales[0, h].cpu().numpy(), rs)
+            assert np.array_equal(codes[0, h].cpu().numpy(), rc)
+
+    def deq(codes, scales):
+        def per_head(b, h):
+            c = codes[b, h].view(torch.float8_e4m3fn).to(torch.float64).view(cfg.nb, 64, cfg.D)
+            return (c * scales[b, h].to(torch.float64)[:, None, None]).view(cfg.S, cfg.D).cpu().numpy()
+        return per_head
+    out = _attention_as_benchmarked(gpu_lib, cfg, qa, ka, v, keep, q_scale=qs, k_scale=ks)
+    blocks = sample_blocks(keep, 16, seed=12)
+    _check_blocks(f"cfg5 fp8 rotated thr {thr}", out,
+                  oracle_attention_blocks(q, k, v, keep, blocks, cfg.S_valid, q_deq=deq(qa, qs), k_deq=deq(ka, ks)))
