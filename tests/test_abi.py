@@ -241,3 +241,26 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     bad = bsa.Shape(1, 2, 250, 250, 128, 64)
     assert lib.nabla_build_mask_noalloc(ctypes.byref(q), ctypes.byref(q), ctypes.byref(bad), 0.2, 0.0, None, 0, 0,
                                         4096, None, None) == 1
+
+
+def test_rotated_quantisation_rejects_bad_arguments(lib):
+    """Incoherent processing: the sign words are required and key_side is 0 or 1; both are
+    checked on the host before any launch."""
+    shape = bsa.Shape(1, 2, 256, 256, 128, 64)
+    x, codes = _t(), _t(dtype=bsa.BSA_FP8_E4M3FN)
+    words = (ctypes.c_uint64 * 2)(0x5, 0x3)
+    assert lib.quantize_fp8_blocks_rotated(ctypes.byref(x), ctypes.byref(shape), None, 0, ctypes.byref(codes),
+                                           4096, None) == 1
+    assert "sign_bits" in lib.bsa_last_error().decode()
+    assert lib.quantize_fp8_blocks_rotated(ctypes.byref(x), ctypes.byref(shape), words, 2, ctypes.byref(codes),
+                                           4096, None) == 1
+    assert "key_side" in lib.bsa_last_error().decode()
+    q8, k8 = _t(dtype=bsa.BSA_FP8_E4M3FN), _t(dtype=bsa.BSA_FP8_E4M3FN)
+    st = lib.nabla_build_mask_fp8_rotated(ctypes.byref(_t()), ctypes.byref(_t()), ctypes.byref(shape), 0.2, 0.0,
+                                          None, 0, 0, 4096, None, None, ctypes.byref(q8), 8192,
+                                          ctypes.byref(k8), 12288, 16384, 1 << 40, None)
+    assert st == 1 and "sign_bits" in lib.bsa_last_error().decode()
+    with pytest.raises(ValueError):
+        bsa._sign_words([1.0, -1.0, 0.5] + [1.0] * 125, 128)
+    w = bsa._sign_words([-1.0 if d in (0, 63, 64, 127) else 1.0 for d in range(128)], 128)
+    assert list(w) == [(1 << 0) | (1 << 63), (1 << 0) | (1 << 63)]

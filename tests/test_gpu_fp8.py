@@ -157,3 +157,30 @@ def test_rotation_lowers_fp8_attention_error_with_outlier_channels(gpu_lib):
     e_rot = attention_errors(o_rot, ref)[1]
     print(f"  mean error against the exact inputs: plain fp8 {e_plain:.3e}, rotated fp8 {e_rot:.3e}", flush=True)
     assert e_rot < 0.75 * e_plain, (e_plain, e_rot)
+
+
+def test_quantize_rotated_strided_input(gpu_lib):
+    from synth import make_signs
+    g = torch.Generator(device="cpu").manual_seed(19)
+    big = torch.randn(1, 4, 256, 256, generator=g).to(torch.bfloat16).to(DEV)
+    x = big[:, 1:3, :, 64:192]                            # head and row strides of the parent
+    signs = make_signs(128, seed=5)
+    for key_side in (False, True):
+        codes, scales = gpu_lib.quantize_fp8_blocks_rotated(x, signs, key_side)
+        torch.cuda.synchronize()
+        _check_rotated(codes, scales, x, signs, key_side)
+
+
+def test_fused_rotated_f32_d64(gpu_lib):
+    """The fused rotated quantisation with f32 inputs at D = 64 (the tiny config's shape):
+    mask equal to the unrotated build's, codes and scales bit-exact."""
+    from synth import make_signs
+    cfg = get_config(1)
+    q, k, v = make_inputs(cfg, seed=3, device=DEV)
+    signs = make_signs(cfg.D, seed=1)
+    m_ref = gpu_lib.nabla_build_mask(q, k, cfg.thrs[0])
+    m, (q8, qs), (k8, ks) = gpu_lib.nabla_build_mask_fp8_rotated(q, k, cfg.thrs[0], signs)
+    torch.cuda.synchronize()
+    assert torch.equal(m, m_ref)
+    _check_rotated(q8, qs, q, signs, False)
+    _check_rotated(k8, ks, k, signs, True)
