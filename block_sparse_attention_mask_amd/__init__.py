@@ -16,6 +16,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbsa.so")
+# the checked build (-DBSA_CHECKED): same entry points, list indices tested in the kernels
+CHECKED_LIB_PATH = os.path.join(_PKG, "libbsa_checked.so")
 
 BSA_F32, BSA_BF16, BSA_FP8_E4M3FN = 0, 1, 2
 _STATUS = {0: "BSA_OK", 1: "BSA_EINVAL", 2: "BSA_EUNSUPPORTED", 3: "BSA_EWORKSPACE", 4: "BSA_EHIP"}
@@ -31,7 +33,7 @@ EXPORTS = ["nabla_workspace_size", "nabla_build_mask", "nabla_build_mask_noalloc
            "attn_csr_workspace_size", "block_sparse_attn_fwd_csr", "block_sparse_attn_fwd_lists",
            "attn_work_order_slots", "attn_work_order",
            "attn_bwd_workspace_size", "block_sparse_attn_bwd", "token_reorder", "bsa_last_error",
-           "bsa_abi_version"]
+           "bsa_abi_version", "bsa_checked_build", "bsa_check_flags"]
 
 
 class BsaError(RuntimeError):
@@ -102,6 +104,8 @@ def load(path: Optional[str] = None):
         "block_sparse_attn_bwd": (i32, [PT, PT, PT, PT, PT, vp, PS, vp, i64, i64, dbl, PT, PT, PT, vp, sz, vp]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_abi_version": (i32, []),
+        "bsa_checked_build": (i32, []),
+        "bsa_check_flags": (ctypes.c_uint, [i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -82,7 +82,25 @@ bsa_status check_tensor(const char* name, const bsa_tensor* t, const bsa_shape* 
 extern "C" {
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
-int bsa_abi_version(void) { return 12; }
+int bsa_abi_version(void) { return 13; }
+
+int bsa_checked_build(void) {
+#ifdef BSA_CHECKED
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+unsigned bsa_check_flags(int clear) {
+  const unsigned w[3] = {bsa::check_flags_attn(clear), bsa::check_flags_mask_ops(clear), bsa::check_flags_bwd(clear)};
+  unsigned v = 0;
+  for (unsigned x : w) {
+    if (x == ~0u) return ~0u;
+    v |= x;
+  }
+  return v;
+}
 
 // ---------------------------------------------------------------------------
 size_t nabla_workspace_size(const bsa_shape* s) {

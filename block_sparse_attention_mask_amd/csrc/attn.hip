@@ -161,6 +161,10 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     eA = row_ptr[rowA + 1];
     if (hasB) { sB = row_ptr[rowB]; eB = row_ptr[rowB + 1]; }
   }
+  if (!BSA_CHECK(sA <= eA && eA - sA <= a.nb && sB <= eB && eB - sB <= a.nb, CHK_ATTN_LEN)) {
+    eA = sA;   // (checked build: a bad list is walked as empty)
+    eB = sB;
+  }
   const int i = pr ? iB : iA;                      // this wave's query block
   const bool mine_valid = pr == 0 || hasB;
   const int row = bh * a.nb + i;
@@ -253,6 +257,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
       flags = (int)((curA >> t) & 1ull) | (int)(((curB >> t) & 1ull) << 1);
       curA &= ~(1ull << t);
       curB &= ~(1ull << t);
+      if (!BSA_CHECK(64 * wi + t < a.nb, CHK_ATTN_ENTRY)) { flags = 0; return -1; }
       // the fp8 key scale of the entry, a scalar load used two steps later
       if constexpr (MODE == ATTN_FP8) ksc = ((const float __attribute__((address_space(4)))*)(uintptr_t)k_scale)[bh * a.nb + 64 * wi + t];
       return 64 * wi + t;
@@ -264,6 +269,7 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     const int jb = ib < eB ? __builtin_amdgcn_readlane(cacheB, ib - cbB) : BIG;
     const int j = min(ja, jb);
     if (j == BIG) { flags = 0; return -1; }
+    if (!BSA_CHECK(j >= 0 && j < a.nb && max(ja, jb) >= 0, CHK_ATTN_ENTRY)) { flags = 0; return -1; }
     flags = (ja == j ? 1 : 0) | (jb == j ? 2 : 0);
     if constexpr (MODE == ATTN_FP8)
       ksc = __int_as_float(ja == j ? __builtin_amdgcn_readlane(__float_as_int(kscA), ia - cbA)
@@ -654,6 +660,8 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
                      a.k_scale);
   return hipGetLastError();
 }
+
+BSA_CHECK_ACCESSOR(check_flags_attn)
 
 hipError_t launch_attn(const AttnArgs& a, AttnMode mode, hipStream_t st) {
   if (a.D == 64) {

@@ -223,6 +223,7 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
     const int jb = ib < eB ? __builtin_amdgcn_readlane(cacheB, ib - cbB) : BIG;
     const int jm = min(ja, jb);
     if (jm == BIG) { flags = 0; return -1; }
+    if (!BSA_CHECK(jm >= 0 && jm < a.nb, CHK_BWD_ENTRY)) { flags = 0; return -1; }
     flags = (ja == jm ? 1 : 0) | (jb == jm ? 2 : 0);
     ia += ja == jm;
     ib += jb == jm;
@@ -441,6 +442,7 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
     const int jb = ib < eB ? __builtin_amdgcn_readlane(cacheB, ib - cbB) : BIG;
     const int jm = min(ja, jb);
     if (jm == BIG) { flags = 0; return -1; }
+    if (!BSA_CHECK(jm >= 0 && jm < a.nb, CHK_BWD_ENTRY)) { flags = 0; return -1; }
     flags = (ja == jm ? 1 : 0) | (jb == jm ? 2 : 0);
     ia += ja == jm;
     ib += jb == jm;
@@ -573,5 +575,7 @@ hipError_t launch_bwd(const BwdArgs& a, bool f32_out, const int32_t* row_ptr, co
   return f32_out ? launch_bwd_t<128, true>(a, row_ptr, col_idx, col_ptr, row_idx, ld, st)
                  : launch_bwd_t<128, false>(a, row_ptr, col_idx, col_ptr, row_idx, ld, st);
 }
+
+BSA_CHECK_ACCESSOR(check_flags_bwd)
 
 }  // namespace bsa

@@ -18,6 +18,40 @@ typedef unsigned short u16;
 
 #define BSA_LDS __attribute__((address_space(3)))
 
+// Checked build (-DBSA_CHECKED): indices that kernels read from list data (kv-list entries,
+// list lengths) are tested before use; a failed test sets its bit in this translation
+// unit's device word (read and cleared by bsa_check_flags) and the access is skipped.
+// Elsewhere BSA_CHECK is the constant true and the tests compile away.
+enum : unsigned {
+  CHK_ATTN_ENTRY = 1u,     // attention: kv-list entry outside [0, nb)
+  CHK_ATTN_LEN = 2u,       // attention / work order: list length outside [0, nb]
+  CHK_ROW_BITS = 4u,       // pairing: list entry outside the bit row
+  CHK_BWD_ENTRY = 8u,      // backward: list entry outside [0, nb)
+};
+#ifdef BSA_CHECKED
+static __device__ unsigned bsa_check_word;
+__device__ __forceinline__ bool bsa_check(bool ok, unsigned bit) {
+  if (!ok) atomicOr(&bsa_check_word, bit);
+  return ok;
+}
+#define BSA_CHECK(ok, bit) bsa_check((ok), (bit))
+// host: this translation unit's word (and clear it), synchronous
+#define BSA_CHECK_ACCESSOR(fn)                                              \
+  unsigned fn(int clear) {                                                  \
+    unsigned v = 0;                                                         \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(bsa_check_word), sizeof v) != hipSuccess) return ~0u; \
+    if (clear) {                                                            \
+      const unsigned z = 0;                                                 \
+      if (hipMemcpyToSymbol(HIP_SYMBOL(bsa_check_word), &z, sizeof z) != hipSuccess) return ~0u; \
+    }                                                                       \
+    return v;                                                               \
+  }
+#else
+#define BSA_CHECK(ok, bit) true
+#define BSA_CHECK_ACCESSOR(fn) \
+  unsigned fn(int) { return 0; }
+#endif
+
 __device__ __forceinline__ float bf16_bits_to_f32(u16 h) {
   return __uint_as_float(((unsigned)h) << 16);
 }

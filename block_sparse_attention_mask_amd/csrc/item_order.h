@@ -79,6 +79,7 @@ __device__ int kth_longest_item(Len len, int nb, int* sm, int lo, int R, int k, 
     const int2 pb = pair_blocks(it - bh * npair, pair_d ? pair_d[bh] : 1, nb);
     int c = len(bh * nb + pb.x);
     if (pb.y >= 0) c = max(c, len(bh * nb + pb.y));
+    if (!BSA_CHECK(c >= 0 && c <= nb, CHK_ATTN_LEN)) c = min(max(c, 0), nb);   // (histogram index)
     c = min(max(c, 0), nb);
     cost[i] = c;
     atomicAdd(&hist[c], 1);

@@ -126,6 +126,12 @@ hipError_t launch_token_reorder(const void* src, const int64_t* s_strides_bytes,
                                 const int64_t* d_strides_bytes, int B, int H, int S, int row_bytes,
                                 const ReorderGeom& g, bool inverse, hipStream_t st);
 
+// checked build: each translation unit's flag word (CHK_* bits of common.h), read and
+// optionally cleared; synchronous; 0 in the production build, ~0u on a HIP error
+unsigned check_flags_attn(int clear);
+unsigned check_flags_mask_ops(int clear);
+unsigned check_flags_bwd(int clear);
+
 // attn.hip
 struct AttnArgs {
   const void* q; int64_t q_sb, q_sh, q_ss;

@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256) void row_bits_kernel(const int32_t* __restrict
     }
     for (int e = lo + l; e < hi; e += 64) {
       const int j = col_idx[e];
-      atomicOr(&w[j >> 6], 1ull << (j & 63));
+      if (BSA_CHECK((unsigned)j < (unsigned)(64 * nw), CHK_ROW_BITS)) atomicOr(&w[j >> 6], 1ull << (j & 63));
     }
   }
   __syncthreads();
@@ -546,5 +546,7 @@ hipError_t launch_pair_offsets(const int32_t* row_ptr, const int32_t* col_idx, c
   hipLaunchKernelGGL(pair_pick_kernel, dim3((unsigned)BH), dim3(64), 0, st, cost, dmax, pair_d);
   return hipGetLastError();
 }
+
+BSA_CHECK_ACCESSOR(check_flags_mask_ops)
 
 }  // namespace bsa

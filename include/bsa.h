@@ -486,6 +486,23 @@ const char* bsa_last_error(void);
 /* Version of this interface (incremented on incompatible changes). */
 int bsa_abi_version(void);
 
+/* ---------------------------------------------------------------------------
+ * Checked build (libbsa_checked.so, compiled with -DBSA_CHECKED; for tests and
+ * debugging, not for timing). Its kernels test the indices they read from list data
+ * before using them: kv-list entries in [0, nb) and list lengths in [0, nb] in the
+ * attention forward and its in-kernel work order, list entries inside the bit rows of
+ * the pairing pass, list entries of the backward walks. A failed test sets a bit of a
+ * device flag word and skips the access (the bad list is cut short), so a run with bad
+ * lists from a caller completes and reports instead of reading or writing out of bounds.
+ * bsa_checked_build: 1 in the checked library, 0 in the production one.
+ * bsa_check_flags: the OR of the flag words since the last clear (bit 0: attention list
+ * entry, bit 1: list length, bit 2: bit-row entry, bit 3: backward list entry); clear != 0
+ * also resets them. Synchronous (waits for the device); 0 in the production library;
+ * 0xFFFFFFFF if reading the device words failed.
+ * ------------------------------------------------------------------------- */
+int bsa_checked_build(void);
+unsigned bsa_check_flags(int clear);
+
 #ifdef __cplusplus
 }
 #endif

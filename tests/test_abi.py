@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bsa_abi_version() == 12
+    assert lib.bsa_abi_version() == 13
 
 
 def _t(ptr=256, dtype=bsa.BSA_BF16, ss=128):
@@ -264,3 +264,18 @@ def test_rotated_quantisation_rejects_bad_arguments(lib):
         bsa._sign_words([1.0, -1.0, 0.5] + [1.0] * 125, 128)
     w = bsa._sign_words([-1.0 if d in (0, 63, 64, 127) else 1.0 for d in range(128)], 128)
     assert list(w) == [(1 << 0) | (1 << 63), (1 << 0) | (1 << 63)]
+
+
+def test_checked_build_exports_the_same_calls():
+    """The checked library (built beside the production one) exports every declared call,
+    reports itself as checked and starts with no flag set (reading the flags needs no GPU
+    work: both calls are host-side in the production library)."""
+    lib = bsa.load()
+    assert lib.bsa_checked_build() == 0
+    assert lib.bsa_check_flags(0) == 0
+    assert os.path.exists(bsa.CHECKED_LIB_PATH), "libbsa_checked.so is not built"
+    chk = ctypes.CDLL(bsa.CHECKED_LIB_PATH)
+    for n in _declared():
+        assert hasattr(chk, n), n
+    assert chk.bsa_checked_build() == 1
+    assert chk.bsa_abi_version() == lib.bsa_abi_version()
