@@ -53,14 +53,16 @@ class Shape(ctypes.Structure):
 
 
 _lib = None
+_lib_path = None
 
 
 def load(path: Optional[str] = None):
-    """Load libbsa.so and declare its signatures; raises if it is not built."""
-    global _lib
-    if _lib is not None:
+    """Load libbsa.so (or the library at `path`, e.g. CHECKED_LIB_PATH, which then serves
+    every call of this module) and declare its signatures; raises if it is not built."""
+    global _lib, _lib_path
+    p = path or _lib_path or LIB_PATH
+    if _lib is not None and p == _lib_path:
         return _lib
-    p = path or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"libbsa.so not found at {p}; build it with "
                            "`python -m block_sparse_attention_mask_amd.build`")
@@ -110,7 +112,7 @@ def load(path: Optional[str] = None):
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
         f.restype, f.argtypes = res, args
-    _lib = lib
+    _lib, _lib_path = lib, p
     return lib
 
 

@@ -22,12 +22,11 @@ DEV = "cuda"
 @contextlib.contextmanager
 def _library(path):
     """Run the binding against the library at `path`, then restore the production one."""
-    saved = bsa._lib
-    bsa._lib = None
+    saved = bsa._lib, bsa._lib_path
     try:
         yield bsa.load(path)
     finally:
-        bsa._lib = saved
+        bsa._lib, bsa._lib_path = saved
 
 
 def _step(cfg, q, k, v):
