@@ -395,7 +395,8 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
       }
       // The normaliser sums the probabilities as rounded to bf16 for the PV product, so
       // that O is an exact convex combination of those weights: the rounding then moves
-      // O by 2^-9 sum_k w_k |V_k - O| at most, instead of 2^-9 |O|.
+      // O by 2^-8 sum_k w_k |V_k - O| at most (bf16's unit roundoff: 8 significant bits),
+      // instead of 2^-8 |O|.
       const float mr = m_run;
       float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll

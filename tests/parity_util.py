@@ -157,7 +157,7 @@ def sample_blocks(keep: np.ndarray, per_head: int, seed: int = 0, full_heads=())
     return out
 
 # Gradient tolerances per head, relative to the largest reference gradient. Three
-# roundings enter: P and dS as bf16 MFMA operands (unit roundoff 2^-9), the bf16 output,
+# roundings enter: P and dS as bf16 MFMA operands (unit roundoff 2^-8), the bf16 output,
 # and delta = <dO, O> formed from the forward's bf16 output O. Since sum_k dS_qk = 0, dQ
 # and dK are sums with cancellation, so these roundings are relative to the absolute
 # terms, not to the result: each of the first and the last moves dQ by up to ~1% of

@@ -49,7 +49,8 @@ def test_chunked_config2_full(gpu_lib, chunked, w):
     print(f"[chunked w={w}] {cfg.name}: max err {mx:.3e} mean err {mean:.3e}", flush=True)
     assert mx <= MAX_ERR and mean <= MEAN_ERR
     # against the whole-row walk: both within the tolerance of the oracle, and lse within
-    # two bf16 normaliser bounds of each other (each within -log(1 - 2^-9) of exact)
+    # 5e-3 of each other (each within -log(1 - 2^-8) ~ 3.9e-3 of exact in the worst case;
+    # the roundings of the two walks' normalisers are not all one way)
     chunked(0)
     whole, lse_w = gpu_lib.block_sparse_attn_fwd(q, k, v, mask, return_lse=True)
     torch.cuda.synchronize()
@@ -87,7 +88,8 @@ def test_chunked_edge_rows(gpu_lib, chunked, D, w):
         assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR
         fin = np.isfinite(L)
         assert np.array_equal(fin, np.isfinite(f64(lse[0, h])))
-        # the normaliser is the sum of the bf16-rounded weights: |lse - exact| <= -log(1 - 2^-9)
+        # the normaliser is the sum of the bf16-rounded weights: |lse - exact| <= -log(1 - 2^-8)
+        # (3.9e-3) in the worst case; held to 2.5e-3 here, inside that bound
         assert np.abs(f64(lse[0, h])[fin] - L[fin]).max() < 2.5e-3
 
 

@@ -249,8 +249,9 @@ def test_attention_edge_rows(gpu_lib):
             assert np.abs(f64(out[0, h]) - O).max() <= MAX_ERR
             fin = np.isfinite(L)
             # lse is the log of the normaliser the kernel divides by: the sum of the weights
-            # as rounded to bf16 for the PV product, each within 2^-9 (relative) of exact,
-            # so |lse - exact| <= -log(1 - 2^-9) ~ 1.96e-3 (plus fp32 noise)
+            # as rounded to bf16 for the PV product, each within 2^-8 (relative; bf16 has 8
+            # significant bits) of exact, so |lse - exact| <= -log(1 - 2^-8) ~ 3.9e-3 in the
+            # worst case (all roundings one way); the test holds it to 2.5e-3, inside that bound
             assert np.abs(f64(lse[0, h])[fin] - L[fin]).max() < 2.5e-3
 
 

@@ -7,7 +7,9 @@ fp64 emulation that inserts exactly these roundings (and nothing else) measures 
 error they cause on a 2B-DiT-like head; the tolerance must exceed it with a margin of 3
 for the fp32 accumulation order and the final output rounding, which the emulation
 leaves out. Also: compare_masks excuses a pivot tie only when the difference is a swap
-of entries whose probabilities agree to the map's fp64 rounding.
+of entries whose probabilities agree to the map's fp64 rounding; and the lse bound: the
+attention normalises by the fp32 sum of its probabilities as rounded to bf16, so lse lies
+within -log(1 - 2^-8) of exact (bf16 keeps 8 significant bits).
 """
 import numpy as np
 import pytest
@@ -92,3 +94,25 @@ def test_compare_masks_excuses_only_pivot_ties():
     extra[0, j_drop] = True
     assert compare_masks(torch.from_numpy(extra[None, None].astype(np.uint8)), keep4, E4, 0.35, P=P4)[0] == 1
     assert TIE_REL < 1e-9
+
+
+def test_lse_bound_of_the_bf16_normaliser():
+    """Each probability rounded to bf16 (round to nearest even, 8 significant bits) is within
+    2^-8 (relative) of exact, so the sum of the rounded terms is within that factor of the
+    exact sum and lse within -log(1 - 2^-8) ~ 3.9e-3. Terms all just below a rounding
+    midpoint (1 + 2^-8 - 2^-20 rounds to 1) come within 0.5% of the bound, so a bound from a
+    unit roundoff of 2^-9 would be wrong; rows of random scores under the kernel's offsets
+    (the running maximum, or up to 8 below the row maximum with the lazy rescale) stay inside."""
+    bound = -np.log1p(-2.0 ** -8)
+    x = np.full(1000, 1.0 + 2.0 ** -8 - 2.0 ** -20)
+    worst = abs(np.log(_bf16(x).sum()) - np.log(x.sum()))
+    assert 0.995 * bound < worst <= bound
+    assert worst > -np.log1p(-2.0 ** -9)
+    rng = np.random.default_rng(3)
+    for sigma in (0.5, 3.0, 12.0):
+        s = rng.normal(0.0, sigma, (200, 512))
+        for shift in (0.0, 4.0, 8.0):
+            m = s.max(axis=1, keepdims=True) - shift
+            p = np.exp2(s - m)
+            err = np.abs(np.log(_bf16(p).sum(axis=1)) - np.log(p.sum(axis=1)))
+            assert err.max() <= bound, (sigma, shift, err.max())
