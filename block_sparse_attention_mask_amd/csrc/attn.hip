@@ -124,6 +124,23 @@ void attn_fwd_kernel(AttnArgs a, const int32_t* __restrict__ row_ptr, const int3
     const int hi = (int)(((int64_t)(g + 1) * total + BSA_NXCD - 1) / BSA_NXCD);
     if (k >= hi - lo) return;
     lin = lo + k;
+  } else if (a.derive_order == 2 && a.pair_d && a.pair_d[0] > 1) {
+    // Scattered lists (the heads pair blocks at an offset > 1, e.g. one frame apart in a
+    // row-major video layout): neighbouring items share few kv tiles, so what counts is that
+    // the heads being walked keep their K and V in the last-level cache. XCDs 2g and 2g+1
+    // share range g of four and take its items alternately: four heads live at a time
+    // instead of eight. (Where blocks pair adjacently, each XCD's own contiguous range keeps
+    // the tiles that neighbouring items share in its L2, which matters more.)
+    constexpr int NG = BSA_NXCD / 2;
+    const int x = blockIdx.x % BSA_NXCD, p = blockIdx.x / BSA_NXCD, g = x >> 1;
+    const int chunk = (total + NG - 1) / NG;
+    lin = g * chunk + 2 * p + (x & 1);
+    if (lin >= min((g + 1) * chunk, total)) return;
+    if (kth_longest_fits(a.nb, npair, sizeof(smem))) {
+      // longest first inside each head
+      const int head0 = lin / npair * npair;
+      lin = kth_longest_item<256>(list_len, a.nb, (int*)smem, head0, npair, lin - head0, a.pair_d);
+    }
   } else {
     const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
     lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
