@@ -124,6 +124,23 @@ __device__ __forceinline__ bf16x8_t pack8(const float* x) {
 //     are read with transposing LDS reads (the forward's P V step with the query
 //     index contracted).
 // The two query halves' partial dK^T, dV^T are summed through LDS at the end.
+// Natural item of this workgroup, or -1: one contiguous range of the items per XCD, or
+// (share) one of four ranges per pair of XCDs, whose two take its items alternately -- the
+// forward's placement for heads that pair blocks at an offset above 1 (scattered lists),
+// where fewer heads live at a time keep their tiles in the last-level cache.
+__device__ __forceinline__ int xcd_range_item(int total, bool share) {
+  const int x = blockIdx.x % BSA_NXCD, p = blockIdx.x / BSA_NXCD;
+  if (share) {
+    constexpr int NG = BSA_NXCD / 2;
+    const int g = x >> 1, chunk = (total + NG - 1) / NG;
+    const int lin = g * chunk + 2 * p + (x & 1);
+    return lin < min((g + 1) * chunk, total) ? lin : -1;
+  }
+  const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
+  const int lin = x * chunk + p;
+  return lin < total ? lin : -1;
+}
+
 template <int D, bool F32, bool BITS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
@@ -142,9 +159,8 @@ void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32
 
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
-  const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
-  int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
-  if (lin >= total) return;
+  int lin = xcd_range_item(total, a.derive_order && a.pair_dk && a.pair_dk[0] > 1);
+  if (lin < 0) return;
   if (a.derive_order && kth_longest_fits(a.nb, npair, sizeof(smem))) {
     // the same ranges, longest first inside each head (natural order where its tables
     // would not fit in smem)
@@ -375,9 +391,8 @@ void bwd_dq_kernel(BwdArgs a, const int32_t* __restrict__ row_ptr, const int32_t
 
   const int npair = (a.nb + 1) / 2;
   const int total = a.B * a.H * npair;
-  const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
-  int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
-  if (lin >= total) return;
+  int lin = xcd_range_item(total, a.derive_order && a.pair_dq && a.pair_dq[0] > 1);
+  if (lin < 0) return;
   if (a.derive_order && kth_longest_fits(a.nb, npair, sizeof(smem))) {
     // the same ranges, longest first inside each head (natural order where its tables
     // would not fit in smem)
