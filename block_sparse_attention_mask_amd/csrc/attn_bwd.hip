@@ -125,19 +125,13 @@ __device__ __forceinline__ bf16x8_t pack8(const float* x) {
 //     index contracted).
 // The two query halves' partial dK^T, dV^T are summed through LDS at the end.
 // Natural item of this workgroup, or -1: one contiguous range of the items per XCD, or
-// (share) one of four ranges per pair of XCDs, whose two take its items alternately -- the
-// forward's placement for heads that pair blocks at an offset above 1 (scattered lists),
-// where fewer heads live at a time keep their tiles in the last-level cache.
-__device__ __forceinline__ int xcd_range_item(int total, bool share) {
-  const int x = blockIdx.x % BSA_NXCD, p = blockIdx.x / BSA_NXCD;
-  if (share) {
-    constexpr int NG = BSA_NXCD / 2;
-    const int g = x >> 1, chunk = (total + NG - 1) / NG;
-    const int lin = g * chunk + 2 * p + (x & 1);
-    return lin < min((g + 1) * chunk, total) ? lin : -1;
-  }
+// (shared) the plain order, in which all eight XCDs walk one head together -- the forward's
+// placement for heads that pair blocks at an offset above 1 (scattered lists), where the
+// head being walked keeps its tiles in the last-level cache.
+__device__ __forceinline__ int xcd_range_item(int total, bool shared) {
+  if (shared) return (int)blockIdx.x < total ? (int)blockIdx.x : -1;
   const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
-  const int lin = x * chunk + p;
+  const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
   return lin < total ? lin : -1;
 }
 
