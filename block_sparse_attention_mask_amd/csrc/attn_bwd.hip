@@ -107,6 +107,18 @@ __device__ __forceinline__ bf16x8_t pack8(const float* x) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// Natural item of this workgroup, or -1: one contiguous range of the items per XCD, or
+// (shared) the plain order, in which all eight XCDs walk one head together, so that its
+// tiles stay in the last-level cache. The kernels share where the heads pair blocks at an
+// offset above 1 (scattered lists; the forward shares ranges between pairs of XCDs there,
+// the backward gains more from sharing among all eight).
+__device__ __forceinline__ int xcd_range_item(int total, bool shared) {
+  if (shared) return (int)blockIdx.x < total ? (int)blockIdx.x : -1;
+  const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
+  const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
+  return lin < total ? lin : -1;
+}
+
 // ---- dK, dV -------------------------------------------------------------------------
 // One workgroup of eight waves per PAIR of adjacent key blocks (2p, 2p+1). Wave w works
 // on key block 2p + (w >> 2); inside it, it owns keys 32 (w & 1) .. +32 (its MFMA
@@ -124,17 +136,6 @@ __device__ __forceinline__ bf16x8_t pack8(const float* x) {
 //     are read with transposing LDS reads (the forward's P V step with the query
 //     index contracted).
 // The two query halves' partial dK^T, dV^T are summed through LDS at the end.
-// Natural item of this workgroup, or -1: one contiguous range of the items per XCD, or
-// (shared) the plain order, in which all eight XCDs walk one head together -- the forward's
-// placement for heads that pair blocks at an offset above 1 (scattered lists), where the
-// head being walked keeps its tiles in the last-level cache.
-__device__ __forceinline__ int xcd_range_item(int total, bool shared) {
-  if (shared) return (int)blockIdx.x < total ? (int)blockIdx.x : -1;
-  const int chunk = (total + BSA_NXCD - 1) / BSA_NXCD;
-  const int lin = (int)(blockIdx.x % BSA_NXCD) * chunk + (int)(blockIdx.x / BSA_NXCD);
-  return lin < total ? lin : -1;
-}
-
 template <int D, bool F32, bool BITS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a, const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
