@@ -165,3 +165,34 @@ def test_backward_deterministic(gpu_lib):
     b = _run(gpu_lib, q, k, v, do, m, 1000)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_backward_plain_order_writes_every_row(gpu_lib):
+    """14B shape with 3 heads (an odd head count, so items do not split evenly over the
+    XCDs): its heads pair blocks one frame apart, so the backward kernels take their items in
+    plain order. Every gradient row is written (NaN-initialised outputs, padded rows 0) and
+    the result equals the gradients of the same heads computed one head at a time."""
+    cfg = get_config(3, heads=3)
+    q, k, v = make_inputs(cfg, seed=2, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(8)
+    do = (torch.randn(q.shape, generator=g, device=DEV) * 0.1).to(torch.bfloat16)
+    m = gpu_lib.nabla_build_mask(q, k, cfg.thrs[0])
+    rp, ci = gpu_lib.mask_to_csr(m)
+    d = gpu_lib.attn_pair_offsets(q, rp, ci, s_valid=cfg.S_valid)
+    assert int(d[0]) > 1, "this shape should pair blocks at an offset above 1"
+    o, lse = gpu_lib.block_sparse_attn_fwd(q, k, v, m, s_valid=cfg.S_valid, return_lse=True)
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    dq, dk, dv = gpu_lib.block_sparse_attn_bwd(q, k, v, o, do, lse, m, s_valid=cfg.S_valid, out=grads)
+    torch.cuda.synchronize()
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isfinite(x).all(), name
+        assert torch.all(x[:, :, cfg.S_valid:] == 0), name
+    for h in range(cfg.H):   # one head per call: a single-head launch
+        sl = slice(h, h + 1)
+        o1, l1 = gpu_lib.block_sparse_attn_fwd(q[:, sl], k[:, sl], v[:, sl], m[:, sl], s_valid=cfg.S_valid,
+                                               return_lse=True)
+        g1 = gpu_lib.block_sparse_attn_bwd(q[:, sl], k[:, sl], v[:, sl], o1, do[:, sl], l1, m[:, sl],
+                                           s_valid=cfg.S_valid)
+        torch.cuda.synchronize()
+        for name, full, one in zip(("dq", "dk", "dv"), (dq, dk, dv), g1):
+            assert torch.equal(full[:, sl], one), (name, h)
