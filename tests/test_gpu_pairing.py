@@ -116,3 +116,28 @@ def test_pairing_outputs_equal_adjacent_pairs(gpu_lib, nb):
     mx, mean = attention_errors(out, oracle_attention_blocks(q, k, v, keep, blocks, sv))
     print(f"  max err {mx:.3e} mean err {mean:.3e}", flush=True)
     assert mx <= MAX_ERR and mean <= MEAN_ERR
+
+
+@pytest.mark.parametrize("heads", [3, 5])
+def test_xcd_pair_placement_writes_every_block(gpu_lib, heads):
+    """14B shape with an odd head count (items that do not split evenly over the XCD pairs):
+    its heads pair blocks one frame apart, so pairs of XCDs share ranges and take their items
+    alternately. Every valid output row is written (NaN-initialised output) and each head's
+    output equals a single-head launch of it bit for bit."""
+    from synth import get_config, make_inputs
+    cfg = get_config(3, heads=heads)
+    q, k, v = make_inputs(cfg, seed=4, device=DEV)
+    m = gpu_lib.nabla_build_mask(q, k, cfg.thrs[0])
+    rp, ci = gpu_lib.mask_to_csr(m)
+    d = gpu_lib.attn_pair_offsets(q, rp, ci, s_valid=cfg.S_valid)
+    assert int(d[0]) > 1, "this shape should pair blocks at an offset above 1"
+    out = torch.full(v.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    gpu_lib.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=cfg.S_valid, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:, :, :cfg.S_valid]).all()
+    assert torch.all(out[:, :, cfg.S_valid:] == 0)
+    for h in range(heads):
+        sl = slice(h, h + 1)
+        one = gpu_lib.block_sparse_attn_fwd(q[:, sl], k[:, sl], v[:, sl], m[:, sl], s_valid=cfg.S_valid)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, sl], one), h
