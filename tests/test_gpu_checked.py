@@ -5,7 +5,7 @@ bit-row entries, backward list entries) and record a failed test in a device fla
 instead of touching memory out of bounds. On the benchmark step's calls -- the short-row
 list path (2B-DiT shape), the long-row path with pairing offsets, bit rows and the work
 order each workgroup derives (14B shape, 2 heads), the kv lists handed in by the caller,
-and the backward -- no flag may be set, and every output must equal the production
+fp8 Q/K, the kv-chunked walk and the backward -- no flag may be set, and every output must equal the production
 library's bit for bit (the tests compile away there)."""
 import contextlib
 
@@ -45,6 +45,15 @@ def _step(cfg, q, k, v):
     outs["csr"] = bsa.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=cfg.S_valid)
     o, lse = bsa.block_sparse_attn_fwd(q, k, v, m, s_valid=cfg.S_valid, return_lse=True)
     outs["o"], outs["lse"] = o, lse
+    # fp8 Q/K (codes and scales from the mask build's own read) through the same attention
+    m8, (q8, qs), (k8, ks) = bsa.nabla_build_mask_fp8(q, k, thr)
+    outs["fp8"] = bsa.block_sparse_attn_fwd(q8, k8, v, m8, s_valid=cfg.S_valid, q_scale=qs, k_scale=ks)
+    # the kv-chunked walk and its combine
+    bsa.set_attn_kv_chunk(7)
+    try:
+        outs["chunked"] = bsa.block_sparse_attn_fwd_csr(q, k, v, rp, ci, s_valid=cfg.S_valid)
+    finally:
+        bsa.set_attn_kv_chunk(0)
     g = torch.Generator(device=DEV).manual_seed(5)
     do = (torch.randn(q.shape, generator=g, device=DEV) * 0.1).to(torch.bfloat16)
     outs["dq"], outs["dk"], outs["dv"] = bsa.block_sparse_attn_bwd(q, k, v, o, do, lse, m, s_valid=cfg.S_valid)
